@@ -1,0 +1,226 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA chunked-prefill library.
+ *
+ * The library computes multi-head latent attention (MLA) prefill over a
+ * paged cache that stores, per token and layer, one packed record of the
+ * 512-wide compressed latent c_kv followed by the 64-wide rope key k_rope
+ * (576 elements), in 64-token blocks. The packed record is never split per
+ * head: per-head keys and values are decompressed from it through kv_b_proj
+ * chunk by chunk, and chunk results are merged by log-sum-exp.
+ *
+ * Pages the operations follow:
+ *   [DSMLA]   "DeepSeek MLA -- Prefix Cache and Chunked Prefill" notes,
+ *             section 4.2 (context + extend stages), 4.3 (merge_attn_states),
+ *             4.4 (_compute_prefill_context chunk loop), 5.2 (576-element
+ *             packed record).
+ *   [PAGED]   "PagedAttention assumed MHA. DeepSeek-V4 says that assumption
+ *             is broken.", sections "Block size is not a tuning knob here"
+ *             (64-token blocks) and "What DeepSeek-V4 breaks" (bf16 rope next
+ *             to fp8 content within one block).
+ *   [REDKNOT] "RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4
+ *             Long-Context Serving", Abstract and sections 1-3 (query-side
+ *             RoPE relocation, Local/Global heads, protected rows, sliced
+ *             projection before one shared output projection, Equation 4).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named dev_* or typed as tensors are DEVICE pointers to memory
+ *     the caller owns (allocated by the caller, e.g. through PyTorch). The
+ *     library never allocates, frees or synchronises; every call only
+ *     enqueues kernels.
+ *   - stream is a hipStream_t (passed as void*; NULL = the null stream).
+ *     Every call only enqueues kernels on that stream and returns; results
+ *     are ready when the stream reaches that point.
+ *   - Return value: MLA_OK, or a negative mla_status. Arguments are checked
+ *     on the host before anything is enqueued; on error nothing is enqueued
+ *     and mla_last_error() describes the problem (thread-local string).
+ *   - Geometry is fixed: d_c = 512, d_rope = 64, d_nope = d_v = 128,
+ *     d_qk = 192, block = 64 tokens. Strides are in ELEMENTS of the stated
+ *     dtype. Base pointers must be 16-byte aligned and row strides multiples
+ *     of 8 elements (16 bytes for bf16).
+ *   - bf16 is bfloat16 (top half of IEEE fp32); fp8 is OCP E4M3FN (max 448);
+ *     fp32 is IEEE single.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad stride/alignment */
+  MLA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (dtype, geometry)  */
+  MLA_ERR_LAUNCH = -3,        /* the HIP runtime refused the launch           */
+  MLA_ERR_OUT_OF_RANGE = -4   /* device-side: a block id outside the pool     */
+} mla_status;
+
+typedef enum {
+  MLA_DTYPE_BF16 = 0,
+  MLA_DTYPE_FP8_E4M3 = 1,
+  MLA_DTYPE_FP32 = 2
+} mla_dtype;
+
+typedef enum {
+  MLA_ROPE_INTERLEAVED = 0,   /* pair k = elements (2k, 2k+1)  */
+  MLA_ROPE_HALF = 1           /* pair k = elements (k, k + 32) */
+} mla_rope_pairing;
+
+/* Message describing the last error returned on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* ABI version, currently 1. */
+int mla_abi_version(void);
+
+/*
+ * mla_gather_context -- [DSMLA] 4.4 step 1 (_gather_cache); block addressing
+ * per [PAGED] "Block size is not a tuning knob here".
+ *
+ * For each request b in [0, batch), copies the latent records of its tokens
+ * t in [chunk_start[b], chunk_start[b] + chunk_len[b]) into consecutive rows
+ * [cu_out[b], cu_out[b] + chunk_len[b]) of out_latent. Token t lives in
+ * physical block block_table[b * bt_stride + t / 64] at slot t % 64.
+ *
+ *   pool        device; cache_dtype == MLA_DTYPE_BF16: bf16 [num_blocks][64][576]
+ *               (record = c_kv[512] then k_rope[64]).
+ *               cache_dtype == MLA_DTYPE_FP8_E4M3: bytes [num_blocks][41216]; per
+ *               block c_kv codes [64][512] at byte 0, k_rope bf16 [64][64] at
+ *               byte 32768, per-token fp32 scale [64] at byte 40960.
+ *   block_table device int32 [batch][bt_stride].
+ *   chunk_start, chunk_len, cu_out  device int32 [batch], [batch], [batch+1].
+ *   max_len     host; >= every chunk_len[b] (sizes the launch).
+ *   out_latent  device bf16 [cu_out[batch]][576], row stride 576.
+ *   dev_status  device int32 or NULL. A block id outside [0, num_blocks)
+ *               makes the kernel write zeros for that token and store
+ *               MLA_ERR_OUT_OF_RANGE into *dev_status (never cleared by the
+ *               library; the caller zeroes it).
+ * bf16 cache: out is a bit copy. fp8 cache: c_kv out = bf16_rne(fp32
+ * product of the decoded code and the token's scale), k_rope copied.
+ */
+int mla_gather_context(const void* pool, int cache_dtype, int num_blocks,
+                       const int32_t* block_table, int64_t bt_stride,
+                       const int32_t* chunk_start, const int32_t* chunk_len,
+                       const int32_t* cu_out, int batch, int max_len,
+                       void* out_latent, int32_t* dev_status, void* stream);
+
+/*
+ * mla_pack_weight_t -- weight layout transform done once at load time (not
+ * part of the per-prefill path): out[n][k] = w[k][n] for a bf16 matrix
+ * w [K][N] (row-major). Used to store kv_b_proj [512][H*256] and the sliced
+ * and shared output projections as [N][K], so that both MFMA operands read
+ * contiguous K. K and N must be multiples of 8.
+ */
+int mla_pack_weight_t(const void* w, int K, int N, void* out, void* stream);
+
+/*
+ * mla_decompress -- [DSMLA] 4.4 step 2: kv = c_kv . kv_b_proj, split into
+ * per-head k_nope and v.
+ *
+ *   latent      device bf16 [n_tokens][ld_latent]; c_kv = columns 0..511.
+ *   w_t         device bf16 [H_total*256][512]: kv_b_proj packed by
+ *               mla_pack_weight_t (row j = output column j; columns
+ *               [0, H*128) are W_UK of heads 0..H-1, [H*128, H*256) W_UV).
+ *   heads       [h_begin, h_end) of H_total are produced, hs = h - h_begin.
+ *   k_nope      device bf16; k_nope[hs * k_head_stride + t * 128 + d].
+ *   v           device bf16; v[hs * v_head_stride + t * 128 + d].
+ *               Head strides >= n_tokens * 128 (head-major, so one head's
+ *               keys of a chunk are contiguous).
+ * fp32 accumulation, one bf16 rounding of each output.
+ */
+int mla_decompress(const void* latent, int64_t ld_latent, int n_tokens,
+                   const void* w_t, int H_total, int h_begin, int h_end,
+                   void* k_nope, int64_t k_head_stride,
+                   void* v, int64_t v_head_stride, void* stream);
+
+/*
+ * mla_prefill_attn -- [DSMLA] 4.4 steps 3-4 (attention returning (out, lse))
+ * for the context pass (causal = 0) and the extend pass (causal = 1) of
+ * [DSMLA] 4.2.
+ *
+ * For request b: logical query rows i in [0, n_q), n_q = cu_q[b+1]-cu_q[b];
+ * keys t in [cu_k[b], cu_k[b+1]), n_k = cu_k[b+1]-cu_k[b]. For head h in
+ * [h_begin, h_end) (hs = h - h_begin):
+ *   s_t = scale * (q_nope . k_nope[hs][t] + q_rope . k_rope[t])
+ * where q = q[p * q_row_stride + h * 192 + (0..191)] (nope first) with
+ * p = q_row_ids ? q_row_ids[cu_q[b] + i] : cu_q[b] + i, and k_rope[t] =
+ * latent[t * ld_latent + 512 + (0..63)] shared by every head. causal = 1
+ * keeps key t iff (t - cu_k[b]) <= i + n_k - n_q (bottom-right aligned).
+ *   out[(cu_q[b]+i) * out_row_stride + hs * 128 + d] = sum_t softmax(s)_t v[t][d]
+ *   lse[(cu_q[b]+i) * lse_row_stride + hs]            = ln sum_t e^{s_t}
+ * with v[t] = v[hs * v_head_stride + t * 128 + (0..127)].
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *   q          device bf16; k_nope / v as written by mla_decompress
+ *              (row t of head hs at hs * head_stride + t * 128).
+ *   out_dtype  MLA_DTYPE_BF16 or MLA_DTYPE_FP32.
+ *   max_q      host; >= every n_q (sizes the launch).
+ */
+int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                     const void* k_nope, int64_t k_head_stride,
+                     const void* v, int64_t v_head_stride,
+                     const void* latent, int64_t ld_latent,
+                     const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_row_ids,
+                     int batch, int max_q, float scale, int causal,
+                     void* out, int out_dtype, int64_t out_row_stride,
+                     float* lse, int64_t lse_row_stride, void* stream);
+
+/*
+ * mla_merge_states -- [DSMLA] 4.3 (merge_attn_states), with the merged lse
+ * m + ln(e^{la-m} + e^{lb-m}) that the chunk loop of 4.4 consumes.
+ *
+ * rows independent states of 128 values: out_x[r * 128 + d], lse_x[r].
+ *   out = (wa * out_a + wb * out_b) / (wa + wb), wa = e^{lse_a - m},
+ *   wb = e^{lse_b - m}, m = max(lse_a, lse_b); lse = m + ln(wa + wb).
+ * A side with lse = -inf contributes nothing (its out is not read); both
+ * -inf gives out = 0, lse = -inf. out may alias out_a or out_b and lse_out
+ * may alias lse_a or lse_b (each element is read before it is written).
+ * dtype_a, dtype_b, dtype_out: MLA_DTYPE_BF16 or MLA_DTYPE_FP32.
+ */
+int mla_merge_states(const void* out_a, int dtype_a, const float* lse_a,
+                     const void* out_b, int dtype_b, const float* lse_b,
+                     int64_t rows, void* out, int dtype_out, float* lse_out,
+                     void* stream);
+
+/*
+ * mla_rope_relocate_q -- [REDKNOT] Abstract and section 2 (query-side RoPE
+ * relocation): for every row r < T and head h < H, the rope part
+ * q[r * q_row_stride + h * 192 + 128 + (0..63)] is rotated by the angle
+ * -delta * rope_base^(-2k/64) for pair k (pairing selects which elements form
+ * pair k), moving a query at request position p to position p - delta, the
+ * canonical frame of a document placed at request offset delta. The 32
+ * cos/sin values are computed on the host in fp64 and applied in fp32; the
+ * result is rounded to bf16 and written to q_out (same layout and stride).
+ * q_out may equal q_in (in place); otherwise the nope part (elements
+ * 0..127 of each head) is copied unchanged.
+ */
+int mla_rope_relocate_q(const void* q_in, void* q_out, int64_t q_row_stride, int T, int H,
+                        int64_t delta, double rope_base, int pairing, void* stream);
+
+/*
+ * mla_head_partition_merge -- [REDKNOT] sections 1-3 (Equation 4): Local
+ * rows come from the artifact except protected rows, which are replaced by
+ * their recomputation (not added); Local and Global head outputs go through
+ * their slices of the first output projection, add, and pass through the
+ * one shared second projection:
+ *   O_L[r] = r in prot_rows ? rec_out[index of r] : art_out[r]
+ *   z = O_L . W_aL + O_G . W_aG      (bf16 [T][d_mid], fp32 accumulate)
+ *   y = z . W_b                      (bf16 [T][d_model])
+ *   art_out   device bf16 [T][HL][128];  rec_out bf16 [P][HL][128];
+ *   prot_rows device int32 [P], strictly increasing, each < T;
+ *   glob_out  device bf16 [T][HG][128];
+ *   wa_t      device bf16 [d_mid][(HL+HG)*128]: [W_aL ; W_aG] stacked along
+ *             K (Local rows first) and packed by mla_pack_weight_t;
+ *   wb_t      device bf16 [d_model][d_mid]: W_b packed by mla_pack_weight_t;
+ *   z         device bf16 [T][d_mid], caller-owned workspace.
+ */
+int mla_head_partition_merge(const void* art_out, const void* rec_out,
+                             const int32_t* prot_rows, int P, const void* glob_out,
+                             const void* wa_t, const void* wb_t, int T, int HL, int HG,
+                             int d_mid, int d_model, void* z, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,147 @@
+"""ctypes binding of libmla.so: argument marshalling only.
+
+Every function takes device pointers (ints) or torch tensors (their
+data_ptr() is passed) and a stream handle; it raises MlaError when the
+library returns a non-zero status. No computation happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_LAUNCH = -3
+MLA_ERR_OUT_OF_RANGE = -4
+
+DTYPE_BF16 = 0
+DTYPE_FP8_E4M3 = 1
+DTYPE_FP32 = 2
+
+ROPE_INTERLEAVED = 0
+ROPE_HALF = 1
+
+EXPORTS = (
+    "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_pack_weight_t",
+    "mla_decompress", "mla_prefill_attn", "mla_merge_states", "mla_rope_relocate_q",
+    "mla_head_partition_merge",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} -> {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int
+I64 = ctypes.c_int64
+F32 = ctypes.c_float
+F64 = ctypes.c_double
+
+_SIGS = {
+    "mla_gather_context": [P, I32, I32, P, I64, P, P, P, I32, I32, P, P, P],
+    "mla_pack_weight_t": [P, I32, I32, P, P],
+    "mla_decompress": [P, I64, I32, P, I32, I32, I32, P, I64, P, I64, P],
+    "mla_prefill_attn": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
+                         I32, I32, F32, I32, P, I32, I64, P, I64, P],
+    "mla_merge_states": [P, I32, P, P, I32, P, I64, P, I32, P, P],
+    "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
+    "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
+}
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mla_long_context_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_abi_version.restype = I32
+    lib.mla_abi_version.argtypes = []
+    for name, args in _SIGS.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = I32
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _call(name, *args):
+    lib = load()
+    rc = getattr(lib, name)(*args)
+    if rc != MLA_OK:
+        raise MlaError(name, rc, lib.mla_last_error().decode())
+    return rc
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def mla_gather_context(pool, cache_dtype, num_blocks, block_table, bt_stride, chunk_start,
+                       chunk_len, cu_out, batch, max_len, out_latent, dev_status=None, stream=None):
+    return _call("mla_gather_context", _ptr(pool), cache_dtype, num_blocks, _ptr(block_table),
+                 bt_stride, _ptr(chunk_start), _ptr(chunk_len), _ptr(cu_out), batch, max_len,
+                 _ptr(out_latent), _ptr(dev_status), _stream(stream))
+
+
+def mla_pack_weight_t(w, K, N, out, stream=None):
+    return _call("mla_pack_weight_t", _ptr(w), K, N, _ptr(out), _stream(stream))
+
+
+def mla_decompress(latent, ld_latent, n_tokens, w_t, H_total, h_begin, h_end, k_nope,
+                   k_head_stride, v, v_head_stride, stream=None):
+    return _call("mla_decompress", _ptr(latent), ld_latent, n_tokens, _ptr(w_t), H_total, h_begin,
+                 h_end, _ptr(k_nope), k_head_stride, _ptr(v), v_head_stride, _stream(stream))
+
+
+def mla_prefill_attn(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,
+                     v_head_stride, latent, ld_latent, cu_q, cu_k, q_row_ids, batch, max_q,
+                     scale, causal, out, out_dtype, out_row_stride, lse, lse_row_stride,
+                     stream=None):
+    return _call("mla_prefill_attn", _ptr(q), q_row_stride, H_q, h_begin, h_end, _ptr(k_nope),
+                 k_head_stride, _ptr(v), v_head_stride, _ptr(latent), ld_latent, _ptr(cu_q),
+                 _ptr(cu_k), _ptr(q_row_ids), batch, max_q, float(scale), int(causal), _ptr(out),
+                 out_dtype, out_row_stride, _ptr(lse), lse_row_stride, _stream(stream))
+
+
+def mla_merge_states(out_a, dtype_a, lse_a, out_b, dtype_b, lse_b, rows, out, dtype_out, lse_out,
+                     stream=None):
+    return _call("mla_merge_states", _ptr(out_a), dtype_a, _ptr(lse_a), _ptr(out_b), dtype_b,
+                 _ptr(lse_b), rows, _ptr(out), dtype_out, _ptr(lse_out), _stream(stream))
+
+
+def mla_rope_relocate_q(q_in, q_out, q_row_stride, T, H, delta, rope_base=10000.0,
+                        pairing=ROPE_INTERLEAVED, stream=None):
+    return _call("mla_rope_relocate_q", _ptr(q_in), _ptr(q_out), q_row_stride, T, H, int(delta),
+                 float(rope_base), pairing, _stream(stream))
+
+
+def mla_head_partition_merge(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_t, T, HL, HG,
+                             d_mid, d_model, z, y, stream=None):
+    return _call("mla_head_partition_merge", _ptr(art_out), _ptr(rec_out), _ptr(prot_rows), P,
+                 _ptr(glob_out), _ptr(wa_t), _ptr(wb_t), T, HL, HG, d_mid, d_model, _ptr(z),
+                 _ptr(y), _stream(stream))

@@ -1,0 +1,31 @@
+// Thread-local error reporting for the C ABI.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "mla_internal.h"
+
+namespace {
+thread_local char g_err[512] = {0};
+}
+
+void mla_set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void mla_clear_error() { g_err[0] = 0; }
+
+int mla_check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    mla_set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+    return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+extern "C" const char* mla_last_error(void) { return g_err; }
+
+extern "C" int mla_abi_version(void) { return 1; }

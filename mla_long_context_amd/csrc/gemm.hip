@@ -1,0 +1,300 @@
+// bf16 MFMA GEMM core for gfx950, D[t][n] = sum_k A[t][k] * Bt[n][k], with
+// both operands K-contiguous (weights are packed once by mla_pack_weight_t).
+// Used for:
+//   * kv_b_proj decompression (DeepSeek MLA -- Prefix Cache and Chunked
+//     Prefill, section 4.4 step 2): A = c_kv rows of the gathered latent,
+//     Bt = packed [W_UK | W_UV], output split per head into k_nope and v.
+//   * the sliced first output projection and the shared second projection of
+//     the Local/Global head partition (RedKnot-MLA, sections 1-3, Equation 4),
+//     with protected-row replacement fused into the A-operand load.
+//
+// Tiling: 256 threads (4 wavefronts of 64), a 128 x 128 output tile per
+// workgroup, K in steps of 64 through double-buffered LDS; each wavefront
+// owns a 64 x 64 sub-tile as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks. The MFMA
+// is issued as D^T = Bt_frag x A_frag so that each lane ends up holding four
+// consecutive output columns of one row, which the epilogue packs into 8-byte
+// LDS writes before 16-byte coalesced global stores.
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kLdsK = BK + 8;            // padded row (elements): 144 B, conflict-free b128 reads
+constexpr int kLdsC = BN + 8;            // padded epilogue row
+constexpr int kTileElems = BM * kLdsK;   // one operand tile
+
+// ---------------------------------------------------------------- problem policies
+
+struct DecompressP {
+  const uint16_t* lat; int64_t ld; int M;
+  const uint16_t* wt; int H_total, h_begin, Hsel;
+  uint16_t* k; int64_t khs; uint16_t* v; int64_t vhs;
+
+  __device__ int rows() const { return M; }
+  __device__ int K() const { return kDc; }
+  __device__ void a_rows(int t, const uint16_t*& pl, const uint16_t*& pg, int& ksplit) const {
+    pl = t < M ? lat + (int64_t)t * ld : nullptr;
+    pg = nullptr;
+    ksplit = kDc;
+  }
+  __device__ const uint16_t* b_row(int nt, int r) const {
+    const int h = h_begin + (nt < Hsel ? nt : nt - Hsel);
+    const int64_t row = (nt < Hsel ? 0 : (int64_t)H_total * kDnope) + (int64_t)h * kDnope + r;
+    return wt + row * kDc;
+  }
+  __device__ void store(int t, int nt, int vec, u32x4 val) const {
+    uint16_t* dst = nt < Hsel ? k + (int64_t)nt * khs : v + (int64_t)(nt - Hsel) * vhs;
+    *reinterpret_cast<u32x4*>(dst + (int64_t)t * kDnope + vec * 8) = val;
+  }
+};
+
+// A = [O_L | O_G] with O_L rows from the artifact or, for protected rows, from
+// the recomputation; Bt = packed [W_aL ; W_aG]; D = z.
+struct SlicedProjP {
+  const uint16_t* art; const uint16_t* rec; const int32_t* prot; int P;
+  const uint16_t* glob; int T, HL, HG;
+  const uint16_t* wt; int Kt;       // (HL+HG)*128
+  uint16_t* z; int ldz;
+
+  __device__ int rows() const { return T; }
+  __device__ int K() const { return Kt; }
+  __device__ void a_rows(int t, const uint16_t*& pl, const uint16_t*& pg, int& ksplit) const {
+    ksplit = HL * kDv;
+    if (t >= T) { pl = pg = nullptr; return; }
+    // binary search of t among the strictly increasing protected rows
+    int lo = 0, hi = P;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (prot[mid] < t) lo = mid + 1; else hi = mid;
+    }
+    const bool is_prot = lo < P && prot[lo] == t;
+    pl = is_prot ? rec + (int64_t)lo * HL * kDv : art + (int64_t)t * HL * kDv;
+    pg = glob + (int64_t)t * HG * kDv - ksplit;   // indexed with the global k
+  }
+  __device__ const uint16_t* b_row(int nt, int r) const { return wt + ((int64_t)nt * BN + r) * Kt; }
+  __device__ void store(int t, int nt, int vec, u32x4 val) const {
+    *reinterpret_cast<u32x4*>(z + (int64_t)t * ldz + nt * BN + vec * 8) = val;
+  }
+};
+
+// Plain row-major A [T][K] times packed Bt [N][K] into D [T][N].
+struct PlainP {
+  const uint16_t* a; int T; int Kt; const uint16_t* wt; uint16_t* d; int ldd;
+
+  __device__ int rows() const { return T; }
+  __device__ int K() const { return Kt; }
+  __device__ void a_rows(int t, const uint16_t*& pl, const uint16_t*& pg, int& ksplit) const {
+    pl = t < T ? a + (int64_t)t * Kt : nullptr;
+    pg = nullptr;
+    ksplit = Kt;
+  }
+  __device__ const uint16_t* b_row(int nt, int r) const { return wt + ((int64_t)nt * BN + r) * Kt; }
+  __device__ void store(int t, int nt, int vec, u32x4 val) const {
+    *reinterpret_cast<u32x4*>(d + (int64_t)t * ldd + nt * BN + vec * 8) = val;
+  }
+};
+
+// ---------------------------------------------------------------- kernel
+
+template <class P>
+__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(P p, int n_mt, int n_nt) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kTileElems];   // A0 B0 A1 B1
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // tile of this workgroup (m fastest within an XCD's contiguous range)
+  const uint32_t work = xcd_remap(blockIdx.x, (uint32_t)(n_mt * n_nt));
+  const int mt = (int)(work % (uint32_t)n_mt);
+  const int nt = (int)(work / (uint32_t)n_mt);
+  const int t0 = mt * BM;
+
+  // each thread loads 4 rows x one 16-byte vector of the A and B tiles per k-step
+  const int lrow = tid >> 3, lvec = tid & 7;
+  const uint16_t* apl[4];
+  const uint16_t* apg[4];
+  const uint16_t* bp[4];
+  int ksplit = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p.a_rows(t0 + lrow + 32 * i, apl[i], apg[i], ksplit);
+    bp[i] = p.b_row(nt, lrow + 32 * i);
+  }
+  const int K = p.K();
+  const int nk = K / BK;
+
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+    const int k = kt * BK + lvec * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* src = k < ksplit ? apl[i] : apg[i];
+      ra[i] = src ? *reinterpret_cast<const u32x4*>(src + k) : u32x4{0u, 0u, 0u, 0u};
+      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* As = lds + (2 * buf) * kTileElems;
+    uint16_t* Bs = lds + (2 * buf + 1) * kTileElems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(As + (lrow + 32 * i) * kLdsK + lvec * 8) = ra[i];
+      *reinterpret_cast<u32x4*>(Bs + (lrow + 32 * i) * kLdsK + lvec * 8) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint16_t* As = lds + (2 * cur) * kTileElems;
+    const uint16_t* Bs = lds + (2 * cur + 1) * kTileElems;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        af[tb] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + tb * 32 + l32) * kLdsK + ks * 16 + g * 8);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + nb * 32 + l32) * kLdsK + ks * 16 + g * 8);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[tb], acc[nb][tb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds D^T rows n = 8*(i/4) + 4*g + (i%4), column t = l32
+  uint16_t* Cs = lds;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = wm * 64 + tb * 32 + l32;
+        const int n = wn * 64 + nb * 32 + 8 * q + 4 * g;
+        u32x2 w;
+        w.x = pack_bf16x2(acc[nb][tb][4 * q + 0], acc[nb][tb][4 * q + 1]);
+        w.y = pack_bf16x2(acc[nb][tb][4 * q + 2], acc[nb][tb][4 * q + 3]);
+        *reinterpret_cast<u32x2*>(Cs + t * kLdsC + n) = w;
+      }
+  __syncthreads();
+  const int M = p.rows();
+#pragma unroll
+  for (int i = 0; i < (BM * BN / 8) / kThreads; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx >> 4, vec = idx & 15;
+    if (t0 + r < M) p.store(t0 + r, nt, vec, *reinterpret_cast<const u32x4*>(Cs + r * kLdsC + vec * 8));
+  }
+}
+
+template <class P>
+int launch_gemm(const P& p, int M, int N, hipStream_t s, const char* what) {
+  const int n_mt = (M + BM - 1) / BM, n_nt = N / BN;
+  const int64_t total = (int64_t)n_mt * n_nt;
+  MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "%s: problem too large", what);
+  hipLaunchKernelGGL(gemm_nt_kernel<P>, dim3((unsigned)total), dim3(kThreads), 0, s, p, n_mt, n_nt);
+  return mla_check_launch(what);
+}
+
+// ---------------------------------------------------------------- weight pack (transpose)
+
+constexpr int kTr = 64;
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ w, int K, int N,
+                                                         uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[kTr][kTr + 2];
+  const int k0 = blockIdx.y * kTr, n0 = blockIdx.x * kTr;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < kTr; r += 4) {
+    const int k = k0 + r, n = n0 + tx;
+    tile[r][tx] = (k < K && n < N) ? w[(int64_t)k * N + n] : 0;
+  }
+  __syncthreads();
+  for (int r = ty; r < kTr; r += 4) {
+    const int n = n0 + r, k = k0 + tx;
+    if (n < N && k < K) out[(int64_t)n * K + k] = tile[tx][r];
+  }
+}
+
+}  // namespace
+
+extern "C" int mla_pack_weight_t(const void* w, int K, int N, void* out, void* stream) {
+  mla_clear_error();
+  MLA_REQUIRE(w && out, MLA_ERR_INVALID_ARG, "mla_pack_weight_t: null pointer argument");
+  MLA_REQUIRE(K > 0 && N > 0 && K % 8 == 0 && N % 8 == 0, MLA_ERR_INVALID_ARG,
+              "mla_pack_weight_t: K (%d) and N (%d) must be positive multiples of 8", K, N);
+  MLA_REQUIRE(w != out, MLA_ERR_INVALID_ARG, "mla_pack_weight_t: in-place transpose is not supported");
+  dim3 g((N + kTr - 1) / kTr, (K + kTr - 1) / kTr);
+  hipLaunchKernelGGL(transpose_kernel, g, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(w), K, N, static_cast<uint16_t*>(out));
+  return mla_check_launch("mla_pack_weight_t");
+}
+
+extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_tokens,
+                              const void* w_t, int H_total, int h_begin, int h_end,
+                              void* k_nope, int64_t k_head_stride,
+                              void* v, int64_t v_head_stride, void* stream) {
+  mla_clear_error();
+  MLA_REQUIRE(n_tokens >= 0, MLA_ERR_INVALID_ARG, "mla_decompress: n_tokens must be >= 0");
+  MLA_REQUIRE(H_total > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_total, MLA_ERR_INVALID_ARG,
+              "mla_decompress: need 0 <= h_begin (%d) < h_end (%d) <= H_total (%d)", h_begin, h_end, H_total);
+  if (n_tokens == 0) return MLA_OK;
+  MLA_REQUIRE(latent && w_t && k_nope && v, MLA_ERR_INVALID_ARG, "mla_decompress: null pointer argument");
+  MLA_REQUIRE(mla_aligned16(latent) && mla_aligned16(w_t) && mla_aligned16(k_nope) && mla_aligned16(v),
+              MLA_ERR_INVALID_ARG, "mla_decompress: pointers must be 16-byte aligned");
+  MLA_REQUIRE(ld_latent >= kDc && ld_latent % 8 == 0, MLA_ERR_INVALID_ARG,
+              "mla_decompress: ld_latent (%lld) must be >= 512 and a multiple of 8", (long long)ld_latent);
+  const int Hsel = h_end - h_begin;
+  MLA_REQUIRE(k_head_stride >= (int64_t)n_tokens * kDnope && v_head_stride >= (int64_t)n_tokens * kDv &&
+                  k_head_stride % 8 == 0 && v_head_stride % 8 == 0,
+              MLA_ERR_INVALID_ARG, "mla_decompress: head strides must be >= n_tokens*128 and multiples of 8");
+  DecompressP p{static_cast<const uint16_t*>(latent), ld_latent, n_tokens,
+                static_cast<const uint16_t*>(w_t), H_total, h_begin, Hsel,
+                static_cast<uint16_t*>(k_nope), k_head_stride, static_cast<uint16_t*>(v), v_head_stride};
+  return launch_gemm(p, n_tokens, 2 * Hsel * BN, reinterpret_cast<hipStream_t>(stream), "mla_decompress");
+}
+
+extern "C" int mla_head_partition_merge(const void* art_out, const void* rec_out,
+                                        const int32_t* prot_rows, int P, const void* glob_out,
+                                        const void* wa_t, const void* wb_t, int T, int HL, int HG,
+                                        int d_mid, int d_model, void* z, void* y, void* stream) {
+  mla_clear_error();
+  MLA_REQUIRE(T >= 0 && P >= 0 && P <= T && HL >= 0 && HG >= 0 && HL + HG > 0, MLA_ERR_INVALID_ARG,
+              "mla_head_partition_merge: need T >= 0, 0 <= P <= T, HL, HG >= 0, HL + HG > 0");
+  if (T == 0) return MLA_OK;
+  MLA_REQUIRE(wa_t && wb_t && z && y && (HL == 0 || art_out) && (HG == 0 || glob_out) &&
+                  (P == 0 || (rec_out && prot_rows)),
+              MLA_ERR_INVALID_ARG, "mla_head_partition_merge: null pointer argument");
+  MLA_REQUIRE(d_mid > 0 && d_model > 0 && d_mid % BN == 0 && d_model % BN == 0, MLA_ERR_UNSUPPORTED,
+              "mla_head_partition_merge: d_mid (%d) and d_model (%d) must be multiples of 128", d_mid, d_model);
+  MLA_REQUIRE((HL * kDv) % BK == 0, MLA_ERR_UNSUPPORTED, "mla_head_partition_merge: HL*128 must be a multiple of 64");
+  const void* ptrs[] = {art_out, rec_out, glob_out, wa_t, wb_t, z, y};
+  for (const void* q : ptrs) MLA_REQUIRE(!q || mla_aligned16(q), MLA_ERR_INVALID_ARG,
+                                         "mla_head_partition_merge: pointers must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SlicedProjP p1{static_cast<const uint16_t*>(art_out), static_cast<const uint16_t*>(rec_out), prot_rows, P,
+                 static_cast<const uint16_t*>(glob_out), T, HL, HG, static_cast<const uint16_t*>(wa_t),
+                 (HL + HG) * kDv, static_cast<uint16_t*>(z), d_mid};
+  int rc = launch_gemm(p1, T, d_mid, s, "mla_head_partition_merge (sliced projection)");
+  if (rc != MLA_OK) return rc;
+  PlainP p2{static_cast<const uint16_t*>(z), T, d_mid, static_cast<const uint16_t*>(wb_t),
+            static_cast<uint16_t*>(y), d_model};
+  return launch_gemm(p2, T, d_model, s, "mla_head_partition_merge (shared projection)");
+}

@@ -1,0 +1,128 @@
+// Log-sum-exp merge of two attention states (DeepSeek MLA -- Prefix Cache and
+// Chunked Prefill, section 4.3 merge_attn_states; the merged lse that the
+// chunk loop of section 4.4 consumes is m + ln(wa + wb)).
+//
+// HBM-bound. 16 lanes own one 128-wide state row, 8 values per lane, so a
+// wavefront streams 4 rows of each operand with 16- or 32-byte accesses.
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int kDt>
+struct Vec8;
+template <>
+struct Vec8<MLA_DTYPE_BF16> {
+  __device__ static void load(const void* p, int64_t off, float* f) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + off);
+    f[0] = bf16_bits_to_f32(u.x & 0xffffu); f[1] = bf16_bits_to_f32(u.x >> 16);
+    f[2] = bf16_bits_to_f32(u.y & 0xffffu); f[3] = bf16_bits_to_f32(u.y >> 16);
+    f[4] = bf16_bits_to_f32(u.z & 0xffffu); f[5] = bf16_bits_to_f32(u.z >> 16);
+    f[6] = bf16_bits_to_f32(u.w & 0xffffu); f[7] = bf16_bits_to_f32(u.w >> 16);
+  }
+  __device__ static void store(void* p, int64_t off, const float* f) {
+    u32x4 u;
+    u.x = pack_bf16x2(f[0], f[1]); u.y = pack_bf16x2(f[2], f[3]);
+    u.z = pack_bf16x2(f[4], f[5]); u.w = pack_bf16x2(f[6], f[7]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p) + off) = u;
+  }
+};
+template <>
+struct Vec8<MLA_DTYPE_FP32> {
+  __device__ static void load(const void* p, int64_t off, float* f) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + off);
+    const f32x4 a = q[0], b = q[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ static void store(void* p, int64_t off, const float* f) {
+    f32x4* q = reinterpret_cast<f32x4*>(static_cast<float*>(p) + off);
+    q[0] = f32x4{f[0], f[1], f[2], f[3]};
+    q[1] = f32x4{f[4], f[5], f[6], f[7]};
+  }
+};
+
+template <int kDa, int kDb, int kDo>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const void* oa, const float* la,
+                                                          const void* ob, const float* lb,
+                                                          int64_t rows, void* out, float* lo) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = gid >> 4;
+  const int part = (int)(gid & 15);
+  if (row >= rows) return;
+  const float a = la[row], b = lb[row];
+  const float m = fmaxf(a, b);
+  const int64_t off = row * kDv + part * 8;
+  float r[8];
+  float lse;
+  if (m == -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = 0.f;
+    lse = -INFINITY;
+  } else {
+    const float wa = (a == -INFINITY) ? 0.f : expf(a - m);
+    const float wb = (b == -INFINITY) ? 0.f : expf(b - m);
+    const float s = wa + wb;
+    const float ca = wa / s, cb = wb / s;
+    float fa[8], fb[8];
+    if (wa != 0.f) Vec8<kDa>::load(oa, off, fa);
+    else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fa[j] = 0.f;
+    }
+    if (wb != 0.f) Vec8<kDb>::load(ob, off, fb);
+    else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = ca * fa[j] + cb * fb[j];
+    lse = m + logf(s);
+  }
+  Vec8<kDo>::store(out, off, r);
+  if (part == 0) lo[row] = lse;
+}
+
+template <int kDa, int kDb>
+int launch_o(int dto, dim3 g, hipStream_t s, const void* oa, const float* la, const void* ob,
+             const float* lb, int64_t rows, void* out, float* lo) {
+  if (dto == MLA_DTYPE_BF16)
+    hipLaunchKernelGGL((merge_kernel<kDa, kDb, MLA_DTYPE_BF16>), g, dim3(kThreads), 0, s, oa, la, ob, lb, rows, out, lo);
+  else
+    hipLaunchKernelGGL((merge_kernel<kDa, kDb, MLA_DTYPE_FP32>), g, dim3(kThreads), 0, s, oa, la, ob, lb, rows, out, lo);
+  return mla_check_launch("mla_merge_states");
+}
+
+template <int kDa>
+int launch_b(int dtb, int dto, dim3 g, hipStream_t s, const void* oa, const float* la,
+             const void* ob, const float* lb, int64_t rows, void* out, float* lo) {
+  if (dtb == MLA_DTYPE_BF16) return launch_o<kDa, MLA_DTYPE_BF16>(dto, g, s, oa, la, ob, lb, rows, out, lo);
+  return launch_o<kDa, MLA_DTYPE_FP32>(dto, g, s, oa, la, ob, lb, rows, out, lo);
+}
+
+bool ok_dt(int d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP32; }
+
+}  // namespace
+
+extern "C" int mla_merge_states(const void* out_a, int dtype_a, const float* lse_a,
+                                const void* out_b, int dtype_b, const float* lse_b,
+                                int64_t rows, void* out, int dtype_out, float* lse_out,
+                                void* stream) {
+  mla_clear_error();
+  MLA_REQUIRE(rows >= 0, MLA_ERR_INVALID_ARG, "mla_merge_states: rows (%lld) must be >= 0", (long long)rows);
+  if (rows == 0) return MLA_OK;
+  MLA_REQUIRE(out_a && lse_a && out_b && lse_b && out && lse_out, MLA_ERR_INVALID_ARG,
+              "mla_merge_states: null pointer argument");
+  MLA_REQUIRE(ok_dt(dtype_a) && ok_dt(dtype_b) && ok_dt(dtype_out), MLA_ERR_UNSUPPORTED,
+              "mla_merge_states: dtypes must be bf16 or fp32 (got %d, %d, %d)", dtype_a, dtype_b, dtype_out);
+  MLA_REQUIRE(mla_aligned16(out_a) && mla_aligned16(out_b) && mla_aligned16(out), MLA_ERR_INVALID_ARG,
+              "mla_merge_states: state pointers must be 16-byte aligned");
+  MLA_REQUIRE(rows <= (int64_t)1 << 40, MLA_ERR_INVALID_ARG, "mla_merge_states: rows too large");
+  const int64_t threads = rows * 16;
+  dim3 g((unsigned)((threads + kThreads - 1) / kThreads));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype_a == MLA_DTYPE_BF16)
+    return launch_b<MLA_DTYPE_BF16>(dtype_b, dtype_out, g, s, out_a, lse_a, out_b, lse_b, rows, out, lse_out);
+  return launch_b<MLA_DTYPE_FP32>(dtype_b, dtype_out, g, s, out_a, lse_a, out_b, lse_b, rows, out, lse_out);
+}

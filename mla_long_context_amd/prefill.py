@@ -1,0 +1,269 @@
+"""Host orchestration of MLA prefill over the C ABI (argument marshalling and
+launch order only; every step runs in the HIP kernels of libmla.so).
+
+ChunkedPrefill -- the two-stage prefill of "DeepSeek MLA -- Prefix Cache and
+Chunked Prefill" (section 4.2) with the context-chunk loop of section 4.4:
+for each context chunk: gather -> decompress -> attention (no mask) -> merge;
+then the new tokens: decompress -> causal attention -> merge into the final
+(out, lse).
+
+ReusePrefill -- head-partitioned reuse of RedKnot-MLA (Abstract, sections
+1-3): queries are relocated into the document's canonical frame, Global heads
+are recomputed over the whole document for every row, Local heads only for
+the protected rows; Local rows come from the artifact with protected rows
+replaced, and the sliced first projection plus the shared second projection
+give the layer output (Equation 4).
+
+PyTorch provides device memory and the stream; nothing here computes.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+D_LAT = 576
+D_V = 128
+D_QK = 192
+
+
+def _bf16(a: np.ndarray, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def _i32(a, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
+
+
+def _cu(lens) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+
+
+def pack_weight(w_bits: np.ndarray, device, stream=None) -> torch.Tensor:
+    """Upload a bf16 [K][N] weight and store it as [N][K] with mla_pack_weight_t."""
+    w = _bf16(w_bits, device)
+    K, N = w.shape
+    wt = torch.empty((N, K), dtype=torch.bfloat16, device=device)
+    L.mla_pack_weight_t(w, K, N, wt, stream)
+    return wt
+
+
+def upload_pool(prob, device) -> torch.Tensor:
+    if prob.cache_dtype == "bf16":
+        return _bf16(prob.pool, device)
+    return torch.from_numpy(np.ascontiguousarray(prob.pool)).to(device)
+
+
+class ChunkedPrefill:
+    """Configs with a paged context and new (extend) tokens per request."""
+
+    def __init__(self, prob, device="cuda", chunk=None):
+        self.prob = prob
+        self.device = device
+        H = self.H = prob.H
+        self.B = prob.B
+        self.S = int(chunk or prob.chunk)
+        self.cache_dtype = L.DTYPE_BF16 if prob.cache_dtype == "bf16" else L.DTYPE_FP8_E4M3
+        self.pool = upload_pool(prob, device)
+        self.bt = _i32(prob.block_table, device)
+        self.ext = _bf16(prob.ext_latent, device)
+        self.q = _bf16(prob.q, device)
+        self.w_t = pack_weight(prob.W, device)
+        self.T = int(prob.ext_len.sum())
+        self.maxE = int(prob.ext_len.max()) if self.B else 0
+        self.cu_ext = _i32(_cu(prob.ext_len), device)
+        # chunk plan: chunk c of request r covers context tokens [c*S, min((c+1)*S, C_r))
+        C = prob.ctx_len.astype(np.int64)
+        n_chunks = int(max((int(c) + self.S - 1) // self.S for c in C)) if self.B else 0
+        self.chunks = []
+        for c in range(n_chunks):
+            start = np.full(self.B, c * self.S, dtype=np.int64)
+            ln = np.clip(C - c * self.S, 0, self.S)
+            self.chunks.append(dict(start=_i32(start, device), len=_i32(ln, device),
+                                    cu=_i32(_cu(ln), device), n=int(ln.sum()), max_len=int(ln.max())))
+        self.max_tok = max([ch["n"] for ch in self.chunks] + [self.T, 1])
+        max_ctx_tok = max([ch["n"] for ch in self.chunks] + [1])
+        self.lat_ws = torch.empty((max_ctx_tok, D_LAT), dtype=torch.bfloat16, device=device)
+        self.k_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
+        self.v_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
+        self.hstride = self.max_tok * D_V
+        T = max(self.T, 1)
+        self.tmp_o = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
+        self.tmp_l = torch.empty((T, H), dtype=torch.float32, device=device)
+        self.acc_o = torch.empty((T, H, D_V), dtype=torch.float32, device=device)
+        self.acc_l = torch.empty((T, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
+        self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    # one step of the path per call
+    def gather(self, ch, stream=None):
+        L.mla_gather_context(self.pool, self.cache_dtype, self.prob.num_blocks, self.bt,
+                             self.bt.shape[1], ch["start"], ch["len"], ch["cu"], self.B,
+                             ch["max_len"], self.lat_ws, self.dev_status, stream)
+
+    def decompress(self, latent, n, stream=None):
+        L.mla_decompress(latent, D_LAT, n, self.w_t, self.H, 0, self.H, self.k_ws, self.hstride,
+                         self.v_ws, self.hstride, stream)
+
+    def attend(self, latent, cu_k, causal, out, out_dtype, lse, stream=None):
+        L.mla_prefill_attn(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
+                           self.v_ws, self.hstride, latent, D_LAT, self.cu_ext, cu_k, None, self.B,
+                           self.maxE, self.prob.scale, causal, out, out_dtype, self.H * D_V, lse,
+                           self.H, stream)
+
+    def merge(self, a, da, la, b, db, lb, out, dout, lout, stream=None):
+        L.mla_merge_states(a, da, la, b, db, lb, self.T * self.H, out, dout, lout, stream)
+
+    def run(self, stream=None):
+        if self.T == 0:
+            return self.out, self.lse
+        for ci, ch in enumerate(self.chunks):
+            self.gather(ch, stream)
+            self.decompress(self.lat_ws, ch["n"], stream)
+            if ci == 0:
+                self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
+            else:
+                self.attend(self.lat_ws, ch["cu"], 0, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
+                self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16, self.tmp_l,
+                           self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
+        self.decompress(self.ext, self.T, stream)
+        if not self.chunks:
+            self.attend(self.ext, self.cu_ext, 1, self.out, L.DTYPE_BF16, self.lse, stream)
+        else:
+            self.attend(self.ext, self.cu_ext, 1, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
+            self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16, self.tmp_l,
+                       self.out, L.DTYPE_BF16, self.lse, stream)
+        return self.out, self.lse
+
+    # ---------------------------------------------------------------- accounting
+    def work(self) -> dict:
+        """Algorithmic work of one run: 2*512*256 flop per decompressed
+        (token, head); 640 flop per visible (row, key, head); bytes for the
+        HBM-bound steps (gather 2304 B/token bf16, 1796 B/token fp8; merge
+        per (row, head) = reads + writes of both states)."""
+        p, H = self.prob, self.H
+        C = p.ctx_len.astype(np.int64)
+        E = p.ext_len.astype(np.int64)
+        dec_tok = int(C.sum() + E.sum())
+        ctx_pairs = int((C * E).sum())
+        ext_pairs = int((E * (E + 1) // 2).sum())
+        n_merge = max(len(self.chunks) - 1, 0) + (1 if self.chunks else 0)
+        return dict(
+            dec_flops=2 * 512 * 256 * H * dec_tok,
+            attn_flops=640 * H * (ctx_pairs + ext_pairs),
+            ctx_attn_flops=640 * H * ctx_pairs,
+            ext_attn_flops=640 * H * ext_pairs,
+            gather_tokens=int(C.sum()),
+            gather_bytes=int(C.sum()) * (2304 if p.cache_dtype == "bf16" else 644 + 1152),
+            new_tokens=int(E.sum()), ctx_tokens=int(C.sum()), merges=n_merge,
+        )
+
+
+class ReusePrefill:
+    """Head-partitioned reuse over one document at canonical positions."""
+
+    def __init__(self, prob, device="cuda", chunk=None):
+        assert prob.is_reuse
+        self.prob = prob
+        self.device = device
+        H = self.H = prob.H
+        self.HL, self.HG = prob.n_local, H - prob.n_local
+        self.S = int(chunk or prob.chunk)
+        self.Ldoc = int(prob.ctx_len[0])
+        self.T = prob.T
+        self.P = int(len(prob.prot_rows))
+        self.d_mid = prob.WaL.shape[1]
+        self.d_model = prob.Wb.shape[1]
+        self.pool = upload_pool(prob, device)
+        self.bt = _i32(prob.block_table, device)
+        self.q = _bf16(prob.q, device)
+        self.q_rel = torch.empty_like(self.q)
+        self.w_t = pack_weight(prob.W, device)
+        self.art = _bf16(prob.art_out, device)
+        self.prot = _i32(prob.prot_rows, device)
+        self.wa_t = pack_weight(np.concatenate([prob.WaL, prob.WaG], axis=0), device)
+        self.wb_t = pack_weight(prob.Wb, device)
+        self.chunks = []
+        for s0 in range(0, self.Ldoc, self.S):
+            n = min(self.S, self.Ldoc - s0)
+            self.chunks.append(dict(start=_i32([s0], device), len=_i32([n], device),
+                                    cu=_i32([0, n], device), n=n))
+        S = self.S
+        self.lat_ws = torch.empty((S, D_LAT), dtype=torch.bfloat16, device=device)
+        self.k_ws = torch.empty((H, S, D_V), dtype=torch.bfloat16, device=device)
+        self.v_ws = torch.empty((H, S, D_V), dtype=torch.bfloat16, device=device)
+        self.hstride = S * D_V
+        T, P, HL, HG = self.T, max(self.P, 1), self.HL, self.HG
+        f32, bf = torch.float32, torch.bfloat16
+        self.cu_T = _i32([0, T], device)
+        self.cu_P = _i32([0, self.P], device)
+        self.acc_G = torch.empty((T, HG, D_V), dtype=f32, device=device)
+        self.accl_G = torch.empty((T, HG), dtype=f32, device=device)
+        self.tmp_G = torch.empty((T, HG, D_V), dtype=bf, device=device)
+        self.tmpl_G = torch.empty((T, HG), dtype=f32, device=device)
+        self.glob_out = torch.empty((T, HG, D_V), dtype=bf, device=device)
+        self.lse_G = torch.empty((T, HG), dtype=f32, device=device)
+        self.acc_L = torch.empty((P, HL, D_V), dtype=f32, device=device)
+        self.accl_L = torch.empty((P, HL), dtype=f32, device=device)
+        self.tmp_L = torch.empty((P, HL, D_V), dtype=bf, device=device)
+        self.tmpl_L = torch.empty((P, HL), dtype=f32, device=device)
+        self.rec_out = torch.empty((P, HL, D_V), dtype=bf, device=device)
+        self.lse_L = torch.empty((P, HL), dtype=f32, device=device)
+        self.z = torch.empty((T, self.d_mid), dtype=bf, device=device)
+        self.y = torch.empty((T, self.d_model), dtype=bf, device=device)
+        self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def _attn(self, h0, h1, cu_q, row_ids, n_rows, cu_k, out, out_dtype, lse, stream):
+        Hs = h1 - h0
+        L.mla_prefill_attn(self.q_rel, self.H * D_QK, self.H, h0, h1, self.k_ws[h0], self.hstride,
+                           self.v_ws[h0], self.hstride, self.lat_ws, D_LAT, cu_q, cu_k, row_ids, 1,
+                           n_rows, self.prob.scale, 0, out, out_dtype, Hs * D_V, lse, Hs, stream)
+
+    def run(self, stream=None):
+        p = self.prob
+        H, HL, HG, T, P = self.H, self.HL, self.HG, self.T, self.P
+        L.mla_rope_relocate_q(self.q, self.q_rel, H * D_QK, T, H, p.delta, p.rope_base,
+                              L.ROPE_INTERLEAVED, stream)
+        last = len(self.chunks) - 1
+        for ci, ch in enumerate(self.chunks):
+            L.mla_gather_context(self.pool, L.DTYPE_BF16, p.num_blocks, self.bt, self.bt.shape[1],
+                                 ch["start"], ch["len"], ch["cu"], 1, ch["n"], self.lat_ws,
+                                 self.dev_status, stream)
+            L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, H, 0, H, self.k_ws, self.hstride,
+                             self.v_ws, self.hstride, stream)
+            for (h0, h1, cu_q, rid, nr, acc, accl, tmp, tmpl, fin, finl) in (
+                    (HL, H, self.cu_T, None, T, self.acc_G, self.accl_G, self.tmp_G, self.tmpl_G,
+                     self.glob_out, self.lse_G),
+                    (0, HL, self.cu_P, self.prot, P, self.acc_L, self.accl_L, self.tmp_L, self.tmpl_L,
+                     self.rec_out, self.lse_L)):
+                if h1 <= h0 or nr == 0:
+                    continue
+                rows = nr * (h1 - h0)
+                if ci == 0 and last == 0:
+                    self._attn(h0, h1, cu_q, rid, nr, ch["cu"], fin, L.DTYPE_BF16, finl, stream)
+                elif ci == 0:
+                    self._attn(h0, h1, cu_q, rid, nr, ch["cu"], acc, L.DTYPE_FP32, accl, stream)
+                else:
+                    self._attn(h0, h1, cu_q, rid, nr, ch["cu"], tmp, L.DTYPE_BF16, tmpl, stream)
+                    if ci < last:
+                        L.mla_merge_states(acc, L.DTYPE_FP32, accl, tmp, L.DTYPE_BF16, tmpl, rows,
+                                           acc, L.DTYPE_FP32, accl, stream)
+                    else:
+                        L.mla_merge_states(acc, L.DTYPE_FP32, accl, tmp, L.DTYPE_BF16, tmpl, rows,
+                                           fin, L.DTYPE_BF16, finl, stream)
+        L.mla_head_partition_merge(self.art, self.rec_out, self.prot, P, self.glob_out, self.wa_t,
+                                   self.wb_t, T, HL, HG, self.d_mid, self.d_model, self.z, self.y,
+                                   stream)
+        return self.y
+
+    def work(self) -> dict:
+        H, HL, HG, T, P, Ld = self.H, self.HL, self.HG, self.T, self.P, self.Ldoc
+        return dict(
+            dec_flops=2 * 512 * 256 * H * Ld,
+            attn_flops=640 * Ld * (T * HG + P * HL),
+            proj_flops=2 * T * ((HL + HG) * 128 * self.d_mid + self.d_mid * self.d_model),
+            gather_tokens=Ld, gather_bytes=Ld * 2304, new_tokens=T, ctx_tokens=Ld,
+        )

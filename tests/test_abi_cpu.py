@@ -1,0 +1,108 @@
+"""The C-ABI library loads without a GPU, exports every entry point the header
+declares, and rejects bad arguments on the host before anything is enqueued
+(these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_long_context_amd as mla
+from mla_long_context_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "mla.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmla.so is not built (python -m mla_long_context_amd.build)")
+    return mla.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert len(declared) >= 9
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+    assert lib.mla_abi_version() == 1
+
+
+def _err(fn, *args):
+    with pytest.raises(mla.MlaError) as ei:
+        fn(*args, stream=0)
+    return ei.value.code, str(ei.value)
+
+
+FAKE = 1 << 20      # a 16-byte aligned non-null "device pointer" never dereferenced
+
+
+def test_gather_validation(lib):
+    code, msg = _err(mla.mla_gather_context, None, 0, 4, FAKE, 4, FAKE, FAKE, FAKE, 1, 64, FAKE, None)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "null" in msg
+    code, _ = _err(mla.mla_gather_context, FAKE, 7, 4, FAKE, 4, FAKE, FAKE, FAKE, 1, 64, FAKE, None)
+    assert code == _lib.MLA_ERR_UNSUPPORTED
+    code, _ = _err(mla.mla_gather_context, FAKE + 2, 0, 4, FAKE, 4, FAKE, FAKE, FAKE, 1, 64, FAKE, None)
+    assert code == _lib.MLA_ERR_INVALID_ARG
+    code, _ = _err(mla.mla_gather_context, FAKE, 0, 0, FAKE, 4, FAKE, FAKE, FAKE, 1, 64, FAKE, None)
+    assert code == _lib.MLA_ERR_INVALID_ARG
+    # empty work is a no-op, even with null pointers
+    assert mla.mla_gather_context(None, 0, 0, None, 0, None, None, None, 0, 0, None, None, stream=0) == 0
+
+
+def test_decompress_validation(lib):
+    code, _ = _err(mla.mla_decompress, FAKE, 576, 10, FAKE, 8, 3, 3, FAKE, 1280, FAKE, 1280)
+    assert code == _lib.MLA_ERR_INVALID_ARG                      # empty head range
+    code, _ = _err(mla.mla_decompress, FAKE, 576, 10, FAKE, 8, 0, 9, FAKE, 1280, FAKE, 1280)
+    assert code == _lib.MLA_ERR_INVALID_ARG                      # h_end > H
+    code, _ = _err(mla.mla_decompress, FAKE, 500, 10, FAKE, 8, 0, 8, FAKE, 1280, FAKE, 1280)
+    assert code == _lib.MLA_ERR_INVALID_ARG                      # ld < 512
+    code, _ = _err(mla.mla_decompress, FAKE, 576, 10, FAKE, 8, 0, 8, FAKE, 1000, FAKE, 1280)
+    assert code == _lib.MLA_ERR_INVALID_ARG                      # head stride too small
+    assert mla.mla_decompress(None, 576, 0, None, 8, 0, 8, None, 0, None, 0, stream=0) == 0
+
+
+def test_attn_validation(lib):
+    base = [FAKE, 8 * 192, 8, 0, 8, FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE, FAKE, None, 1, 10,
+            0.07, 0, FAKE, 0, 8 * 128, FAKE, 8]
+    args = list(base); args[19] = 5
+    assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_UNSUPPORTED
+    args = list(base); args[1] = 8 * 192 - 8
+    assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[16] = -1.0
+    assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[0] = None
+    assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[10] = 512
+    assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[20] = 100
+    assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_merge_rope_partition_pack_validation(lib):
+    assert _err(mla.mla_merge_states, FAKE, 9, FAKE, FAKE, 0, FAKE, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_merge_states, FAKE, 0, FAKE, FAKE + 4, 0, FAKE, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert mla.mla_merge_states(None, 0, None, None, 0, None, 0, None, 0, None, stream=0) == 0
+    assert _err(mla.mla_rope_relocate_q, FAKE, FAKE, 8 * 192, 4, 8, 4096, 10000.0, 3)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_rope_relocate_q, FAKE, FAKE, 100, 4, 8, 4096, 10000.0, 0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_rope_relocate_q, FAKE, FAKE, 8 * 192, 4, 8, 4096, 0.5, 0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_head_partition_merge, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 16, 7, 1, 2000,
+                4096, FAKE, FAKE)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_head_partition_merge, FAKE, FAKE, FAKE, 20, FAKE, FAKE, FAKE, 16, 7, 1, 2048,
+                4096, FAKE, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG          # P > T
+    assert _err(mla.mla_pack_weight_t, FAKE, 10, 16, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_pack_weight_t, FAKE, 16, 16, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG   # in place
+
+
+def test_last_error_is_thread_local_and_cleared(lib):
+    _err(mla.mla_pack_weight_t, FAKE, 10, 16, FAKE)
+    assert b"multiples of 8" in lib.mla_last_error()
+    assert mla.mla_merge_states(None, 0, None, None, 0, None, 0, None, 0, None, stream=0) == 0
+    assert lib.mla_last_error() == b""

@@ -1,0 +1,254 @@
+"""Per-kernel parity on the GPU through the C ABI against the fp64 oracle:
+gather (bit-exact), merge, RoPE relocation, decompression, attention and the
+head-partition projection, on seeded inputs spanning several tiles plus
+ragged tails and the degenerate cases (empty key sets, empty requests)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import mla_long_context_amd as mla
+from mla_long_context_amd import prefill as pf
+from oracle import mla_oracle as orc
+
+from gpu_util import (bf16_dev, bits, check_lse, check_out, f64, rel_l2, require_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _i32(a):
+    return torch.tensor(np.asarray(a, dtype=np.int32), device="cuda")
+
+
+# ---------------------------------------------------------------- gather
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_gather_bit_exact(dtype):
+    require_gpu()
+    say(f"gather {dtype}")
+    prob = mi.make_problem(4, [256, 64 * 7, 0, 128], [1, 1, 1, 1], 128, dtype, seed=41,
+                           extra_blocks=5, poison=True)
+    pool = pf.upload_pool(prob, "cuda")
+    bt = _i32(prob.block_table)
+    # ragged windows: unaligned starts, a zero-length request, block-crossing ranges
+    starts = np.array([3, 70, 0, 64]); lens = np.array([250, 301, 0, 64])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    out = torch.full((int(cu[-1]) + 1, 576), -7.0, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_gather_context(pool, mla.DTYPE_BF16 if dtype == "bf16" else mla.DTYPE_FP8_E4M3,
+                           prob.num_blocks, bt, bt.shape[1], _i32(starts), _i32(lens), _i32(cu), 4,
+                           int(lens.max()), out, status)
+    torch.cuda.synchronize()
+    got = bits(out)
+    for r in range(4):
+        if dtype == "bf16":
+            ref = orc.gather_bf16_bits(prob.pool, prob.block_table, r, int(starts[r]), int(lens[r]))
+        else:
+            ref = orc.gather_fp8_expected_bits(prob.pool, prob.block_table, r, int(starts[r]), int(lens[r]))
+        assert np.array_equal(got[cu[r]:cu[r + 1]], ref), f"request {r}"
+    # the row after the last request is untouched
+    assert np.all(f64(out[-1]) == -7.0)
+    assert int(status.item()) == 0
+    # no NaN from the poisoned unused blocks leaked
+    assert not np.any(np.isnan(f64(out[:-1])))
+
+
+def test_gather_out_of_range_block_sets_status_and_writes_zeros():
+    require_gpu()
+    prob = mi.make_problem(1, [128], [1], 64, "bf16", seed=42)
+    pool = pf.upload_pool(prob, "cuda")
+    bt = prob.block_table.copy()
+    bt[0, 1] = prob.num_blocks + 3          # second block points outside the pool
+    out = torch.full((128, 576), 5.0, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_gather_context(pool, mla.DTYPE_BF16, prob.num_blocks, _i32(bt), bt.shape[1], _i32([0]),
+                           _i32([128]), _i32([0, 128]), 1, 128, out, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == mla._lib.MLA_ERR_OUT_OF_RANGE
+    got = bits(out)
+    assert np.array_equal(got[:64], orc.gather_bf16_bits(prob.pool, prob.block_table, 0, 0, 64))
+    assert np.all(got[64:] == 0)
+
+
+# ---------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("da,db,do", [(2, 0, 2), (2, 0, 0), (0, 0, 0), (2, 2, 2)])
+def test_merge_states(da, db, do):
+    require_gpu()
+    rng = np.random.default_rng(43)
+    rows = 4099
+    oa = rng.standard_normal((rows, 128)).astype(np.float32)
+    ob = rng.standard_normal((rows, 128)).astype(np.float32)
+    la = (rng.standard_normal(rows) * 3 + 8).astype(np.float32)
+    lb = (rng.standard_normal(rows) * 3 + 8).astype(np.float32)
+    la[:7] = -np.inf; lb[3:11] = -np.inf            # one side empty, and both empty (rows 3..6)
+    la[20] = 80.0; lb[20] = -80.0                   # extreme weights
+    tdt = {0: torch.bfloat16, 2: torch.float32}
+    ta = torch.tensor(oa).to(tdt[da]).cuda(); tb = torch.tensor(ob).to(tdt[db]).cuda()
+    tla = torch.tensor(la).cuda(); tlb = torch.tensor(lb).cuda()
+    out = torch.empty((rows, 128), dtype=tdt[do], device="cuda")
+    lout = torch.empty(rows, dtype=torch.float32, device="cuda")
+    mla.mla_merge_states(ta, da, tla, tb, db, tlb, rows, out, do, lout)
+    # in place into a, as the chunk loop does
+    ta2 = ta.clone(); tla2 = tla.clone()
+    mla.mla_merge_states(ta2, da, tla2, tb, db, tlb, rows, ta2, da, tla2)
+    torch.cuda.synchronize()
+    ref_o, ref_l = orc.merge_states(f64(ta), la.astype(np.float64), f64(tb), lb.astype(np.float64))
+    tol = 1e-6 if do == 2 else 2 ** -8
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - ref_o) / np.maximum(np.abs(ref_o), 1.0)) <= tol
+    check_lse(f64(lout), ref_l, tol=1e-5)
+    if da == do:
+        assert torch.equal(ta2, out) and torch.equal(tla2, lout)
+
+
+# ---------------------------------------------------------------- rope relocation
+
+@pytest.mark.parametrize("delta", [0, 1, 4096, 2 ** 18])
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_rope_relocate(delta, pairing):
+    require_gpu()
+    rng = np.random.default_rng(44)
+    T, H = 37, 5
+    q = mi.f32_to_bf16_bits(rng.standard_normal((T, H, 192)).astype(np.float32))
+    tq = bf16_dev(q)
+    tout = torch.empty_like(tq)
+    mla.mla_rope_relocate_q(tq, tout, H * 192, T, H, delta, 10000.0, pairing)
+    tin = tq.clone()
+    mla.mla_rope_relocate_q(tin, tin, H * 192, T, H, delta, 10000.0, pairing)
+    torch.cuda.synchronize()
+    ref = orc.relocate_q(orc.bf16_to_f64(q[..., 128:]), delta, pairing="interleaved" if pairing == 0 else "half")
+    got = f64(tout)
+    assert np.array_equal(bits(tout)[..., :128], q[..., :128])       # nope part copied
+    err = np.abs(got[..., 128:] - ref)
+    assert np.all(err <= 2 ** -8 * np.maximum(np.abs(ref), 2 ** -6) + 1e-6)
+    assert torch.equal(tin, tout)                                     # in place == out of place
+    assert np.array_equal(bits(tq), q)                                # input untouched
+
+
+# ---------------------------------------------------------------- decompression
+
+@pytest.mark.parametrize("H,h0,h1,n", [(8, 0, 8, 300), (4, 1, 3, 129), (2, 0, 2, 1)])
+def test_decompress(H, h0, h1, n):
+    require_gpu()
+    say(f"decompress H={H} heads [{h0},{h1}) n={n}")
+    rng = np.random.default_rng(45)
+    lat = mi.f32_to_bf16_bits(rng.standard_normal((n, 576)).astype(np.float32))
+    W = mi.f32_to_bf16_bits((rng.standard_normal((512, H * 256)) / math.sqrt(512)).astype(np.float32))
+    w_t = pf.pack_weight(W, "cuda")
+    Hs = h1 - h0
+    hst = (n + 3) * 128
+    k = torch.zeros((Hs, n + 3, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((Hs, n + 3, 128), dtype=torch.bfloat16, device="cuda")
+    mla.mla_decompress(bf16_dev(lat), 576, n, w_t, H, h0, h1, k, hst, v, hst)
+    torch.cuda.synchronize()
+    # packing itself is exact
+    assert np.array_equal(bits(w_t), W.T)
+    Wf = orc.bf16_to_f64(W)
+    for hs, h in enumerate(range(h0, h1)):
+        kr, vr = orc.decompress_head(orc.bf16_to_f64(lat[:, :512]), Wf, H, h)
+        check_out(f64(k[hs, :n]), kr, max_abs=0.05, rl2=4e-3, what=f"k head {h}")
+        check_out(f64(v[hs, :n]), vr, max_abs=0.05, rl2=4e-3, what=f"v head {h}")
+        assert np.all(f64(k[hs, n:]) == 0) and np.all(f64(v[hs, n:]) == 0)   # no write past n
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(seed, H, h0, h1, nq, nk, causal, out_dtype, row_ids=False):
+    rng = np.random.default_rng(seed)
+    B = len(nq)
+    Hs = h1 - h0
+    cu_q = np.concatenate([[0], np.cumsum(nq)]); cu_k = np.concatenate([[0], np.cumsum(nk)])
+    NK = int(cu_k[-1])
+    Tphys = int(cu_q[-1]) + 9
+    q = mi.f32_to_bf16_bits(rng.standard_normal((Tphys, H, 192)).astype(np.float32))
+    kn = mi.f32_to_bf16_bits(rng.standard_normal((Hs, max(NK, 1), 128)).astype(np.float32))
+    v = mi.f32_to_bf16_bits(rng.standard_normal((Hs, max(NK, 1), 128)).astype(np.float32))
+    lat = mi.f32_to_bf16_bits(rng.standard_normal((max(NK, 1), 576)).astype(np.float32))
+    rid = rng.permutation(Tphys)[:int(cu_q[-1])].astype(np.int32) if row_ids else None
+    T = int(cu_q[-1])
+    scale = 1 / math.sqrt(192)
+    odt = torch.float32 if out_dtype == mla.DTYPE_FP32 else torch.bfloat16
+    out = torch.full((T, Hs, 128), 9.0, dtype=odt, device="cuda")
+    lse = torch.full((T, Hs), 9.0, dtype=torch.float32, device="cuda")
+    hst = max(NK, 1) * 128
+    mla.mla_prefill_attn(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(kn), hst, bf16_dev(v), hst,
+                         bf16_dev(lat), 576, _i32(cu_q), _i32(cu_k),
+                         None if rid is None else _i32(rid), B, int(max(nq)), scale, int(causal),
+                         out, out_dtype, Hs * 128, lse, Hs)
+    torch.cuda.synchronize()
+    go, gl = f64(out), f64(lse)
+    worst = (0.0, 0.0, 0.0)
+    for b in range(B):
+        rows = np.arange(cu_q[b], cu_q[b + 1])
+        prow = rid[rows] if rid is not None else rows
+        keys = np.arange(cu_k[b], cu_k[b + 1])
+        vis = orc.causal_visible(nq[b], nk[b] - nq[b]) if causal else None
+        for hs, h in enumerate(range(h0, h1)):
+            ro, rl = orc.attend(orc.bf16_to_f64(q[prow, h]), orc.bf16_to_f64(kn[hs, keys]),
+                                orc.bf16_to_f64(lat[keys, 512:]), orc.bf16_to_f64(v[hs, keys]), scale, vis)
+            ma, r = check_out(go[rows, hs], ro, what=f"b{b} h{h} out")
+            le = check_lse(gl[rows, hs], rl, what=f"b{b} h{h} lse")
+            worst = tuple(max(x, y) for x, y in zip(worst, (ma, r, le)))
+    say(f"  attn worst max-abs {worst[0]:.2e} rel-L2 {worst[1]:.2e} lse {worst[2]:.2e}")
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("out_dtype", [mla.DTYPE_BF16, mla.DTYPE_FP32])
+def test_attention_varlen(causal, out_dtype):
+    require_gpu()
+    say(f"attn varlen causal={causal} out={out_dtype}")
+    # several query tiles (NW=8 -> 256 rows), ragged tails, an empty request
+    nq = [300, 1, 0, 77]
+    nk = [300 + 130, 1, 5, 77] if causal else [700, 64, 5, 0]
+    _attn_case(50 + causal, 3, 0, 3, nq, nk, causal, out_dtype)
+
+
+@pytest.mark.parametrize("nq", [[64], [100], [40, 64]])
+def test_attention_row_ids_and_head_range(nq):
+    require_gpu()
+    say(f"attn row ids nq={nq}")
+    _attn_case(60, 6, 2, 5, nq, [513] * len(nq), 0, mla.DTYPE_FP32, row_ids=True)
+
+
+def test_attention_empty_keys_give_zero_and_neg_inf():
+    require_gpu()
+    _attn_case(61, 2, 0, 2, [33, 5], [0, 0], 0, mla.DTYPE_BF16)
+
+
+# ---------------------------------------------------------------- head partition merge
+
+def test_head_partition_merge():
+    require_gpu()
+    say("head partition merge")
+    rng = np.random.default_rng(62)
+    T, HL, HG, P, d_mid, d_model = 300, 7, 1, 13, 256, 384
+    art = mi.f32_to_bf16_bits(rng.standard_normal((T, HL, 128)).astype(np.float32) * 0.05)
+    rec = mi.f32_to_bf16_bits(rng.standard_normal((P, HL, 128)).astype(np.float32) * 0.05)
+    glob = mi.f32_to_bf16_bits(rng.standard_normal((T, HG, 128)).astype(np.float32) * 0.05)
+    prot = np.sort(rng.choice(T, P, replace=False)).astype(np.int32)
+    prot[0] = 0; prot[-1] = T - 1
+    prot = np.unique(prot)
+    P = len(prot); rec = rec[:P]
+    WaL = mi.f32_to_bf16_bits((rng.standard_normal((HL * 128, d_mid)) / math.sqrt(HL * 128)).astype(np.float32))
+    WaG = mi.f32_to_bf16_bits((rng.standard_normal((HG * 128, d_mid)) / math.sqrt(HG * 128)).astype(np.float32))
+    Wb = mi.f32_to_bf16_bits((rng.standard_normal((d_mid, d_model)) / math.sqrt(d_mid)).astype(np.float32))
+    wa_t = pf.pack_weight(np.concatenate([WaL, WaG], 0), "cuda")
+    wb_t = pf.pack_weight(Wb, "cuda")
+    z = torch.empty((T, d_mid), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, d_model), dtype=torch.bfloat16, device="cuda")
+    mla.mla_head_partition_merge(bf16_dev(art), bf16_dev(rec), _i32(prot), P, bf16_dev(glob), wa_t, wb_t,
+                                 T, HL, HG, d_mid, d_model, z, y)
+    torch.cuda.synchronize()
+    O_L = orc.replace_protected(orc.bf16_to_f64(art), orc.bf16_to_f64(rec), prot)
+    ref = orc.head_partition_merge(O_L, orc.bf16_to_f64(glob), orc.bf16_to_f64(WaL),
+                                   orc.bf16_to_f64(WaG), orc.bf16_to_f64(Wb))
+    ma, r = check_out(f64(y), ref, what="y")
+    say(f"  y max-abs {ma:.2e} rel-L2 {r:.2e}")
+    # a missed replacement would show: rows use rec, not art
+    wrong = orc.head_partition_merge(orc.bf16_to_f64(art), orc.bf16_to_f64(glob), orc.bf16_to_f64(WaL),
+                                     orc.bf16_to_f64(WaG), orc.bf16_to_f64(Wb))
+    assert rel_l2(f64(y)[prot], wrong[prot]) > 0.1
