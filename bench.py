@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA chunked prefill on one MI355X.
+
+Workload (default): DeepSeek-V3 geometry, one layer, 128 heads, 4 requests x
+(8192 cached context tokens + 1024 new tokens), 64-token blocks in a shuffled
+pool, context chunk 4096, bf16 cache. A step is one pass of the whole path:
+per context chunk gather -> kv_b_proj decompression -> attention -> LSE merge,
+then decompression of the new tokens -> causal attention -> final merge.
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+
+Prints one JSON line: TFLOP/s of algorithmic work (2*512*256 flop per
+decompressed (token, head), 640 flop per visible (row, key, head)), prefill
+tokens/s, the roofline of the dominant kernel (context attention, per-launch
+duration from HIP events on the launch stream during the timed steps) and the
+fp64 CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import contextlib
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MLA chunked-prefill TFLOP/s + prefill tokens/s; % of MFMA/HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_ctx_dsv3_hbm_traffic.json")
+
+
+class KernelTimer:
+    """HIP events around each launch, on the stream the kernels run on."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.spans = []
+
+    @contextlib.contextmanager
+    def span(self, name):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        yield
+        e1.record()
+        self.spans.append((name, e0, e1))
+
+    def summary(self):
+        self.torch.cuda.synchronize()
+        out = {}
+        for name, e0, e1 in self.spans:
+            c, t = out.get(name, (0, 0.0))
+            out[name] = (c + 1, t + e0.elapsed_time(e1))
+        return out
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_src):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, scaled by a plain copy's counter reading; None when absent or
+    when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        d = json.load(f)
+    if d.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(prob, budget_s=15.0):
+    """The fp64 oracle as it stands, on request 0 of the same workload, one
+    head at a time, until about budget_s seconds of host work are spent."""
+    import numpy as np
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    C, E = int(prob.ctx_len[0]), int(prob.ext_len[0])
+    per_head = 2 * 512 * 256 * (C + E) + 640 * (C * E + E * (E + 1) // 2)
+    heads = 0
+    t0 = time.time()
+    while heads < prob.H and time.time() - t0 < budget_s:
+        orc.prefill_reference(prob, heads=[heads], rows={0: np.arange(E)})
+        heads += 1
+    dt = time.time() - t0
+    flops = per_head * heads
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"request 0 (C={C}, E={E}), heads 0..{heads - 1} of {prob.H}, all {E} new rows: "
+                      f"{flops / 1e9:.1f} GFLOP fp64 in {dt:.1f} s; NumPy/OpenBLAS with "
+                      f"{blas_threads} BLAS threads (exp single-threaded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="standard workload number (1-4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only; the prefill path has no multi-GPU mode. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.calibrate_copy:
+        n = 1 << 29   # 512 Mi bf16 elements = 1 GiB
+        a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 2 * n, "bytes_written": 2 * n, "launches": 3}))
+        return
+
+    import mla_inputs
+    import mla_long_context_amd as mla
+    from mla_long_context_amd.prefill import ChunkedPrefill
+
+    mla.load()                       # fails loudly if libmla.so is missing
+    t_gen = time.time()
+    prob = mla_inputs.make_config(args.workload)
+    pre = ChunkedPrefill(prob)
+    work = pre.work()
+    print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.CONFIG_NAMES[args.workload]}",
+          file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        pre.run()
+    torch.cuda.synchronize()
+    assert int(pre.dev_status.item()) == 0, "gather reported an out-of-range block"
+
+    timer = KernelTimer()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        pre.run(timer=timer)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / max(args.steps, 1)
+    kern = timer.summary()
+
+    flops = work["dec_flops"] + work["attn_flops"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    per_step_launch = {k: c / args.steps for k, (c, _) in kern.items()}
+    kernels = {}
+    for name, (c, tot) in kern.items():
+        avg = tot / c
+        entry = {"launches_per_step": per_step_launch[name], "avg_ms": round(avg, 4),
+                 "ms_per_step": round(tot / args.steps, 4)}
+        if name == "attn_ctx":
+            unit = work["ctx_attn_flops"] / per_step_launch[name]
+            entry["tflops"] = round(unit / (avg * 1e-3) / 1e12, 2)
+        elif name == "attn_ext":
+            entry["tflops"] = round(work["ext_attn_flops"] / per_step_launch[name] / (avg * 1e-3) / 1e12, 2)
+        elif name == "decompress":
+            entry["tflops"] = round(work["dec_flops"] / per_step_launch[name] / (avg * 1e-3) / 1e12, 2)
+        elif name == "gather":
+            entry["gbs"] = round(work["gather_bytes"] / per_step_launch[name] / (avg * 1e-3) / 1e9, 1)
+        elif name == "merge":
+            entry["gbs"] = round(work["merge_bytes"] / per_step_launch[name] / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = entry
+
+    c_ms = kern["attn_ctx"][1] / kern["attn_ctx"][0]
+    c_unit = work["ctx_attn_flops"] / per_step_launch["attn_ctx"]
+    achieved = c_unit / (c_ms * 1e-3) / 1e12
+    traffic = traffic_for(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip"))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "mla_prefill_attn (context pass)",
+                "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)}
+
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": mla_inputs.CONFIG_NAMES[args.workload], "heads": prob.H,
+                   "requests": prob.B, "ctx_tokens_per_request": int(prob.ctx_len.max()),
+                   "new_tokens_total": work["new_tokens"], "chunk": prob.chunk,
+                   "cache": prob.cache_dtype},
+        "prefill_tokens_per_s": round(work["new_tokens"] / (ms * 1e-3), 1),
+        "context_tokens_per_s": round(work["ctx_tokens"] / (ms * 1e-3), 1),
+        "algorithmic_flop_per_step": flops,
+        "mfma_roofline_frac_whole_step": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(prob)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,8 @@ PyTorch provides device memory and the stream; nothing here computes.
 """
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 import torch
 
@@ -39,6 +41,14 @@ def _i32(a, device) -> torch.Tensor:
 
 def _cu(lens) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+
+
+_NULL = contextlib.nullcontext()
+
+
+def _span(timer, name):
+    """Timing span around one launch when a timer (bench.py) is given."""
+    return _NULL if timer is None else timer.span(name)
 
 
 def pack_weight(w_bits: np.ndarray, device, stream=None) -> torch.Tensor:
@@ -117,25 +127,34 @@ class ChunkedPrefill:
     def merge(self, a, da, la, b, db, lb, out, dout, lout, stream=None):
         L.mla_merge_states(a, da, la, b, db, lb, self.T * self.H, out, dout, lout, stream)
 
-    def run(self, stream=None):
+    def run(self, stream=None, timer=None):
         if self.T == 0:
             return self.out, self.lse
         for ci, ch in enumerate(self.chunks):
-            self.gather(ch, stream)
-            self.decompress(self.lat_ws, ch["n"], stream)
+            with _span(timer, "gather"):
+                self.gather(ch, stream)
+            with _span(timer, "decompress"):
+                self.decompress(self.lat_ws, ch["n"], stream)
             if ci == 0:
-                self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
+                with _span(timer, "attn_ctx"):
+                    self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
             else:
-                self.attend(self.lat_ws, ch["cu"], 0, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
-                self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16, self.tmp_l,
-                           self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
-        self.decompress(self.ext, self.T, stream)
+                with _span(timer, "attn_ctx"):
+                    self.attend(self.lat_ws, ch["cu"], 0, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
+                with _span(timer, "merge"):
+                    self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16,
+                               self.tmp_l, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
+        with _span(timer, "decompress"):
+            self.decompress(self.ext, self.T, stream)
         if not self.chunks:
-            self.attend(self.ext, self.cu_ext, 1, self.out, L.DTYPE_BF16, self.lse, stream)
+            with _span(timer, "attn_ext"):
+                self.attend(self.ext, self.cu_ext, 1, self.out, L.DTYPE_BF16, self.lse, stream)
         else:
-            self.attend(self.ext, self.cu_ext, 1, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
-            self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16, self.tmp_l,
-                       self.out, L.DTYPE_BF16, self.lse, stream)
+            with _span(timer, "attn_ext"):
+                self.attend(self.ext, self.cu_ext, 1, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
+            with _span(timer, "merge"):
+                self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16, self.tmp_l,
+                           self.out, L.DTYPE_BF16, self.lse, stream)
         return self.out, self.lse
 
     # ---------------------------------------------------------------- accounting
@@ -151,7 +170,12 @@ class ChunkedPrefill:
         ctx_pairs = int((C * E).sum())
         ext_pairs = int((E * (E + 1) // 2).sum())
         n_merge = max(len(self.chunks) - 1, 0) + (1 if self.chunks else 0)
+        # merge bytes per (row, head): fp32 acc read+write (2*516), bf16 chunk
+        # state read (260); the last merge writes bf16 (260) instead of fp32
+        merge_bytes = self.T * H * ((len(self.chunks) - 1) * (516 + 260 + 516) + (516 + 260 + 260)) \
+            if self.chunks else 0
         return dict(
+            merge_bytes=int(merge_bytes),
             dec_flops=2 * 512 * 256 * H * dec_tok,
             attn_flops=640 * H * (ctx_pairs + ext_pairs),
             ctx_attn_flops=640 * H * ctx_pairs,
