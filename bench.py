@@ -173,17 +173,14 @@ def main():
         avg = tot / c
         entry = {"launches_per_step": per_step_launch[name], "avg_ms": round(avg, 4),
                  "ms_per_step": round(tot / args.steps, 4)}
-        if name == "attn_ctx":
-            unit = work["ctx_attn_flops"] / per_step_launch[name]
-            entry["tflops"] = round(unit / (avg * 1e-3) / 1e12, 2)
-        elif name == "attn_ext":
-            entry["tflops"] = round(work["ext_attn_flops"] / per_step_launch[name] / (avg * 1e-3) / 1e12, 2)
-        elif name == "decompress":
-            entry["tflops"] = round(work["dec_flops"] / per_step_launch[name] / (avg * 1e-3) / 1e12, 2)
-        elif name == "gather":
-            entry["gbs"] = round(work["gather_bytes"] / per_step_launch[name] / (avg * 1e-3) / 1e9, 1)
-        elif name == "merge":
-            entry["gbs"] = round(work["merge_bytes"] / per_step_launch[name] / (avg * 1e-3) / 1e9, 1)
+        step_s = tot / args.steps * 1e-3           # this kernel's time per step
+        if name in ("attn_ctx", "attn_ext", "decompress"):
+            w = {"attn_ctx": work["ctx_attn_flops"], "attn_ext": work["ext_attn_flops"],
+                 "decompress": work["dec_flops"]}[name]
+            entry["tflops"] = round(w / step_s / 1e12, 2)
+        else:
+            w = {"gather": work["gather_bytes"], "merge": work["merge_bytes"]}[name]
+            entry["gbs"] = round(w / step_s / 1e9, 1)
         kernels[name] = entry
 
     c_ms = kern["attn_ctx"][1] / kern["attn_ctx"][0]
