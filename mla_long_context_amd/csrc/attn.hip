@@ -27,6 +27,7 @@ constexpr int kKsLd = kDqk + 8;   // 200 elements = 400 B per key row (conflict-
 constexpr int kVtLd = kTileK + 8; // 72 elements = 144 B per dv row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;      // log2 headroom of the lazy softmax reference
 
 struct AttnArgs {
   const uint16_t* q; int64_t q_rs; int h_begin; int Hsel;
@@ -104,27 +105,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   u32x4 pk[kKv], pr[kRv];
   u32x2 pv[kVb][4];
+  // Keys at or past n_k are clamped to the last key: their scores are masked
+  // to -inf and their values meet p = 0, so no load needs a predicate.
+  const int klast = n_k - 1;
   auto gload = [&](int kt0) {
 #pragma unroll
     for (int j = 0; j < kKv; ++j) {
-      const int idx = tid + NT * j, key = idx >> 4, vec = idx & 15;
-      pk[j] = (kt0 + key < n_k) ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)(kt0 + key) * kDnope + vec * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
+      const int idx = tid + NT * j, key = min(kt0 + (idx >> 4), klast), vec = idx & 15;
+      pk[j] = *reinterpret_cast<const u32x4*>(kbase + key * kDnope + vec * 8);
     }
 #pragma unroll
     for (int j = 0; j < kRv; ++j) {
-      const int idx = tid + NT * j, key = idx >> 3, vec = idx & 7;
-      pr[j] = (kt0 + key < n_k) ? *reinterpret_cast<const u32x4*>(rbase + (int64_t)(kt0 + key) * a.ld_lat + vec * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
+      const int idx = tid + NT * j, key = min(kt0 + (idx >> 3), klast), vec = idx & 7;
+      pr[j] = *reinterpret_cast<const u32x4*>(rbase + (int64_t)key * a.ld_lat + vec * 8);
     }
 #pragma unroll
     for (int j = 0; j < kVb; ++j) {
       const int idx = tid + NT * j, kq = idx >> 5, dq = idx & 31;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kt0 + kq * 4 + r;
-        pv[j][r] = (key < n_k) ? *reinterpret_cast<const u32x2*>(vbase + (int64_t)key * kDv + dq * 4)
-                               : u32x2{0u, 0u};
+        const int key = min(kt0 + kq * 4 + r, klast);
+        pv[j][r] = *reinterpret_cast<const u32x2*>(vbase + key * kDv + dq * 4);
       }
     }
   };
@@ -162,20 +163,25 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[d][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;     // reference max (scaled, log2 units), row sum
 
   // last key (exclusive) any row of this wavefront may see
   const int wave_kend = kCausal ? min(n_k, r0 + wave * 32 + 32 + shift) : n_k;
+  const int wave_first_lim = r0 + wave * 32 + shift;   // causal: smallest row limit in the wave
   const int row_lim = row + shift;           // causal: keys <= row_lim are visible
+  const float c = a.scale_log2;              // scale * log2(e); scores stay raw until exp2
 
   if (ntiles > 0) {
     gload(0);
     lstore();
   }
   __syncthreads();
+  const int last_kt0 = (ntiles - 1) * kTileK;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int kt0 = kt * kTileK;
-    if (kt + 1 < ntiles) gload(kt0 + kTileK);
+    // prefetch the next tile (the last iteration re-reads its own tile: the
+    // loop body stays branch-free so the loads overlap the MFMA work below)
+    gload(min(kt0 + kTileK, last_kt0));
     if (kt0 < wave_kend) {
       f32x16 S[2];
 #pragma unroll
@@ -190,47 +196,60 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
           S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
         }
       }
-      // scale, mask, tile max
-      float mt = -INFINITY;
+      // masking only on tiles that cross the key end or the causal diagonal
+      const bool edge = (kt0 + kTileK > n_k) || (kCausal && kt0 + kTileK - 1 > wave_first_lim);
+      if (edge) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          float x = S[kb][i] * a.scale_log2;
-          const bool vis = key < n_k && (!kCausal || key <= row_lim);
-          x = vis ? x : -INFINITY;
-          S[kb][i] = x;
-          mt = fmaxf(mt, x);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool vis = key < n_k && (!kCausal || key <= row_lim);
+            S[kb][i] = vis ? S[kb][i] : -INFINITY;
+          }
+      }
+      // row max of raw scores (scale > 0 keeps the order): own 32 keys, then lane ^ 32
+      float mt = S[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, S[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[1][i]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // Lazy reference max (log2 units): it only moves when the tile max
+      // exceeds it by more than kLazy, so p <= 2^kLazy and the rescale of O is
+      // skipped on almost every tile. The normalisation uses the same
+      // reference, so the result does not depend on when it moved.
+      const float mtc = mt * c;
+      const bool bump = mtc > m_ref + kLazy;     // false while mt = -inf
+      const float m_new = bump ? mtc : m_ref;
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;   // 0 from -inf
+      const float mc = (m_new == -INFINITY) ? 0.f : m_new;
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(S[kb][i] - m_use);
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -mc));
           S[kb][i] = p;
           ps += p;
         }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
+      l_run = fmaf(l_run, alpha, ps);
+      if (__any(bump)) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+        for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+          for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+      }
+      m_ref = m_new;
       // P^T operands: MFMA mm covers keys 16mm..16mm+15 of the tile
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         const int kb = mm >> 1, i0 = 8 * (mm & 1);
         u32x4 u;
-        u.x = pack_bf16x2(S[kb][i0 + 0], S[kb][i0 + 1]);
-        u.y = pack_bf16x2(S[kb][i0 + 2], S[kb][i0 + 3]);
-        u.z = pack_bf16x2(S[kb][i0 + 4], S[kb][i0 + 5]);
-        u.w = pack_bf16x2(S[kb][i0 + 6], S[kb][i0 + 7]);
+        u.x = cvt_pk_bf16(S[kb][i0 + 0], S[kb][i0 + 1]);
+        u.y = cvt_pk_bf16(S[kb][i0 + 2], S[kb][i0 + 3]);
+        u.z = cvt_pk_bf16(S[kb][i0 + 4], S[kb][i0 + 5]);
+        u.w = cvt_pk_bf16(S[kb][i0 + 6], S[kb][i0 + 7]);
         const bf16x8 pf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -240,10 +259,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    if (kt + 1 < ntiles) {
-      lstore();
-      __syncthreads();
-    }
+    lstore();
+    __syncthreads();
   }
 
   // ---- epilogue
@@ -264,11 +281,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4*>(op) = f32x4{o0, o1, o2, o3};
       } else {
         uint16_t* op = static_cast<uint16_t*>(a.out) + orow * a.out_rs + (int64_t)hs * kDv + dv;
-        *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+        *reinterpret_cast<u32x2*>(op) = u32x2{cvt_pk_bf16(o0, o1), cvt_pk_bf16(o2, o3)};
       }
     }
   if (g == 0)
-    a.lse[orow * a.lse_rs + hs] = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    a.lse[orow * a.lse_rs + hs] = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 template <int NW, bool kCausal, bool kRowIds>

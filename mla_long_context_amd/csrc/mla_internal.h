@@ -55,6 +55,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Hardware round-to-nearest-even fp32 -> bf16 of two values (v_cvt_pk_bf16_f32);
+// used where no NaN can occur and bit patterns of NaN do not matter.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // OCP E4M3FN code -> fp32, exact: bias 7, exponent 0 subnormal (m * 2^-9),
 // S.1111.111 NaN, no infinities.
 __device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {

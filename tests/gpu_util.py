@@ -72,7 +72,7 @@ def check_lse(got, ref, tol=LSE_ABS, what="lse"):
     fin = ~ninf_r
     if fin.any():
         tol = np.broadcast_to(np.asarray(tol, np.float64), ref.shape)
-        d = np.abs(got - ref)
+        d = np.where(fin, np.abs(np.where(fin, got, 0.0) - np.where(fin, ref, 0.0)), 0.0)
         bad = fin & ~(d <= tol)
         err = float(np.max(d[fin]))
         assert not bad.any(), f"{what}: max-abs {err:.3e} exceeds its tolerance at {np.argwhere(bad)[:4].tolist()}"
