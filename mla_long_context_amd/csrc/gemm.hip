@@ -1,14 +1,15 @@
-// bf16 MFMA GEMM core for gfx950, D[t][n] = sum_k A[t][k] * Bt[n][k], with
-// both operands K-contiguous (weights are packed once by mla_pack_weight_t).
-// Used for:
+// bf16 MFMA GEMMs for gfx950, D[t][n] = sum_k A[t][k] * Bt[n][k], with both
+// operands K-contiguous (weights are packed once by mla_pack_weight_t):
 //   * kv_b_proj decompression (DeepSeek MLA -- Prefix Cache and Chunked
 //     Prefill, section 4.4 step 2): A = c_kv rows of the gathered latent,
 //     Bt = packed [W_UK | W_UV], output split per head into k_nope and v.
+//     Its own kernel (decompress_kernel) keeps a head's weight slice in LDS.
 //   * the sliced first output projection and the shared second projection of
 //     the Local/Global head partition (RedKnot-MLA, sections 1-3, Equation 4),
-//     with protected-row replacement fused into the A-operand load.
+//     with protected-row replacement fused into the A-operand load
+//     (gemm_nt_kernel).
 //
-// Tiling: 256 threads (4 wavefronts of 64), a 128 x 128 output tile per
+// gemm_nt_kernel tiling: 256 threads (4 wavefronts of 64), a 128 x 128 output tile per
 // workgroup, K in steps of 64 through double-buffered LDS; each wavefront
 // owns a 64 x 64 sub-tile as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks. The MFMA
 // is issued as D^T = Bt_frag x A_frag so that each lane ends up holding four
@@ -25,29 +26,6 @@ constexpr int kLdsC = BN + 8;            // padded epilogue row
 constexpr int kTileElems = BM * kLdsK;   // one operand tile
 
 // ---------------------------------------------------------------- problem policies
-
-struct DecompressP {
-  const uint16_t* lat; int64_t ld; int M;
-  const uint16_t* wt; int H_total, h_begin, Hsel;
-  uint16_t* k; int64_t khs; uint16_t* v; int64_t vhs;
-
-  __device__ int rows() const { return M; }
-  __device__ int K() const { return kDc; }
-  __device__ void a_rows(int t, const uint16_t*& pl, const uint16_t*& pg, int& ksplit) const {
-    pl = t < M ? lat + (int64_t)t * ld : nullptr;
-    pg = nullptr;
-    ksplit = kDc;
-  }
-  __device__ const uint16_t* b_row(int nt, int r) const {
-    const int h = h_begin + (nt < Hsel ? nt : nt - Hsel);
-    const int64_t row = (nt < Hsel ? 0 : (int64_t)H_total * kDnope) + (int64_t)h * kDnope + r;
-    return wt + row * kDc;
-  }
-  __device__ void store(int t, int nt, int vec, u32x4 val) const {
-    uint16_t* dst = nt < Hsel ? k + (int64_t)nt * khs : v + (int64_t)(nt - Hsel) * vhs;
-    *reinterpret_cast<u32x4*>(dst + (int64_t)t * kDnope + vec * 8) = val;
-  }
-};
 
 // A = [O_L | O_G] with O_L rows from the artifact or, for protected rows, from
 // the recomputation; Bt = packed [W_aL ; W_aG]; D = z.
@@ -214,6 +192,156 @@ int launch_gemm(const P& p, int M, int N, hipStream_t s, const char* what) {
   return mla_check_launch(what);
 }
 
+// ---------------------------------------------------------------- decompression kernel
+//
+// 256 x 256 output tile (tokens x columns) per workgroup of 8 wavefronts (two
+// per SIMD: LDS latency is only covered with a second wavefront), each
+// wavefront a 64 x 128 sub-tile held as 2 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 accumulators. Per 16-wide k step a wavefront reads
+// 6 fragments from LDS for 8 MFMAs. Both operands are staged through
+// double-buffered LDS (rows padded to 144 B: conflict-free 16-byte reads) by
+// coalesced 16-byte global loads, prefetched into registers one 64-wide k step
+// ahead. The MFMA is issued as D^T so a lane owns four consecutive output
+// columns; the epilogue goes through LDS so global stores are whole 256-byte
+// rows of one head's k_nope or v. A wavefront's 128 columns are always one
+// head's W_UK or W_UV, also when a tile straddles the W_UK / W_UV boundary.
+constexpr int kDT = 256;                       // tile edge (tokens and columns)
+constexpr int kDBK = 64;                       // k step
+constexpr int kDLd = kDBK + 8;                 // padded LDS row, elements
+constexpr int kDStage = 2 * kDT * kDLd;        // A and B rows of one stage, elements
+constexpr int kDThreads = 512;
+
+struct DecArgs {
+  const uint16_t* lat; int64_t ld; int M;
+  const uint16_t* wt; int H_total, h_begin, Hsel;
+  uint16_t* k; int64_t khs; uint16_t* v; int64_t vhs;
+  int n_mt, n_nt;
+};
+
+__global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];   // [2 stages][A 256 | B 256][kDLd]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;      // 4 x 2 wavefronts: 64 tokens x 128 columns each
+  const int l32 = lane & 31, g = lane >> 5;
+  // Grouped order: within an XCD's contiguous range of tiles, consecutive
+  // tiles walk kGroupM token tiles x all column tiles, so the 32 tiles in
+  // flight on an XCD share 4 latent tiles and 8 weight tiles (3 MB, resident
+  // in its 4 MB L2) instead of streaming 32 latent tiles.
+  constexpr int kGroupM = 4;
+  const int work = (int)xcd_remap(blockIdx.x, (uint32_t)(a.n_mt * a.n_nt));
+  const int per_group = kGroupM * a.n_nt;
+  const int first_mt = (work / per_group) * kGroupM;
+  const int gm = min(a.n_mt - first_mt, kGroupM);
+  const int in_group = work % per_group;
+  const int mt = first_mt + in_group % gm;
+  const int nt = in_group / gm;
+  const int t0 = mt * kDT;
+  const int HK = a.Hsel * kDnope;               // columns of the K part
+
+  // global -> LDS staging: thread loads rows lrow + 64 i (i < 4), vector lvec
+  const int lrow = tid >> 3, lvec = tid & 7;
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 64 * i;
+    ap[i] = a.lat + (int64_t)min(t0 + r, a.M - 1) * a.ld + lvec * 8;
+    const int n = nt * kDT + r;                 // output column -> packed weight row
+    const int64_t wrow = n < HK ? (int64_t)a.h_begin * kDnope + n
+                                : (int64_t)a.H_total * kDnope + (int64_t)a.h_begin * kDnope + (n - HK);
+    bp[i] = a.wt + wrow * kDc + lvec * 8;
+  }
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + kt * kDBK);
+      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + kt * kDBK);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* As = lds + buf * kDStage;
+    uint16_t* Bs = As + kDT * kDLd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(As + (lrow + 64 * i) * kDLd + lvec * 8) = ra[i];
+      *reinterpret_cast<u32x4*>(Bs + (lrow + 64 * i) * kDLd + lvec * 8) = rb[i];
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
+
+  constexpr int nk = kDc / kDBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    gload(min(kt + 1, nk - 1));                 // the last prefetch re-reads step nk-1
+    // keep the prefetch ahead of the MFMA work: without this fence the
+    // scheduler sinks the loads to the LDS store and exposes their latency
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* As = lds + cur * kDStage + (wm * 64) * kDLd;
+    const uint16_t* Bs = lds + cur * kDStage + (kDT + wn * 128) * kDLd;
+#pragma unroll
+    for (int s = 0; s < kDBK / 16; ++s) {
+      bf16x8 af[2], bf[4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        af[tb] = *reinterpret_cast<const bf16x8*>(As + (tb * 32 + l32) * kDLd + s * 16 + g * 8);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        bf[nb] = *reinterpret_cast<const bf16x8*>(Bs + (nb * 32 + l32) * kDLd + s * 16 + g * 8);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[nb], af[tb], acc[nb][tb], 0, 0, 0);
+    }
+    lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue through LDS: lane owns columns n = nb*32 + 8q + 4g + (0..3) of the
+  // wavefront's 128, for token wm*64 + tb*32 + l32; the wavefront writes its
+  // 64 x 128 bf16 block into its own LDS region, then streams it out 16 lanes
+  // per 256-byte token row.
+  const int n0 = nt * kDT + wn * 128;           // first column of this wavefront
+  const bool is_v = n0 >= HK;
+  const int hs = (is_v ? n0 - HK : n0) / kDnope;
+  uint16_t* dst = is_v ? a.v + (int64_t)hs * a.vhs : a.k + (int64_t)hs * a.khs;
+  constexpr int kCLd = 128 + 8;                 // 272-byte rows
+  uint16_t* Cs = lds + wave * (64 * kCLd);      // 8 x 17408 B fits the 147456 B stage area
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 w = {cvt_pk_bf16(acc[nb][tb][4 * q + 0], acc[nb][tb][4 * q + 1]),
+                         cvt_pk_bf16(acc[nb][tb][4 * q + 2], acc[nb][tb][4 * q + 3])};
+        *reinterpret_cast<u32x2*>(Cs + (tb * 32 + l32) * kCLd + nb * 32 + 8 * q + 4 * g) = w;
+      }
+  // a wavefront's LDS instructions complete in order, so its own reads below
+  // see these writes; other wavefronts never touch this region
+  __builtin_amdgcn_wave_barrier();
+  const int rsub = lane >> 4, vec = lane & 15;  // 4 rows per instruction, 16 lanes per row
+#pragma unroll 4
+  for (int r = 0; r < 64; r += 4) {
+    const int t = t0 + wm * 64 + r + rsub;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(Cs + (r + rsub) * kCLd + vec * 8);
+    if (t < a.M) *reinterpret_cast<u32x4*>(dst + (int64_t)t * kDnope + vec * 8) = val;
+  }
+}
+
 // ---------------------------------------------------------------- weight pack (transpose)
 
 constexpr int kTr = 64;
@@ -265,10 +393,21 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
   MLA_REQUIRE(k_head_stride >= (int64_t)n_tokens * kDnope && v_head_stride >= (int64_t)n_tokens * kDv &&
                   k_head_stride % 8 == 0 && v_head_stride % 8 == 0,
               MLA_ERR_INVALID_ARG, "mla_decompress: head strides must be >= n_tokens*128 and multiples of 8");
-  DecompressP p{static_cast<const uint16_t*>(latent), ld_latent, n_tokens,
-                static_cast<const uint16_t*>(w_t), H_total, h_begin, Hsel,
-                static_cast<uint16_t*>(k_nope), k_head_stride, static_cast<uint16_t*>(v), v_head_stride};
-  return launch_gemm(p, n_tokens, 2 * Hsel * BN, reinterpret_cast<hipStream_t>(stream), "mla_decompress");
+  DecArgs d{static_cast<const uint16_t*>(latent), ld_latent, n_tokens,
+            static_cast<const uint16_t*>(w_t), H_total, h_begin, Hsel,
+            static_cast<uint16_t*>(k_nope), k_head_stride, static_cast<uint16_t*>(v), v_head_stride,
+            (n_tokens + kDT - 1) / kDT, Hsel * 2 * kDnope / kDT};
+  const int64_t total = (int64_t)d.n_mt * d.n_nt;
+  MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_decompress: problem too large");
+  const size_t lds = (size_t)2 * kDStage * sizeof(uint16_t);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decompress_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    mla_set_error("mla_decompress: cannot reserve %zu bytes of LDS", lds);
+    return MLA_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(decompress_kernel, dim3((unsigned)total), dim3(kDThreads), lds,
+                     reinterpret_cast<hipStream_t>(stream), d);
+  return mla_check_launch("mla_decompress");
 }
 
 extern "C" int mla_head_partition_merge(const void* art_out, const void* rec_out,

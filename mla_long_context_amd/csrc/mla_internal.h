@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/mla.h"
+#include "mla.h"
 
 // ---------------------------------------------------------------- geometry
 constexpr int kDc = 512;        // compressed latent width
