@@ -39,6 +39,14 @@ struct AttnArgs {
   void* out; int64_t out_rs; float* lse; int64_t lse_rs;
 };
 
+// V^T tile in LDS: row = dv (0..127), 64 key positions per row, 144-byte row
+// pitch. On gfx950 (128 LDS banks, 16-byte reads served 32 lanes at a time)
+// this pitch makes the fragment reads conflict-free, and the transpose writes
+// are conflict-free when the 16 key quads of a tile vary fastest across lanes
+// (lane -> (kq = idx & 15, dq = idx >> 4)); with dv quads fastest instead,
+// rocprofv3 counted 28 bank-conflict cycles per write instruction.
+__device__ __forceinline__ int vt_index(int row, int pos) { return row * kVtLd + pos; }
+
 __device__ __forceinline__ int perm_quad(int kq) {
   // key quad kq (0..15 in the tile) -> LDS position of its 4 keys
   const int q4 = kq & 3;
@@ -55,8 +63,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int kVb = (16 * 32) / NT;        // 4x4 V blocks per thread
   static_assert(kKv >= 1 && kRv >= 1 && kVb >= 1, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTileK * kKsLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kDv * kVtLd];
+  // two LDS buffers: tile t is consumed from one while tile t+1 is written
+  // into the other, so one barrier per tile suffices
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kTileK * kKsLd];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt2[2][kDv * kVtLd];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -103,58 +113,65 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint16_t* vbase = a.v + (int64_t)hs * a.vhs + (int64_t)k0 * kDv;
   const uint16_t* rbase = a.lat + (int64_t)k0 * a.ld_lat + kDc;
 
-  u32x4 pk[kKv], pr[kRv];
-  u32x2 pv[kVb][4];
+  // register prefetch buffers: two tiles in flight (tile t+2 is loaded while
+  // tile t is computed and tile t+1 is written to LDS)
+  struct Pref {
+    u32x4 k[kKv], r[kRv];
+    u32x2 v[kVb][4];
+  };
+  Pref pa, pb;
   // Keys at or past n_k are clamped to the last key: their scores are masked
   // to -inf and their values meet p = 0, so no load needs a predicate.
   const int klast = n_k - 1;
-  auto gload = [&](int kt0) {
+  auto gload = [&](Pref& pf, int kt0) {
 #pragma unroll
     for (int j = 0; j < kKv; ++j) {
       const int idx = tid + NT * j, key = min(kt0 + (idx >> 4), klast), vec = idx & 15;
-      pk[j] = *reinterpret_cast<const u32x4*>(kbase + key * kDnope + vec * 8);
+      pf.k[j] = *reinterpret_cast<const u32x4*>(kbase + key * kDnope + vec * 8);
     }
 #pragma unroll
     for (int j = 0; j < kRv; ++j) {
       const int idx = tid + NT * j, key = min(kt0 + (idx >> 3), klast), vec = idx & 7;
-      pr[j] = *reinterpret_cast<const u32x4*>(rbase + (int64_t)key * a.ld_lat + vec * 8);
+      pf.r[j] = *reinterpret_cast<const u32x4*>(rbase + (int64_t)key * a.ld_lat + vec * 8);
     }
 #pragma unroll
     for (int j = 0; j < kVb; ++j) {
-      const int idx = tid + NT * j, kq = idx >> 5, dq = idx & 31;
+      const int idx = tid + NT * j, kq = idx & 15, dq = idx >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = min(kt0 + kq * 4 + r, klast);
-        pv[j][r] = *reinterpret_cast<const u32x2*>(vbase + key * kDv + dq * 4);
+        pf.v[j][r] = *reinterpret_cast<const u32x2*>(vbase + key * kDv + dq * 4);
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](const Pref& pf, int buf) {
+    uint16_t* Ks = Ks2[buf];
+    uint16_t* Vt = Vt2[buf];
 #pragma unroll
     for (int j = 0; j < kKv; ++j) {
       const int idx = tid + NT * j, key = idx >> 4, vec = idx & 15;
-      *reinterpret_cast<u32x4*>(Ks + key * kKsLd + vec * 8) = pk[j];
+      *reinterpret_cast<u32x4*>(Ks + key * kKsLd + vec * 8) = pf.k[j];
     }
 #pragma unroll
     for (int j = 0; j < kRv; ++j) {
       const int idx = tid + NT * j, key = idx >> 3, vec = idx & 7;
-      *reinterpret_cast<u32x4*>(Ks + key * kKsLd + kDnope + vec * 8) = pr[j];
+      *reinterpret_cast<u32x4*>(Ks + key * kKsLd + kDnope + vec * 8) = pf.r[j];
     }
 #pragma unroll
     for (int j = 0; j < kVb; ++j) {
-      const int idx = tid + NT * j, kq = idx >> 5, dq = idx & 31;
+      const int idx = tid + NT * j, kq = idx & 15, dq = idx >> 4;
       const int pos = perm_quad(kq);
       // 4x4 transpose of bf16: rows = keys r, cols = dv c
-      const uint32_t x0 = pv[j][0].x, y0 = pv[j][0].y, x1 = pv[j][1].x, y1 = pv[j][1].y;
-      const uint32_t x2 = pv[j][2].x, y2 = pv[j][2].y, x3 = pv[j][3].x, y3 = pv[j][3].y;
+      const uint32_t x0 = pf.v[j][0].x, y0 = pf.v[j][0].y, x1 = pf.v[j][1].x, y1 = pf.v[j][1].y;
+      const uint32_t x2 = pf.v[j][2].x, y2 = pf.v[j][2].y, x3 = pf.v[j][3].x, y3 = pf.v[j][3].y;
       u32x2 c0 = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
       u32x2 c1 = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
       u32x2 c2 = {(y0 & 0xffffu) | (y1 << 16), (y2 & 0xffffu) | (y3 << 16)};
       u32x2 c3 = {(y0 >> 16) | (y1 & 0xffff0000u), (y2 >> 16) | (y3 & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(Vt + (dq * 4 + 0) * kVtLd + pos) = c0;
-      *reinterpret_cast<u32x2*>(Vt + (dq * 4 + 1) * kVtLd + pos) = c1;
-      *reinterpret_cast<u32x2*>(Vt + (dq * 4 + 2) * kVtLd + pos) = c2;
-      *reinterpret_cast<u32x2*>(Vt + (dq * 4 + 3) * kVtLd + pos) = c3;
+      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 0, pos)) = c0;
+      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 1, pos)) = c1;
+      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 2, pos)) = c2;
+      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 3, pos)) = c3;
     }
   };
 
@@ -171,17 +188,26 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int row_lim = row + shift;           // causal: keys <= row_lim are visible
   const float c = a.scale_log2;              // scale * log2(e); scores stay raw until exp2
 
+  // software pipeline over key tiles: iteration t loads tile t+2 into one
+  // register buffer, computes tile t from LDS buffer t%2, and writes tile t+1
+  // (loaded one iteration earlier) into LDS buffer (t+1)%2. Out-of-range tile
+  // indices are clamped to the last tile: harmless re-reads keep the loop
+  // body branch-free.
+  const int last_kt0 = (ntiles - 1) * kTileK;
   if (ntiles > 0) {
-    gload(0);
-    lstore();
+    gload(pa, 0);
+    gload(pb, min(kTileK, last_kt0));
+    lstore(pa, 0);
   }
   __syncthreads();
-  const int last_kt0 = (ntiles - 1) * kTileK;
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // pn: free register buffer (its tile is already in LDS); pw: holds tile t+1
+  auto step = [&](int kt, Pref& pn, Pref& pw) {
     const int kt0 = kt * kTileK;
-    // prefetch the next tile (the last iteration re-reads its own tile: the
-    // loop body stays branch-free so the loads overlap the MFMA work below)
-    gload(min(kt0 + kTileK, last_kt0));
+    const int cur = kt & 1;
+    gload(pn, min(kt0 + 2 * kTileK, last_kt0));
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* Ks = Ks2[cur];
+    const uint16_t* Vt = Vt2[cur];
     if (kt0 < wave_kend) {
       f32x16 S[2];
 #pragma unroll
@@ -253,15 +279,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         const bf16x8 pf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (d * 32 + l32) * kVtLd + mm * 16 + g * 8);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + vt_index(d * 32 + l32, mm * 16 + g * 8));
           O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[d], 0, 0, 0);
         }
       }
     }
+    lstore(pw, cur ^ 1);
     __syncthreads();
-    lstore();
-    __syncthreads();
+  };
+  // unrolled by two so each register buffer keeps fixed registers
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(kt, pa, pb);
+    if (kt + 1 < ntiles) step(kt + 1, pb, pa);
   }
+
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
