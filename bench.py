@@ -79,6 +79,51 @@ def traffic_for(kernel_src):
     return d.get("bytes_per_launch")
 
 
+def _counter_rows(csv_path, counter):
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFIC_FILE):
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE per-dispatch counters (KiB) of the
+    context-attention launches into HBM bytes per launch, each scaled by what
+    the same counter reads for the 1 GiB copy of --calibrate-copy."""
+    gib_kib = float(1 << 20)
+    # the copy dispatches (the fill before them reads almost nothing)
+    cal_f = [v for n, v in _counter_rows(cal_fetch_csv, "FETCH_SIZE") if v > gib_kib / 8]
+    cal_w = [v for n, v in _counter_rows(cal_write_csv, "WRITE_SIZE") if v > gib_kib / 8]
+    kf = gib_kib / (sum(cal_f) / len(cal_f))
+    kw = gib_kib / (sum(cal_w) / len(cal_w))
+    ctx = lambda n: "attn_kernel<8, false, false" in n
+    f = [v for n, v in _counter_rows(fetch_csv, "FETCH_SIZE") if ctx(n)]
+    w = [v for n, v in _counter_rows(write_csv, "WRITE_SIZE") if ctx(n)]
+    fetch_b = sum(f) / len(f) * 1024 * kf
+    write_b = sum(w) / len(w) * 1024 * kw
+    d = {"kernel": "mla_prefill_attn (context pass), 4 x (8192 ctx + 1024 new), H=128, chunk 4096",
+         "source_sha256_16": source_hash(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip")),
+         "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+         "bytes_per_launch": round(fetch_b + write_b),
+         "copy_scale": {"fetch": round(kf, 4), "write": round(kw, 4)},
+         "launches": {"fetch": len(f), "write": len(w)},
+         "commands": [
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/w -o w -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/cf -o cf -- python3 bench.py --calibrate-copy",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/cw -o cw -- python3 bench.py --calibrate-copy",
+             "python3 bench.py --write-traffic <out>/f/f_counter_collection.csv <out>/w/w_counter_collection.csv "
+             "<out>/cf/cf_counter_collection.csv <out>/cw/cw_counter_collection.csv"],
+         "note": "per-dispatch counters in KiB, averaged over the context-attention launches; the 1 GiB "
+                 "copy reads FETCH_SIZE x 1/2 and WRITE_SIZE x 1, hence the scales"}
+    with open(out, "w") as fh:
+        json.dump(d, fh, indent=1)
+    print(json.dumps(d))
+
+
 def cpu_baseline(prob, budget_s=15.0):
     """The fp64 oracle as it stands, on request 0 of the same workload, one
     head at a time, until about budget_s seconds of host work are spent."""
@@ -115,7 +160,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
+    ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
+                    help="FETCH_SIZE and WRITE_SIZE counter CSVs of a bench run, then of a "
+                         "--calibrate-copy run: write the HBM-traffic record and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only; the prefill path has no multi-GPU mode. "
               "Run with --gpus 1.", file=sys.stderr)
