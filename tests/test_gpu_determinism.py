@@ -1,0 +1,49 @@
+"""Every kernel is deterministic: two runs on the same inputs give identical
+bits (no atomics or order-dependent reductions anywhere on the path), and
+the chunked path does not depend on workspace contents left by earlier runs
+(workspaces are refilled with NaN between runs)."""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+from mla_long_context_amd.prefill import ChunkedPrefill, ReusePrefill
+
+from gpu_util import bits, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _poison(*ts):
+    for t in ts:
+        t.fill_(float("nan"))
+
+
+def test_chunked_prefill_bitwise_repeatable_with_poisoned_workspaces():
+    require_gpu()
+    say("determinism: chunked prefill")
+    prob = mi.make_problem(8, [64 * 9, 320, 0], [200, 77, 5], 256, "bf16", seed=81, extra_blocks=2,
+                           poison=True)
+    pre = ChunkedPrefill(prob)
+    pre.run()
+    torch.cuda.synchronize()
+    o1, l1 = bits(pre.out).copy(), pre.lse.cpu().numpy().copy()
+    _poison(pre.lat_ws, pre.k_ws, pre.v_ws, pre.tmp_o, pre.tmp_l, pre.acc_o, pre.acc_l, pre.out, pre.lse)
+    pre.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, bits(pre.out))
+    assert np.array_equal(l1.view(np.uint32), pre.lse.cpu().numpy().view(np.uint32))
+
+
+def test_reuse_prefill_bitwise_repeatable_with_poisoned_workspaces():
+    require_gpu()
+    say("determinism: reuse prefill")
+    prob = mi.make_reuse_problem(H=8, n_local=7, L=512 + 64, T=100, delta=4096, P=7,
+                                 d_mid=256, d_model=256, chunk=256, seed=82)
+    pre = ReusePrefill(prob)
+    y1 = bits(pre.run()).copy()
+    _poison(pre.q_rel, pre.lat_ws, pre.k_ws, pre.v_ws, pre.acc_G, pre.acc_L, pre.tmp_G, pre.tmp_L,
+            pre.glob_out, pre.rec_out, pre.z, pre.y)
+    y2 = bits(pre.run())
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2)
