@@ -37,9 +37,17 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags. The attention kernel's softmax reads and rewrites
+# the MFMA accumulators every tile; keeping MFMA results in VGPRs (instead of
+# AGPRs) saves the accumulator copies around each softmax.
+EXTRA = {
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in ln]

@@ -26,6 +26,21 @@ int mla_check_launch(const char* what) {
   return MLA_OK;
 }
 
+int mla_num_cus() {
+  // per-device cache of the compute-unit count (persistent kernels size
+  // their grids by it); 0 until first asked on that device
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 extern "C" const char* mla_last_error(void) { return g_err; }
 
 extern "C" int mla_abi_version(void) { return 1; }

@@ -6,25 +6,22 @@
 //
 // Workgroup = (request, head, tile of 32*NW query rows), NW wavefronts of 64
 // lanes, one wavefront per 32 query rows. Per 64-key tile:
-//   S^T[key][q] = K . Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS (the
-//                             k_rope columns are read once per tile for the
-//                             workgroup), B = Q held in VGPRs for the kernel.
+//   S^T[key][q] = K . Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q
+//                             held in VGPRs for the whole kernel.
 //   online softmax            lane l owns query row l%32; its 32 scores of a
 //                             tile sit in its own accumulators and those of
 //                             lane l^32, so a row max/sum is one lane swap.
-//   O^T[dv][q] += V^T . P^T   A = V^T from LDS, B = P^T converted in place
-//                             from the S^T accumulators (no LDS round trip).
-// V rows are transposed into LDS with a 4x4 register transpose, and the key
-// order inside each 16-key group is permuted so that the PV operand of a
-// lane is one 16-byte LDS read. The next tile is prefetched into registers
-// while the current one is consumed.
+//   O^T[dv][q] += V^T . P^T   A = V^T read from the row-major V tile with
+//                             transposing LDS reads, B = P^T converted in
+//                             place from the S^T accumulators.
+// K and V tiles go from HBM straight into LDS (global_load_lds, no register
+// staging) through two or three LDS stages, so the loads of the next tiles
+// run while the current one is computed.
 #include "mla_internal.h"
 
 namespace {
 
 constexpr int kTileK = 64;
-constexpr int kKsLd = kDqk + 8;   // 200 elements = 400 B per key row (conflict-free b128 reads)
-constexpr int kVtLd = kTileK + 8; // 72 elements = 144 B per dv row
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;      // log2 headroom of the lazy softmax reference
@@ -39,37 +36,55 @@ struct AttnArgs {
   void* out; int64_t out_rs; float* lse; int64_t lse_rs;
 };
 
-// V^T tile in LDS: row = dv (0..127), 64 key positions per row, 144-byte row
-// pitch. On gfx950 (128 LDS banks, 16-byte reads served 32 lanes at a time)
-// this pitch makes the fragment reads conflict-free, and the transpose writes
-// are conflict-free when the 16 key quads of a tile vary fastest across lanes
-// (lane -> (kq = idx & 15, dq = idx >> 4)); with dv quads fastest instead,
-// rocprofv3 counted 28 bank-conflict cycles per write instruction.
-__device__ __forceinline__ int vt_index(int row, int pos) { return row * kVtLd + pos; }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ int perm_quad(int kq) {
-  // key quad kq (0..15 in the tile) -> LDS position of its 4 keys
-  const int q4 = kq & 3;
-  const int pos4 = (q4 == 1) ? 2 : (q4 == 2 ? 1 : q4);
-  return (kq & ~3) * 4 + pos4 * 4;
+// LDS tiles are filled by global->LDS DMA (one 16-byte chunk per lane, 64
+// consecutive chunks per wavefront instruction), so rows carry no padding;
+// bank conflicts of the fragment reads are removed by XOR-swizzling chunk
+// positions inside a row instead. Measured on gfx950 with rocprofv3
+// (SQ_LDS_BANK_CONFLICT) both read patterns below are conflict-free, while the
+// unswizzled layouts cost 4 (K) and 6 (V) conflict cycles per read.
+//   K tile: 64 keys x 384 B (k_nope 16 chunks | k_rope 8 chunks); chunk c of
+//           key r sits at position c ^ ((r >> 1) & 7) (low three bits only).
+//   V tile: 64 keys x 256 B (16 chunks), row-major; chunk c of key r sits at
+//           position c ^ ((r & 3) << 2). The PV operand (eight keys of one dv
+//           column per lane) is read with ds_read_b64_tr_b16, which hands
+//           each lane four consecutive keys of one column.
+constexpr int kKRow = 384;                 // bytes per K row in LDS
+constexpr int kVRow = 256;                 // bytes per V row in LDS
+constexpr int kKTile = kTileK * kKRow;     // 24576
+constexpr int kVTile = kTileK * kVRow;     // 16384
+
+// third LDS stage, allocated only by kernels that use three stages
+template <int NB>
+__device__ __forceinline__ uint8_t* lds_stage2() {
+  if constexpr (NB == 3) {
+    __shared__ __attribute__((aligned(1024))) uint8_t S2[kKTile + kVTile];
+    return S2;
+  } else {
+    return nullptr;
+  }
 }
 
 template <int NW, bool kCausal, bool kRowIds, int kOutDt>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
   constexpr int ROWS = 32 * NW;
-  constexpr int kKv = (kTileK * 16) / NT;    // 16-byte k_nope vectors per thread
-  constexpr int kRv = (kTileK * 8) / NT;     // 16-byte rope vectors per thread (>= 1 for NW <= 8)
-  constexpr int kVb = (16 * 32) / NT;        // 4x4 V blocks per thread
-  static_assert(kKv >= 1 && kRv >= 1 && kVb >= 1, "tile split");
+  constexpr int NB = (NW == 8) ? 3 : 2;    // LDS stages (tiles in flight)
+  constexpr int kKj = (kTileK * 24) / (64 * NW);   // K DMA instructions per wavefront per tile
+  constexpr int kVj = (kTileK * 16) / (64 * NW);   // V DMA instructions per wavefront per tile
+  constexpr int kDma = kKj + kVj;
+  static_assert(kKj * 64 * NW == kTileK * 24 && kVj * 64 * NW == kTileK * 16, "tile split");
 
-  // two LDS buffers: tile t is consumed from one while tile t+1 is written
-  // into the other, so one barrier per tile suffices
-  __shared__ __attribute__((aligned(16))) uint16_t Ks2[2][kTileK * kKsLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt2[2][kDv * kVtLd];
+  // one array per stage (K tile then V tile); two stages take 80 KB, so two
+  // 4-wavefront workgroups fit in one CU's 160 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t S0[kKTile + kVTile], S1[kKTile + kVTile];
+  uint8_t* S2 = lds_stage2<NB>();
+  uint8_t *K0 = S0, *V0 = S0 + kKTile, *K1 = S1, *V1 = S1 + kKTile;
+  uint8_t *K2 = S2, *V2 = S2 + kKTile;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   const uint32_t total = (uint32_t)a.batch * a.Hsel * a.n_qt;
@@ -113,67 +128,44 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint16_t* vbase = a.v + (int64_t)hs * a.vhs + (int64_t)k0 * kDv;
   const uint16_t* rbase = a.lat + (int64_t)k0 * a.ld_lat + kDc;
 
-  // register prefetch buffers: two tiles in flight (tile t+2 is loaded while
-  // tile t is computed and tile t+1 is written to LDS)
-  struct Pref {
-    u32x4 k[kKv], r[kRv];
-    u32x2 v[kVb][4];
-  };
-  Pref pa, pb;
-  // Keys at or past n_k are clamped to the last key: their scores are masked
-  // to -inf and their values meet p = 0, so no load needs a predicate.
+  // DMA sources of this lane: chunk slot -> (key row, global chunk); keys at
+  // or past n_k are clamped to the last key (masked scores, p = 0 values), so
+  // no load needs a predicate.
   const int klast = n_k - 1;
-  auto gload = [&](Pref& pf, int kt0) {
+  auto dma = [&](uint8_t* Kd, uint8_t* Vd, int kt0) {
 #pragma unroll
-    for (int j = 0; j < kKv; ++j) {
-      const int idx = tid + NT * j, key = min(kt0 + (idx >> 4), klast), vec = idx & 15;
-      pf.k[j] = *reinterpret_cast<const u32x4*>(kbase + key * kDnope + vec * 8);
+    for (int j = 0; j < kKj; ++j) {
+      const int slot = (j * NW + wave) * 64 + lane;
+      const int r = slot / 24, c = slot % 24;
+      const int gc = (c & ~7) | ((c ^ (r >> 1)) & 7);
+      const int key = min(kt0 + r, klast);
+      const uint16_t* src = gc < 16 ? kbase + (int64_t)key * kDnope + gc * 8
+                                    : rbase + (int64_t)key * a.ld_lat + (gc - 16) * 8;
+      dma16(src, Kd + (j * NW + wave) * 1024);
     }
 #pragma unroll
-    for (int j = 0; j < kRv; ++j) {
-      const int idx = tid + NT * j, key = min(kt0 + (idx >> 3), klast), vec = idx & 7;
-      pf.r[j] = *reinterpret_cast<const u32x4*>(rbase + (int64_t)key * a.ld_lat + vec * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < kVb; ++j) {
-      const int idx = tid + NT * j, kq = idx & 15, dq = idx >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(kt0 + kq * 4 + r, klast);
-        pf.v[j][r] = *reinterpret_cast<const u32x2*>(vbase + key * kDv + dq * 4);
-      }
-    }
-  };
-  auto lstore = [&](const Pref& pf, int buf) {
-    uint16_t* Ks = Ks2[buf];
-    uint16_t* Vt = Vt2[buf];
-#pragma unroll
-    for (int j = 0; j < kKv; ++j) {
-      const int idx = tid + NT * j, key = idx >> 4, vec = idx & 15;
-      *reinterpret_cast<u32x4*>(Ks + key * kKsLd + vec * 8) = pf.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kRv; ++j) {
-      const int idx = tid + NT * j, key = idx >> 3, vec = idx & 7;
-      *reinterpret_cast<u32x4*>(Ks + key * kKsLd + kDnope + vec * 8) = pf.r[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kVb; ++j) {
-      const int idx = tid + NT * j, kq = idx & 15, dq = idx >> 4;
-      const int pos = perm_quad(kq);
-      // 4x4 transpose of bf16: rows = keys r, cols = dv c
-      const uint32_t x0 = pf.v[j][0].x, y0 = pf.v[j][0].y, x1 = pf.v[j][1].x, y1 = pf.v[j][1].y;
-      const uint32_t x2 = pf.v[j][2].x, y2 = pf.v[j][2].y, x3 = pf.v[j][3].x, y3 = pf.v[j][3].y;
-      u32x2 c0 = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-      u32x2 c1 = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-      u32x2 c2 = {(y0 & 0xffffu) | (y1 << 16), (y2 & 0xffffu) | (y3 << 16)};
-      u32x2 c3 = {(y0 >> 16) | (y1 & 0xffff0000u), (y2 >> 16) | (y3 & 0xffff0000u)};
-      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 0, pos)) = c0;
-      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 1, pos)) = c1;
-      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 2, pos)) = c2;
-      *reinterpret_cast<u32x2*>(Vt + vt_index(dq * 4 + 3, pos)) = c3;
+    for (int j = 0; j < kVj; ++j) {
+      const int slot = (j * NW + wave) * 64 + lane;
+      const int r = slot >> 4, c = slot & 15;
+      const int gc = c ^ ((r & 3) << 2);
+      const int key = min(kt0 + r, klast);
+      dma16(vbase + (int64_t)key * kDv + gc * 8, Vd + (j * NW + wave) * 1024);
     }
   };
+
+  // per-lane fragment read offsets (bytes)
+  int koff[4];                               // K: row l32, chunk 2s+g -> + (s>>2)*128 + kb*32 rows
+  {
+    const int m = (l32 >> 1) & 7;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) koff[qd] = l32 * kKRow + (((2 * qd + g) ^ m) * 16);
+  }
+  int voff[4];                               // V^T: dv block d; + (16 mm + 8 half) rows
+  {
+    const int a4 = (lane & 15) >> 2, b4 = lane & 3, g16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) voff[d] = (4 * g + a4) * kVRow + 64 * (d ^ a4) + 32 * g16 + 8 * b4;
+  }
 
   f32x16 O[4];
 #pragma unroll
@@ -188,111 +180,125 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int row_lim = row + shift;           // causal: keys <= row_lim are visible
   const float c = a.scale_log2;              // scale * log2(e); scores stay raw until exp2
 
-  // software pipeline over key tiles: iteration t loads tile t+2 into one
-  // register buffer, computes tile t from LDS buffer t%2, and writes tile t+1
-  // (loaded one iteration earlier) into LDS buffer (t+1)%2. Out-of-range tile
-  // indices are clamped to the last tile: harmless re-reads keep the loop
-  // body branch-free.
-  const int last_kt0 = (ntiles - 1) * kTileK;
-  if (ntiles > 0) {
-    gload(pa, 0);
-    gload(pb, min(kTileK, last_kt0));
-    lstore(pa, 0);
-  }
-  __syncthreads();
-  // pn: free register buffer (its tile is already in LDS); pw: holds tile t+1
-  auto step = [&](int kt, Pref& pn, Pref& pw) {
-    const int kt0 = kt * kTileK;
-    const int cur = kt & 1;
-    gload(pn, min(kt0 + 2 * kTileK, last_kt0));
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* Ks = Ks2[cur];
-    const uint16_t* Vt = Vt2[cur];
-    if (kt0 < wave_kend) {
-      f32x16 S[2];
+  auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int kt0) {
+    f32x16 S[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kDqk / 16; ++s) {
+    for (int s = 0; s < kDqk / 16; ++s) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * kKsLd + s * 16 + g * 8);
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + koff[s & 3] + (s >> 2) * 128 + kb * 32 * kKRow);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
       }
-      // masking only on tiles that cross the key end or the causal diagonal
-      const bool edge = (kt0 + kTileK > n_k) || (kCausal && kt0 + kTileK - 1 > wave_first_lim);
-      if (edge) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool vis = key < n_k && (!kCausal || key <= row_lim);
-            S[kb][i] = vis ? S[kb][i] : -INFINITY;
-          }
-      }
-      // row max of raw scores (scale > 0 keeps the order): own 32 keys, then lane ^ 32
-      float mt = S[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, S[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[1][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      // Lazy reference max (log2 units): it only moves when the tile max
-      // exceeds it by more than kLazy, so p <= 2^kLazy and the rescale of O is
-      // skipped on almost every tile. The normalisation uses the same
-      // reference, so the result does not depend on when it moved.
-      const float mtc = mt * c;
-      const bool bump = mtc > m_ref + kLazy;     // false while mt = -inf
-      const float m_new = bump ? mtc : m_ref;
-      const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;   // 0 from -inf
-      const float mc = (m_new == -INFINITY) ? 0.f : m_new;
-      float ps = 0.f;
+    }
+    // masking only on tiles that cross the key end or the causal diagonal
+    const bool edge = (kt0 + kTileK > n_k) || (kCausal && kt0 + kTileK - 1 > wave_first_lim);
+    if (edge) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -mc));
-          S[kb][i] = p;
-          ps += p;
+          const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool vis = key < n_k && (!kCausal || key <= row_lim);
+          S[kb][i] = vis ? S[kb][i] : -INFINITY;
         }
-      l_run = fmaf(l_run, alpha, ps);
-      if (__any(bump)) {
+    }
+    // row max of raw scores (scale > 0 keeps the order): own 32 keys, then lane ^ 32
+    float mt = S[0][0];
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, S[0][i]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[1][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // Lazy reference max (log2 units): it only moves when the tile max
+    // exceeds it by more than kLazy, so p <= 2^kLazy and the rescale of O is
+    // skipped on almost every tile. The normalisation uses the same
+    // reference, so the result does not depend on when it moved.
+    const float mtc = mt * c;
+    const bool bump = mtc > m_ref + kLazy;     // false while mt = -inf
+    const float m_new = bump ? mtc : m_ref;
+    const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;   // 0 from -inf
+    const float mc = (m_new == -INFINITY) ? 0.f : m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][i], c, -mc));
+        S[kb][i] = p;
+        ps += p;
       }
-      m_ref = m_new;
-      // P^T operands: MFMA mm covers keys 16mm..16mm+15 of the tile
+    l_run = fmaf(l_run, alpha, ps);
+    if (__any(bump)) {
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const int kb = mm >> 1, i0 = 8 * (mm & 1);
-        u32x4 u;
-        u.x = cvt_pk_bf16(S[kb][i0 + 0], S[kb][i0 + 1]);
-        u.y = cvt_pk_bf16(S[kb][i0 + 2], S[kb][i0 + 3]);
-        u.z = cvt_pk_bf16(S[kb][i0 + 4], S[kb][i0 + 5]);
-        u.w = cvt_pk_bf16(S[kb][i0 + 6], S[kb][i0 + 7]);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, u);
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + vt_index(d * 32 + l32, mm * 16 + g * 8));
-          O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[d], 0, 0, 0);
-        }
+        for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
+    }
+    m_ref = m_new;
+    // P^T operand of MFMA mm (keys 16mm..16mm+15 of the tile): lane slots
+    // 0-3 hold keys 16mm+4g+0..3, slots 4-7 keys 16mm+8+4g+0..3, which is
+    // where the S^T accumulator layout puts them; the V^T operand is read
+    // for the same keys with two transposing reads.
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int kb = mm >> 1, i0 = 8 * (mm & 1);
+      u32x4 u;
+      u.x = cvt_pk_bf16(S[kb][i0 + 0], S[kb][i0 + 1]);
+      u.y = cvt_pk_bf16(S[kb][i0 + 2], S[kb][i0 + 3]);
+      u.z = cvt_pk_bf16(S[kb][i0 + 4], S[kb][i0 + 5]);
+      u.w = cvt_pk_bf16(S[kb][i0 + 6], S[kb][i0 + 7]);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint8_t* vp = Vs + voff[d] + 16 * mm * kVRow;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * kVRow));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[d], 0, 0, 0);
       }
     }
-    lstore(pw, cur ^ 1);
-    __syncthreads();
   };
-  // unrolled by two so each register buffer keeps fixed registers
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    step(kt, pa, pb);
-    if (kt + 1 < ntiles) step(kt + 1, pb, pa);
-  }
 
+  // Pipeline over key tiles with NB LDS stages: step t waits for its own DMA
+  // of tile t, meets the others at the barrier (after which tile t is
+  // visible and stage (t-1) % NB is free), issues the DMA of tile t+NB-1
+  // into that stage and computes tile t. Tile indices past the end are
+  // clamped to the last tile, so every step issues the same number of DMA
+  // instructions and the vector-memory counter stays exact.
+  const int last_kt0 = (ntiles - 1) * kTileK;
+  if (ntiles > 0) {
+    dma(K0, V0, 0);
+    if (NB == 3) dma(K1, V1, min(kTileK, last_kt0));
+  }
+  // the Q fragments (and the first tiles) have landed: without this wait the
+  // compiler, which does not see the DMA, would wait for every outstanding
+  // load before the first product of each tile
+  wait_vmcnt<0>();
+  auto step = [&](int kt, uint8_t* Kc, uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
+    const int kt0 = kt * kTileK;
+    wait_vmcnt<kDma * (NB - 2)>();
+    __syncthreads();
+    dma(Kn, Vn, min(kt0 + (NB - 1) * kTileK, last_kt0));
+    if (kt0 < wave_kend) compute(Kc, Vc, kt0);
+  };
+  if (NB == 3) {
+    for (int kt = 0; kt < ntiles; kt += 3) {
+      step(kt, K0, V0, K2, V2);
+      if (kt + 1 < ntiles) step(kt + 1, K1, V1, K0, V0);
+      if (kt + 2 < ntiles) step(kt + 2, K2, V2, K1, V1);
+    }
+  } else {
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(kt, K0, V0, K1, V1);
+      if (kt + 1 < ntiles) step(kt + 1, K1, V1, K0, V0);
+    }
+  }
+  // no DMA may still be writing this workgroup's LDS when it ends
+  wait_vmcnt<0>();
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -372,9 +378,12 @@ extern "C" int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, in
 
   // rows per workgroup: 256 (8 wavefronts) for long query sets, fewer when
   // that would leave most wavefronts without rows or the grid too small.
+  // Causal passes use at most 4 wavefronts: in a 256-row tile the wavefronts
+  // above the diagonal idle through up to 3.5 key tiles each, and the 80 KB
+  // two-stage LDS of the 4-wavefront kernel lets two workgroups share a CU.
   int NW = 8;
   if (max_q <= 64) NW = 2;
-  else if (max_q <= 128) NW = 4;
+  else if (max_q <= 128 || causal) NW = 4;
   const int rows = 32 * NW;
   const int n_qt = (max_q + rows - 1) / rows;
   const int64_t total = (int64_t)batch * Hsel * n_qt;

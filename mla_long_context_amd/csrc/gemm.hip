@@ -15,6 +15,8 @@
 // is issued as D^T = Bt_frag x A_frag so that each lane ends up holding four
 // consecutive output columns of one row, which the epilogue packs into 8-byte
 // LDS writes before 16-byte coalesced global stores.
+#include <algorithm>
+
 #include "mla_internal.h"
 
 namespace {
@@ -194,22 +196,59 @@ int launch_gemm(const P& p, int M, int N, hipStream_t s, const char* what) {
 
 // ---------------------------------------------------------------- decompression kernel
 //
-// 256 x 256 output tile (tokens x columns) per workgroup of 8 wavefronts (two
-// per SIMD: LDS latency is only covered with a second wavefront), each
-// wavefront a 64 x 128 sub-tile held as 2 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 accumulators. Per 16-wide k step a wavefront reads
-// 6 fragments from LDS for 8 MFMAs. Both operands are staged through
-// double-buffered LDS (rows padded to 144 B: conflict-free 16-byte reads) by
-// coalesced 16-byte global loads, prefetched into registers one 64-wide k step
-// ahead. The MFMA is issued as D^T so a lane owns four consecutive output
-// columns; the epilogue goes through LDS so global stores are whole 256-byte
-// rows of one head's k_nope or v. A wavefront's 128 columns are always one
-// head's W_UK or W_UV, also when a tile straddles the W_UK / W_UV boundary.
+// Persistent: one workgroup of 8 wavefronts per CU walks 256 x 256 output
+// tiles (tokens x columns). Each wavefront owns a 64 x 128 sub-tile, held as
+// 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 accumulators and issued as D^T =
+// W_frag x A_frag, so a lane holds four consecutive output columns of one
+// token. A wavefront's 128 columns are always one head's W_UK or W_UV, also
+// when a tile straddles the W_UK / W_UV boundary.
+//
+// Operands go from HBM straight into LDS (global_load_lds, no register
+// staging) in k steps of 64 through two LDS stages of 64 KB; each DMA
+// instruction moves 8 rows x 128 B, whole cache lines (k steps of 32, which
+// give 64-byte row pieces, measured 6% slower with twice the L2 requests).
+// The pipeline runs over the flattened (tile, k step) sequence of the
+// workgroup, so the first step of the next tile is already in flight while a
+// tile finishes. LDS rows carry no padding: chunks are XOR-swizzled within a
+// row (dec_swz) so that every 16-lane group of a fragment read hits 16
+// distinct 16-byte bank groups.
+//
+// Epilogue: no LDS. One v_permlane32_swap per register pair gives each lane
+// eight consecutive bf16 columns, stored as one 16-byte buffer store (rows past
+// the last token are dropped by the buffer range check). The stores of a
+// tile are issued in the first step of the next tile, after that step's DMA,
+// so they overlap its products.
+//
+// Completion of the DMA is tracked with the vector-memory counter, which
+// counts the buffer stores too. Vector memory operations report completion to
+// the wavefront in issue order, so a step waits until no more operations are
+// outstanding than were issued after its own DMA: the DMAs of the steps
+// already prefetched beyond it, plus the 16 stores of the previous tile when
+// those were issued after this step's DMA (the first kDNS-1 steps after a
+// tile boundary). Every wavefront issues exactly kDDma DMAs per step and 16
+// stores per tile, with no predication, so the count is exact.
 constexpr int kDT = 256;                       // tile edge (tokens and columns)
 constexpr int kDBK = 64;                       // k step
-constexpr int kDLd = kDBK + 8;                 // padded LDS row, elements
-constexpr int kDStage = 2 * kDT * kDLd;        // A and B rows of one stage, elements
+constexpr int kDSteps = kDc / kDBK;            // k steps per tile
+constexpr int kDNS = 2;                        // LDS stages
+constexpr int kDRow = kDBK * 2;                // bytes per row in LDS
+constexpr int kDChunks = kDRow / 16;           // 16-byte chunks per row
+constexpr int kDRowsPerDma = 64 / kDChunks;    // rows covered by one DMA instruction
+constexpr int kDOpB = kDT * kDRow;             // bytes per operand per stage
+constexpr int kDStageB = 2 * kDOpB;            // bytes per stage (A then W)
 constexpr int kDThreads = 512;
+constexpr int kDDmaOp = kDOpB / 1024 / 8;      // DMA instructions per wavefront per operand per step
+constexpr int kDDma = 2 * kDDmaOp;             // DMA instructions per wavefront per step
+constexpr int kDStores = 16;                   // stores per wavefront per tile
+static_assert(kDNS * kDStageB <= 160 * 1024 && (kDNS & (kDNS - 1)) == 0 && (kDSteps & (kDSteps - 1)) == 0,
+              "decompression LDS ring");
+
+// LDS position of chunk c of row r: rows are swizzled so that the 16 rows
+// read by 16 consecutive lanes (same chunk) fall on 16 distinct 16-byte bank
+// groups of a 256-byte bank line
+__device__ __forceinline__ int dec_swz(int r, int c) {
+  return c ^ ((r / (16 / kDChunks)) % kDChunks);
+}
 
 struct DecArgs {
   const uint16_t* lat; int64_t ld; int M;
@@ -218,128 +257,173 @@ struct DecArgs {
   int n_mt, n_nt;
 };
 
+// rank (0 .. n_mt*n_nt-1) -> (token tile, column tile): consecutive ranks
+// walk kGroupM token tiles x all column tiles, so the workgroups of one XCD,
+// which take consecutive ranks together, share 4 latent tiles and 8 weight
+// tiles (3 MB) in that XCD's L2.
+__device__ __forceinline__ void dec_tile(int rank, int n_mt, int n_nt, int& mt, int& nt) {
+  constexpr int kGroupM = 4;
+  const int per_group = kGroupM * n_nt;
+  const int first_mt = (rank / per_group) * kGroupM;
+  const int gm = min(n_mt - first_mt, kGroupM);
+  const int in_group = rank % per_group;
+  mt = first_mt + in_group % gm;
+  nt = in_group / gm;
+}
+
 __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];   // [2 stages][A 256 | B 256][kDLd]
+  extern __shared__ __attribute__((aligned(1024))) uint8_t dlds[];   // kDNS stages
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;      // 4 x 2 wavefronts: 64 tokens x 128 columns each
   const int l32 = lane & 31, g = lane >> 5;
-  // Grouped order: within an XCD's contiguous range of tiles, consecutive
-  // tiles walk kGroupM token tiles x all column tiles, so the 32 tiles in
-  // flight on an XCD share 4 latent tiles and 8 weight tiles (3 MB, resident
-  // in its 4 MB L2) instead of streaming 32 latent tiles.
-  constexpr int kGroupM = 4;
-  const int work = (int)xcd_remap(blockIdx.x, (uint32_t)(a.n_mt * a.n_nt));
-  const int per_group = kGroupM * a.n_nt;
-  const int first_mt = (work / per_group) * kGroupM;
-  const int gm = min(a.n_mt - first_mt, kGroupM);
-  const int in_group = work % per_group;
-  const int mt = first_mt + in_group % gm;
-  const int nt = in_group / gm;
-  const int t0 = mt * kDT;
   const int HK = a.Hsel * kDnope;               // columns of the K part
 
-  // global -> LDS staging: thread loads rows lrow + 64 i (i < 4), vector lvec
-  const int lrow = tid >> 3, lvec = tid & 7;
-  const uint16_t* ap[4];
-  const uint16_t* bp[4];
+  // This workgroup's ranks: XCD x (= blockIdx % 8) owns a contiguous range of
+  // ranks, which its workgroups take round-robin.
+  const int total = a.n_mt * a.n_nt;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nslots = (G - xcd + 7) >> 3;        // workgroups on this XCD
+  const int chunk = (total + 7) >> 3;
+  const int rbeg = min(xcd * chunk, total), rend = min(rbeg + chunk, total);
+  const int my_tiles = rbeg + slot < rend ? (rend - rbeg - slot + nslots - 1) / nslots : 0;
+  const int nsteps = my_tiles * kDSteps;
+  if (nsteps == 0) return;
+
+  // DMA source of this lane for the tile being prefetched: per-lane 32-bit
+  // byte offsets (row kDRowsPerDma * i + lane / kDChunks of instruction
+  // i = 8 i2 + wave, chunk lane % kDChunks at its swizzled position), fixed
+  // for the tile; the k step only moves the uniform base.
+  uint32_t aof[kDDmaOp], bof[kDDmaOp];
+  auto set_dma_tile = [&](int j) __attribute__((always_inline)) {
+    int mt, nt;
+    dec_tile(rbeg + slot + j * nslots, a.n_mt, a.n_nt, mt, nt);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 64 * i;
-    ap[i] = a.lat + (int64_t)min(t0 + r, a.M - 1) * a.ld + lvec * 8;
-    const int n = nt * kDT + r;                 // output column -> packed weight row
-    const int64_t wrow = n < HK ? (int64_t)a.h_begin * kDnope + n
-                                : (int64_t)a.H_total * kDnope + (int64_t)a.h_begin * kDnope + (n - HK);
-    bp[i] = a.wt + wrow * kDc + lvec * 8;
+    for (int i2 = 0; i2 < kDDmaOp; ++i2) {
+      const int r = kDRowsPerDma * (i2 * 8 + wave) + lane / kDChunks;
+      const int gc = dec_swz(r, lane % kDChunks);
+      const int t = min(mt * kDT + r, a.M - 1);
+      aof[i2] = (uint32_t)t * (uint32_t)(a.ld * 2) + gc * 16;
+      const int n = nt * kDT + r;               // output column -> packed weight row
+      const int wrow = n < HK ? a.h_begin * kDnope + n : a.H_total * kDnope + a.h_begin * kDnope + (n - HK);
+      bof[i2] = (uint32_t)wrow * (kDc * 2) + gc * 16;
+    }
+  };
+  // (tile, k step) of the next DMA; past the last step it stays there, so the
+  // clamped copies re-read valid data
+  int dj = 0, dkk = 0;
+  set_dma_tile(0);
+  auto dma_next = [&](int stage) __attribute__((always_inline)) {
+    uint8_t* st = dlds + stage * kDStageB;
+    const uint8_t* sa = reinterpret_cast<const uint8_t*>(a.lat) + dkk * (kDBK * 2);
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.wt) + dkk * (kDBK * 2);
+#pragma unroll
+    for (int i2 = 0; i2 < kDDmaOp; ++i2) {
+      const int i = i2 * 8 + wave;
+      dma16s(sa, aof[i2], st + i * 1024);
+      dma16s(sb, bof[i2], st + kDOpB + i * 1024);
+    }
+    if (++dkk == kDSteps) {
+      if (dj + 1 < my_tiles) {
+        dkk = 0;
+        set_dma_tile(++dj);
+      } else {
+        dkk = kDSteps - 1;
+      }
+    }
+  };
+
+  // fragment read offsets (bytes in a stage) for the 16-wide k sub-steps
+  constexpr int kSub = kDBK / 16;
+  int aoff[kSub], boff[kSub];
+#pragma unroll
+  for (int s2 = 0; s2 < kSub; ++s2) {
+    const int pos = dec_swz(l32, 2 * s2 + g) * 16;
+    aoff[s2] = (wm * 64 + l32) * kDRow + pos;
+    boff[s2] = kDOpB + (wn * 128 + l32) * kDRow + pos;
   }
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + kt * kDBK);
-      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + kt * kDBK);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* As = lds + buf * kDStage;
-    uint16_t* Bs = As + kDT * kDLd;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(As + (lrow + 64 * i) * kDLd + lvec * 8) = ra[i];
-      *reinterpret_cast<u32x4*>(Bs + (lrow + 64 * i) * kDLd + lvec * 8) = rb[i];
-    }
-  };
 
   f32x16 acc[4][2];
+  auto zero = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
-
-  constexpr int nk = kDc / kDBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-#pragma unroll 1
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    gload(min(kt + 1, nk - 1));                 // the last prefetch re-reads step nk-1
-    // keep the prefetch ahead of the MFMA work: without this fence the
-    // scheduler sinks the loads to the LDS store and exposes their latency
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* As = lds + cur * kDStage + (wm * 64) * kDLd;
-    const uint16_t* Bs = lds + cur * kDStage + (kDT + wn * 128) * kDLd;
-#pragma unroll
-    for (int s = 0; s < kDBK / 16; ++s) {
-      bf16x8 af[2], bf[4];
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
-        af[tb] = *reinterpret_cast<const bf16x8*>(As + (tb * 32 + l32) * kDLd + s * 16 + g * 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
+  };
+
+  // Epilogue of the tile with flattened index j: 16 buffer stores per lane.
+  auto store_tile = [&](int j) __attribute__((always_inline)) {
+    int mt, nt;
+    dec_tile(rbeg + slot + j * nslots, a.n_mt, a.n_nt, mt, nt);
+    const int n0 = nt * kDT + wn * 128;         // first column of this wavefront
+    const bool is_v = n0 >= HK;
+    const int hs = (is_v ? n0 - HK : n0) / kDnope;
+    uint16_t* dst = is_v ? a.v + (int64_t)hs * a.vhs : a.k + (int64_t)hs * a.khs;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, a.M * (kDnope * 2), 0x00020000);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = mt * kDT + wm * 64 + tb * 32 + l32;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        bf[nb] = *reinterpret_cast<const bf16x8*>(Bs + (nb * 32 + l32) * kDLd + s * 16 + g * 8);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          // lane g holds columns 8q + 4g .. +3 of q = 2p, 2p+1; after the swap
+          // lane g = 0 holds all 8 columns of q = 2p+1, lane g = 1 those of q = 2p
+          uint32_t x0 = cvt_pk_bf16(acc[nb][tb][8 * p + 0], acc[nb][tb][8 * p + 1]);
+          uint32_t y0 = cvt_pk_bf16(acc[nb][tb][8 * p + 2], acc[nb][tb][8 * p + 3]);
+          uint32_t x1 = cvt_pk_bf16(acc[nb][tb][8 * p + 4], acc[nb][tb][8 * p + 5]);
+          uint32_t y1 = cvt_pk_bf16(acc[nb][tb][8 * p + 6], acc[nb][tb][8 * p + 7]);
+          const auto sx = __builtin_amdgcn_permlane32_swap(x1, x0, false, false);
+          const auto sy = __builtin_amdgcn_permlane32_swap(y1, y0, false, false);
+          const u32x4 val = {sx[0], sy[0], sx[1], sy[1]};
+          const int col = nb * 32 + 8 * (2 * p + 1 - g);
+          __builtin_amdgcn_raw_buffer_store_b128(val, rs, t * (kDnope * 2) + col * 2, 0, 0);
+        }
+    }
+  };
+
+  // Pipeline: step s waits for its own DMA, meets the other wavefronts at the
+  // barrier (then stage s % kDNS is complete and stage (s-1) % kDNS is no
+  // longer read), issues the DMA of step s+kDNS-1 into that stage and
+  // computes step s.
+  // Steps past the end are clamped to the last step: the copy goes into a
+  // stage no later step reads, and every step issues the same number of DMAs.
+#pragma unroll
+  for (int s = 0; s < kDNS - 1; ++s) dma_next(s);
+  zero();
+#pragma unroll 1
+  for (int s = 0; s < nsteps; ++s) {
+    const int kk = s & (kDSteps - 1);
+    if (s >= kDSteps && kk >= 1 && kk <= kDNS - 1) wait_vmcnt<(kDNS - 2) * kDDma + kDStores>();
+    else wait_vmcnt<(kDNS - 2) * kDDma>();
+    __syncthreads();
+    dma_next((s + kDNS - 1) & (kDNS - 1));
+    if (kk == 0 && s > 0) {
+      store_tile(s / kDSteps - 1);
+      zero();
+    }
+    const uint8_t* st = dlds + (s & (kDNS - 1)) * kDStageB;
+#pragma unroll
+    for (int s2 = 0; s2 < kSub; ++s2) {
+      bf16x8 af[2], bf[4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) af[tb] = *reinterpret_cast<const bf16x8*>(st + aoff[s2] + tb * 32 * kDRow);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) bf[nb] = *reinterpret_cast<const bf16x8*>(st + boff[s2] + nb * 32 * kDRow);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
           acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[nb], af[tb], acc[nb][tb], 0, 0, 0);
     }
-    lstore(cur ^ 1);
-    __syncthreads();
   }
-
-  // Epilogue through LDS: lane owns columns n = nb*32 + 8q + 4g + (0..3) of the
-  // wavefront's 128, for token wm*64 + tb*32 + l32; the wavefront writes its
-  // 64 x 128 bf16 block into its own LDS region, then streams it out 16 lanes
-  // per 256-byte token row.
-  const int n0 = nt * kDT + wn * 128;           // first column of this wavefront
-  const bool is_v = n0 >= HK;
-  const int hs = (is_v ? n0 - HK : n0) / kDnope;
-  uint16_t* dst = is_v ? a.v + (int64_t)hs * a.vhs : a.k + (int64_t)hs * a.khs;
-  constexpr int kCLd = 128 + 8;                 // 272-byte rows
-  uint16_t* Cs = lds + wave * (64 * kCLd);      // 8 x 17408 B fits the 147456 B stage area
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x2 w = {cvt_pk_bf16(acc[nb][tb][4 * q + 0], acc[nb][tb][4 * q + 1]),
-                         cvt_pk_bf16(acc[nb][tb][4 * q + 2], acc[nb][tb][4 * q + 3])};
-        *reinterpret_cast<u32x2*>(Cs + (tb * 32 + l32) * kCLd + nb * 32 + 8 * q + 4 * g) = w;
-      }
-  // a wavefront's LDS instructions complete in order, so its own reads below
-  // see these writes; other wavefronts never touch this region
-  __builtin_amdgcn_wave_barrier();
-  const int rsub = lane >> 4, vec = lane & 15;  // 4 rows per instruction, 16 lanes per row
-#pragma unroll 4
-  for (int r = 0; r < 64; r += 4) {
-    const int t = t0 + wm * 64 + r + rsub;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(Cs + (r + rsub) * kCLd + vec * 8);
-    if (t < a.M) *reinterpret_cast<u32x4*>(dst + (int64_t)t * kDnope + vec * 8) = val;
-  }
+  store_tile(my_tiles - 1);
+  // no DMA may still be writing LDS when the workgroup ends
+  wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------- weight pack (transpose)
@@ -389,6 +473,12 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
               MLA_ERR_INVALID_ARG, "mla_decompress: pointers must be 16-byte aligned");
   MLA_REQUIRE(ld_latent >= kDc && ld_latent % 8 == 0, MLA_ERR_INVALID_ARG,
               "mla_decompress: ld_latent (%lld) must be >= 512 and a multiple of 8", (long long)ld_latent);
+  // the kernel addresses the latent and the packed weight with 32-bit byte
+  // offsets and each head's output with a 31-bit buffer range
+  MLA_REQUIRE((int64_t)n_tokens * ld_latent * 2 < ((int64_t)1 << 32) && (int64_t)n_tokens * kDnope * 2 < ((int64_t)1 << 31),
+              MLA_ERR_UNSUPPORTED, "mla_decompress: n_tokens (%d) too large for one call; split the tokens", n_tokens);
+  MLA_REQUIRE((int64_t)H_total * 2 * kDnope * kDc * 2 < ((int64_t)1 << 32), MLA_ERR_UNSUPPORTED,
+              "mla_decompress: H_total (%d) too large", H_total);
   const int Hsel = h_end - h_begin;
   MLA_REQUIRE(k_head_stride >= (int64_t)n_tokens * kDnope && v_head_stride >= (int64_t)n_tokens * kDv &&
                   k_head_stride % 8 == 0 && v_head_stride % 8 == 0,
@@ -399,13 +489,17 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
             (n_tokens + kDT - 1) / kDT, Hsel * 2 * kDnope / kDT};
   const int64_t total = (int64_t)d.n_mt * d.n_nt;
   MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_decompress: problem too large");
-  const size_t lds = (size_t)2 * kDStage * sizeof(uint16_t);
+  const size_t lds = (size_t)kDNS * kDStageB;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decompress_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
     mla_set_error("mla_decompress: cannot reserve %zu bytes of LDS", lds);
     return MLA_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(decompress_kernel, dim3((unsigned)total), dim3(kDThreads), lds,
+  // persistent grid: one workgroup per compute unit, none without a tile
+  const int ncu = mla_num_cus();
+  MLA_REQUIRE(ncu > 0, MLA_ERR_LAUNCH, "mla_decompress: cannot query the compute-unit count");
+  const unsigned grid = (unsigned)std::min<int64_t>(total, ncu);
+  hipLaunchKernelGGL(decompress_kernel, dim3(grid), dim3(kDThreads), lds,
                      reinterpret_cast<hipStream_t>(stream), d);
   return mla_check_launch("mla_decompress");
 }

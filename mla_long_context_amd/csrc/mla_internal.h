@@ -25,10 +25,43 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------- global -> LDS DMA
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte chunk per lane from global memory into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; the LDS base goes through M0). Issued as inline
+// assembly so that the compiler's counter bookkeeping ignores it: completion
+// is awaited explicitly with wait_vmcnt before the barrier that publishes a
+// tile, and before the workgroup ends.
+__device__ __forceinline__ void dma16(const void* src, const void* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)lds;
+  // M0 is a reserved register that compiled code of this file does not use
+  // otherwise, so setting it here disturbs nothing
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(l) : "memory");
+}
+
+// As dma16, with the source split into a wavefront-uniform base (SGPRs) and a
+// per-lane 32-bit byte offset: the address arithmetic of a step is then one
+// scalar add, and the per-lane offsets are computed once per tile.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(l)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------- host error state
 void mla_set_error(const char* fmt, ...);
 void mla_clear_error();
 int mla_check_launch(const char* what);
+// compute units of the current device (0 if the runtime cannot tell)
+int mla_num_cus();
 
 #define MLA_REQUIRE(cond, code, ...)            \
   do {                                          \

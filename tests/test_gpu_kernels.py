@@ -131,7 +131,11 @@ def test_rope_relocate(delta, pairing):
 
 # ---------------------------------------------------------------- decompression
 
-@pytest.mark.parametrize("H,h0,h1,n", [(8, 0, 8, 300), (4, 1, 3, 129), (2, 0, 2, 1)])
+# The last two cases give every workgroup of the persistent grid several
+# tiles (363 and 528 tiles of 256 x 256), the first of them with an odd head
+# count, so one tile straddles the W_UK / W_UV boundary.
+@pytest.mark.parametrize("H,h0,h1,n", [(8, 0, 8, 300), (4, 1, 3, 129), (2, 0, 2, 1),
+                                       (16, 3, 14, 8300), (16, 0, 16, 8250)])
 def test_decompress(H, h0, h1, n):
     require_gpu()
     say(f"decompress H={H} heads [{h0},{h1}) n={n}")
