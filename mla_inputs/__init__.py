@@ -243,7 +243,7 @@ CONFIG_NAMES = {
     2: "dsv3: 128 heads, 4 requests x (8192 ctx + 1024 new), chunk 4096, bf16",
     3: "long: 128 heads, 1 request x (131072 ctx + 2048 new), chunk 8192, bf16",
     4: "fp8-ragged: 128 heads, 16 requests, ctx U[1024,32768]/64*64, new U[256,2048], chunk 4096",
-    5: "reuse: 64 heads (56 Local / 8 Global), 262144-token document, 512 query rows at +4096",
+    5: "reuse: 64 heads (56 Local / 8 Global), 262144-token document, 512 query rows at +4096, chunk 65536",
 }
 
 
@@ -261,5 +261,7 @@ def make_config(k: int) -> Problem:
         c, e = ragged_lengths(rng)
         return _finish(rng, "fp8-ragged", 128, c, e, 4096, "fp8", 4)
     if k == 5:
-        return make_reuse_problem(seed=5, name="reuse")
+        # chunk 65536 (the pages fix none for this workload): 4 chunks of
+        # 2 GB of decompressed k/v each, large enough to fill the GPU
+        return make_reuse_problem(chunk=65536, seed=5, name="reuse")
     raise ValueError(k)

@@ -21,6 +21,15 @@
 
 namespace {
 
+// max of a value over lanes l and l ^ 32: v_permlane32_swap exchanges the
+// two halves of the wavefront in registers (one lane of each pair ends up
+// with its own value in one result and its partner's in the other)
+__device__ __forceinline__ float xor32_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 constexpr int kTileK = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -87,11 +96,18 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  const uint32_t total = (uint32_t)a.batch * a.Hsel * a.n_qt;
-  const uint32_t w = xcd_remap(blockIdx.x, total);
-  int qt = (int)(w % (uint32_t)a.n_qt);
-  const int hs = (int)((w / (uint32_t)a.n_qt) % (uint32_t)a.Hsel);
-  const int b = (int)(w / ((uint32_t)a.n_qt * a.Hsel));
+  // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8).
+  // (request, head) pairs are dealt to the XCDs round-robin too, with all
+  // query tiles of one pair on the same XCD, where they share the pair's K
+  // and V in L2. Dealing pairs (not contiguous ranges of them) keeps the XCDs
+  // evenly loaded when request lengths differ.
+  const int n_bh = a.batch * a.Hsel;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int bh = (j / a.n_qt) * 8 + xcd;
+  if (bh >= n_bh) return;
+  int qt = j % a.n_qt;
+  const int hs = bh % a.Hsel;
+  const int b = bh / a.Hsel;
   if (kCausal) qt = a.n_qt - 1 - qt;   // longest rows first
 
   const int q0 = a.cu_q[b];
@@ -212,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, S[0][i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[1][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = xor32_max(mt);
     // Lazy reference max (log2 units): it only moves when the tile max
     // exceeds it by more than kLazy, so p <= 2^kLazy and the rescale of O is
     // skipped on almost every tile. The normalisation uses the same
@@ -386,7 +402,9 @@ extern "C" int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, in
   else if (max_q <= 128 || causal) NW = 4;
   const int rows = 32 * NW;
   const int n_qt = (max_q + rows - 1) / rows;
-  const int64_t total = (int64_t)batch * Hsel * n_qt;
+  // (request, head) pairs rounded up to a multiple of the 8 XCDs (the
+  // surplus workgroups exit at once)
+  const int64_t total = ((int64_t)batch * Hsel + 7) / 8 * 8 * n_qt;
   MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_prefill_attn: problem too large");
   AttnArgs a{static_cast<const uint16_t*>(q), q_row_stride, h_begin, Hsel,
              static_cast<const uint16_t*>(k_nope), k_head_stride,

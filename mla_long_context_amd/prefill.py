@@ -187,15 +187,26 @@ class ChunkedPrefill:
 
 
 class ReusePrefill:
-    """Head-partitioned reuse over one document at canonical positions."""
+    """Head-partitioned reuse over one document at canonical positions.
 
-    def __init__(self, prob, device="cuda", chunk=None):
+    Per document chunk: gather, decompression of every head, then attention
+    of the Global heads (all query rows) and of the Local heads (protected
+    rows only). There are few query rows, so one (head, row tile) per
+    workgroup would leave most of the GPU idle: every chunk's keys are split
+    into `split`-key pieces, each passed to mla_prefill_attn as a request of
+    its own (the query rows repeated through q_row_ids), and the partial
+    (out, lse) states of all pieces of the document are merged at the end by
+    a log-depth tree of mla_merge_states calls. By the merge identity this
+    equals the chunk-by-chunk merge."""
+
+    def __init__(self, prob, device="cuda", chunk=None, split=2048):
         assert prob.is_reuse
         self.prob = prob
         self.device = device
         H = self.H = prob.H
         self.HL, self.HG = prob.n_local, H - prob.n_local
         self.S = int(chunk or prob.chunk)
+        self.split = max(64, int(split) // 64 * 64)
         self.Ldoc = int(prob.ctx_len[0])
         self.T = prob.T
         self.P = int(len(prob.prot_rows))
@@ -210,84 +221,125 @@ class ReusePrefill:
         self.prot = _i32(prob.prot_rows, device)
         self.wa_t = pack_weight(np.concatenate([prob.WaL, prob.WaG], axis=0), device)
         self.wb_t = pack_weight(prob.Wb, device)
+        T, P = self.T, self.P
+        prot = np.asarray(prob.prot_rows, dtype=np.int64)
+        # chunk plan; piece i of the document is split (chunk c, piece j)
         self.chunks = []
+        n_pieces = 0
         for s0 in range(0, self.Ldoc, self.S):
             n = min(self.S, self.Ldoc - s0)
-            self.chunks.append(dict(start=_i32([s0], device), len=_i32([n], device),
-                                    cu=_i32([0, n], device), n=n))
+            bounds = list(range(0, n, self.split)) + [n]
+            k = len(bounds) - 1
+            self.chunks.append(dict(
+                start=_i32([s0], device), len=_i32([n], device), cu=_i32([0, n], device), n=n,
+                pieces=k, first=n_pieces, cu_k=_i32(bounds, device),
+                cu_qG=_i32(np.arange(k + 1) * T, device), rid_G=_i32(np.tile(np.arange(T), k), device),
+                cu_qL=_i32(np.arange(k + 1) * P, device), rid_L=_i32(np.tile(prot, k), device)))
+            n_pieces += k
+        self.n_pieces = n_pieces
         S = self.S
         self.lat_ws = torch.empty((S, D_LAT), dtype=torch.bfloat16, device=device)
         self.k_ws = torch.empty((H, S, D_V), dtype=torch.bfloat16, device=device)
         self.v_ws = torch.empty((H, S, D_V), dtype=torch.bfloat16, device=device)
         self.hstride = S * D_V
-        T, P, HL, HG = self.T, max(self.P, 1), self.HL, self.HG
+        HL, HG = self.HL, self.HG
         f32, bf = torch.float32, torch.bfloat16
-        self.cu_T = _i32([0, T], device)
-        self.cu_P = _i32([0, self.P], device)
-        self.acc_G = torch.empty((T, HG, D_V), dtype=f32, device=device)
-        self.accl_G = torch.empty((T, HG), dtype=f32, device=device)
-        self.tmp_G = torch.empty((T, HG, D_V), dtype=bf, device=device)
-        self.tmpl_G = torch.empty((T, HG), dtype=f32, device=device)
+        # partial states of every piece, fp32: [pieces * rows, heads, 128]
+        self.part_G = torch.empty((max(n_pieces * T, 1), max(HG, 1), D_V), dtype=f32, device=device)
+        self.partl_G = torch.empty((max(n_pieces * T, 1), max(HG, 1)), dtype=f32, device=device)
+        self.part_L = torch.empty((max(n_pieces * P, 1), max(HL, 1), D_V), dtype=f32, device=device)
+        self.partl_L = torch.empty((max(n_pieces * P, 1), max(HL, 1)), dtype=f32, device=device)
         self.glob_out = torch.empty((T, HG, D_V), dtype=bf, device=device)
         self.lse_G = torch.empty((T, HG), dtype=f32, device=device)
-        self.acc_L = torch.empty((P, HL, D_V), dtype=f32, device=device)
-        self.accl_L = torch.empty((P, HL), dtype=f32, device=device)
-        self.tmp_L = torch.empty((P, HL, D_V), dtype=bf, device=device)
-        self.tmpl_L = torch.empty((P, HL), dtype=f32, device=device)
-        self.rec_out = torch.empty((P, HL, D_V), dtype=bf, device=device)
-        self.lse_L = torch.empty((P, HL), dtype=f32, device=device)
+        self.rec_out = torch.empty((max(P, 1), HL, D_V), dtype=bf, device=device)
+        self.lse_L = torch.empty((max(P, 1), HL), dtype=f32, device=device)
         self.z = torch.empty((T, self.d_mid), dtype=bf, device=device)
         self.y = torch.empty((T, self.d_model), dtype=bf, device=device)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
 
-    def _attn(self, h0, h1, cu_q, row_ids, n_rows, cu_k, out, out_dtype, lse, stream):
+    def _attn_pieces(self, ch, h0, h1, n_rows, cu_q, rid, part, partl, fin, finl, stream):
+        """Attention of heads [h0, h1) for the query rows rid over every piece
+        of chunk ch: piece j's state goes to rows (first + j) * n_rows of the
+        fp32 partial buffers, or straight to the bf16 result when the whole
+        document is one piece."""
         Hs = h1 - h0
+        if self.n_pieces == 1:
+            out, odt, lse = fin, L.DTYPE_BF16, finl
+        else:
+            row0 = ch["first"] * n_rows
+            out, odt, lse = part[row0:], L.DTYPE_FP32, partl[row0:]
         L.mla_prefill_attn(self.q_rel, self.H * D_QK, self.H, h0, h1, self.k_ws[h0], self.hstride,
-                           self.v_ws[h0], self.hstride, self.lat_ws, D_LAT, cu_q, cu_k, row_ids, 1,
-                           n_rows, self.prob.scale, 0, out, out_dtype, Hs * D_V, lse, Hs, stream)
+                           self.v_ws[h0], self.hstride, self.lat_ws, D_LAT, cu_q, ch["cu_k"], rid,
+                           ch["pieces"], n_rows, self.prob.scale, 0, out, odt, Hs * D_V, lse, Hs, stream)
 
-    def run(self, stream=None):
+    def _merge_tree(self, part, partl, n_rows, fin, finl, stream):
+        """Merge the partial states of all pieces into (fin, finl). Each level
+        merges the first half of the remaining pieces with the last half in
+        place (fp32; an odd middle piece waits for the next level); the last
+        level writes the bf16 result."""
+        n = self.n_pieces
+        heads = part.shape[1]
+        while n > 1:
+            h = n // 2
+            m = n - h
+            a, al = part[:h * n_rows], partl[:h * n_rows]
+            b, bl = part[m * n_rows:], partl[m * n_rows:]
+            if n == 2:
+                out, odt, lo = fin, L.DTYPE_BF16, finl
+            else:
+                out, odt, lo = a, L.DTYPE_FP32, al
+            L.mla_merge_states(a, L.DTYPE_FP32, al, b, L.DTYPE_FP32, bl, h * n_rows * heads, out, odt,
+                               lo, stream)
+            n = m
+
+    def run(self, stream=None, timer=None):
         p = self.prob
         H, HL, HG, T, P = self.H, self.HL, self.HG, self.T, self.P
-        L.mla_rope_relocate_q(self.q, self.q_rel, H * D_QK, T, H, p.delta, p.rope_base,
-                              L.ROPE_INTERLEAVED, stream)
-        last = len(self.chunks) - 1
-        for ci, ch in enumerate(self.chunks):
-            L.mla_gather_context(self.pool, L.DTYPE_BF16, p.num_blocks, self.bt, self.bt.shape[1],
-                                 ch["start"], ch["len"], ch["cu"], 1, ch["n"], self.lat_ws,
-                                 self.dev_status, stream)
-            L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, H, 0, H, self.k_ws, self.hstride,
-                             self.v_ws, self.hstride, stream)
-            for (h0, h1, cu_q, rid, nr, acc, accl, tmp, tmpl, fin, finl) in (
-                    (HL, H, self.cu_T, None, T, self.acc_G, self.accl_G, self.tmp_G, self.tmpl_G,
-                     self.glob_out, self.lse_G),
-                    (0, HL, self.cu_P, self.prot, P, self.acc_L, self.accl_L, self.tmp_L, self.tmpl_L,
-                     self.rec_out, self.lse_L)):
-                if h1 <= h0 or nr == 0:
-                    continue
-                rows = nr * (h1 - h0)
-                if ci == 0 and last == 0:
-                    self._attn(h0, h1, cu_q, rid, nr, ch["cu"], fin, L.DTYPE_BF16, finl, stream)
-                elif ci == 0:
-                    self._attn(h0, h1, cu_q, rid, nr, ch["cu"], acc, L.DTYPE_FP32, accl, stream)
-                else:
-                    self._attn(h0, h1, cu_q, rid, nr, ch["cu"], tmp, L.DTYPE_BF16, tmpl, stream)
-                    if ci < last:
-                        L.mla_merge_states(acc, L.DTYPE_FP32, accl, tmp, L.DTYPE_BF16, tmpl, rows,
-                                           acc, L.DTYPE_FP32, accl, stream)
-                    else:
-                        L.mla_merge_states(acc, L.DTYPE_FP32, accl, tmp, L.DTYPE_BF16, tmpl, rows,
-                                           fin, L.DTYPE_BF16, finl, stream)
-        L.mla_head_partition_merge(self.art, self.rec_out, self.prot, P, self.glob_out, self.wa_t,
-                                   self.wb_t, T, HL, HG, self.d_mid, self.d_model, self.z, self.y,
-                                   stream)
+        with _span(timer, "relocate"):
+            L.mla_rope_relocate_q(self.q, self.q_rel, H * D_QK, T, H, p.delta, p.rope_base,
+                                  L.ROPE_INTERLEAVED, stream)
+        for ch in self.chunks:
+            with _span(timer, "gather"):
+                L.mla_gather_context(self.pool, L.DTYPE_BF16, p.num_blocks, self.bt, self.bt.shape[1],
+                                     ch["start"], ch["len"], ch["cu"], 1, ch["n"], self.lat_ws,
+                                     self.dev_status, stream)
+            with _span(timer, "decompress"):
+                L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, H, 0, H, self.k_ws, self.hstride,
+                                 self.v_ws, self.hstride, stream)
+            if HG > 0 and T > 0:
+                with _span(timer, "attn_global"):
+                    self._attn_pieces(ch, HL, H, T, ch["cu_qG"], ch["rid_G"], self.part_G, self.partl_G,
+                                      self.glob_out, self.lse_G, stream)
+            if HL > 0 and P > 0:
+                with _span(timer, "attn_local"):
+                    self._attn_pieces(ch, 0, HL, P, ch["cu_qL"], ch["rid_L"], self.part_L, self.partl_L,
+                                      self.rec_out, self.lse_L, stream)
+        with _span(timer, "merge"):
+            if HG > 0 and T > 0:
+                self._merge_tree(self.part_G, self.partl_G, T, self.glob_out, self.lse_G, stream)
+            if HL > 0 and P > 0:
+                self._merge_tree(self.part_L, self.partl_L, P, self.rec_out, self.lse_L, stream)
+        with _span(timer, "projection"):
+            L.mla_head_partition_merge(self.art, self.rec_out, self.prot, P, self.glob_out, self.wa_t,
+                                       self.wb_t, T, HL, HG, self.d_mid, self.d_model, self.z, self.y,
+                                       stream)
         return self.y
 
     def work(self) -> dict:
+        """Algorithmic work of one run, in the same units as ChunkedPrefill.work
+        (merge bytes per (row, head): fp32 accumulator read + write, bf16 chunk
+        state read; the last merge writes bf16)."""
         H, HL, HG, T, P, Ld = self.H, self.HL, self.HG, self.T, self.P, self.Ldoc
+        n = len(self.chunks)
+        rows = T * HG + P * HL
+        merge_bytes = rows * ((n - 2) * (516 + 260 + 516) + (516 + 260 + 260)) if n > 1 else 0
         return dict(
             dec_flops=2 * 512 * 256 * H * Ld,
-            attn_flops=640 * Ld * (T * HG + P * HL),
+            attn_flops=640 * Ld * rows,
+            global_attn_flops=640 * Ld * T * HG,
+            local_attn_flops=640 * Ld * P * HL,
             proj_flops=2 * T * ((HL + HG) * 128 * self.d_mid + self.d_mid * self.d_model),
+            relocate_bytes=T * H * 768,   # out of place: q head row read (384 B) + written
+            merge_bytes=int(merge_bytes),
             gather_tokens=Ld, gather_bytes=Ld * 2304, new_tokens=T, ctx_tokens=Ld,
         )

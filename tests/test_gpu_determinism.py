@@ -42,7 +42,7 @@ def test_reuse_prefill_bitwise_repeatable_with_poisoned_workspaces():
                                  d_mid=256, d_model=256, chunk=256, seed=82)
     pre = ReusePrefill(prob)
     y1 = bits(pre.run()).copy()
-    _poison(pre.q_rel, pre.lat_ws, pre.k_ws, pre.v_ws, pre.acc_G, pre.acc_L, pre.tmp_G, pre.tmp_L,
+    _poison(pre.q_rel, pre.lat_ws, pre.k_ws, pre.v_ws, pre.part_G, pre.partl_G, pre.part_L, pre.partl_L,
             pre.glob_out, pre.rec_out, pre.z, pre.y)
     y2 = bits(pre.run())
     torch.cuda.synchronize()

@@ -87,12 +87,16 @@ def test_ragged_multichunk_fp8():
     _compare_chunked(prob, pre, rl2=FP8_REL_L2)
 
 
-def test_reuse_small_all_outputs():
+# key splits: one piece per chunk (5 pieces, odd merge tree), four pieces per
+# chunk with a ragged last one, and the whole document as a single piece
+@pytest.mark.parametrize("split,chunk", [(2048, 256), (64, 256), (4096, 2048)])
+def test_reuse_small_all_outputs(split, chunk):
     require_gpu()
-    say("reuse small")
+    say(f"reuse small split={split} chunk={chunk}")
     prob = mi.make_reuse_problem(H=8, n_local=7, L=1024 + 64, T=300, delta=4096, P=9,
-                                 d_mid=256, d_model=384, chunk=256, seed=73)
-    pre = ReusePrefill(prob)
+                                 d_mid=256, d_model=384, chunk=chunk, seed=73)
+    pre = ReusePrefill(prob, split=split)
+    say(f"  {pre.n_pieces} pieces")
     y = pre.run()
     torch.cuda.synchronize()
     ref = orc.reuse_reference(prob)
