@@ -166,6 +166,34 @@ int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, int h_begin, 
                      float* lse, int64_t lse_row_stride, void* stream);
 
 /*
+ * mla_prefill_attn_merge -- mla_prefill_attn followed by the log-sum-exp
+ * merge of [DSMLA] 4.3 with a previous state, in one pass: the chunk loop of
+ * [DSMLA] 4.4 merges every chunk's (out, lse) into the running state, and
+ * here that merge happens in the attention epilogue, in fp32, before the
+ * result is rounded.
+ *
+ * Arguments as mla_prefill_attn, plus the previous state of the same rows
+ * and heads (fp32, 16-byte aligned):
+ *   prev_out[(cu_q[b]+i) * prev_row_stride + hs * 128 + d]
+ *   prev_lse[(cu_q[b]+i) * prev_lse_row_stride + hs]
+ * The result (out, lse) is merge(prev, this pass) as in mla_merge_states: a
+ * side with lse = -inf contributes nothing (its out is not read), both -inf
+ * give out = 0 and lse = -inf. out and lse may be the previous state itself
+ * (same pointers and strides, out_dtype = MLA_DTYPE_FP32): each element is
+ * read before it is written. Any other overlap is undefined.
+ */
+int mla_prefill_attn_merge(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                           const void* k_nope, int64_t k_head_stride,
+                           const void* v, int64_t v_head_stride,
+                           const void* latent, int64_t ld_latent,
+                           const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_row_ids,
+                           int batch, int max_q, float scale, int causal,
+                           const float* prev_out, int64_t prev_row_stride,
+                           const float* prev_lse, int64_t prev_lse_row_stride,
+                           void* out, int out_dtype, int64_t out_row_stride,
+                           float* lse, int64_t lse_row_stride, void* stream);
+
+/*
  * mla_merge_states -- [DSMLA] 4.3 (merge_attn_states), with the merged lse
  * m + ln(e^{la-m} + e^{lb-m}) that the chunk loop of 4.4 consumes.
  *

@@ -27,7 +27,8 @@ ROPE_HALF = 1
 
 EXPORTS = (
     "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_pack_weight_t",
-    "mla_decompress", "mla_prefill_attn", "mla_merge_states", "mla_rope_relocate_q",
+    "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_merge_states",
+    "mla_rope_relocate_q",
     "mla_head_partition_merge",
 )
 
@@ -52,6 +53,8 @@ _SIGS = {
     "mla_decompress": [P, I64, I32, P, I32, I32, I32, P, I64, P, I64, P],
     "mla_prefill_attn": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
                          I32, I32, F32, I32, P, I32, I64, P, I64, P],
+    "mla_prefill_attn_merge": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
+                               I32, I32, F32, I32, P, I64, P, I64, P, I32, I64, P, I64, P],
     "mla_merge_states": [P, I32, P, P, I32, P, I64, P, I32, P, P],
     "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
     "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
@@ -126,6 +129,17 @@ def mla_prefill_attn(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride
                  k_head_stride, _ptr(v), v_head_stride, _ptr(latent), ld_latent, _ptr(cu_q),
                  _ptr(cu_k), _ptr(q_row_ids), batch, max_q, float(scale), int(causal), _ptr(out),
                  out_dtype, out_row_stride, _ptr(lse), lse_row_stride, _stream(stream))
+
+
+def mla_prefill_attn_merge(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,
+                           v_head_stride, latent, ld_latent, cu_q, cu_k, q_row_ids, batch, max_q,
+                           scale, causal, prev_out, prev_row_stride, prev_lse, prev_lse_row_stride,
+                           out, out_dtype, out_row_stride, lse, lse_row_stride, stream=None):
+    return _call("mla_prefill_attn_merge", _ptr(q), q_row_stride, H_q, h_begin, h_end, _ptr(k_nope),
+                 k_head_stride, _ptr(v), v_head_stride, _ptr(latent), ld_latent, _ptr(cu_q),
+                 _ptr(cu_k), _ptr(q_row_ids), batch, max_q, float(scale), int(causal), _ptr(prev_out),
+                 prev_row_stride, _ptr(prev_lse), prev_lse_row_stride, _ptr(out), out_dtype,
+                 out_row_stride, _ptr(lse), lse_row_stride, _stream(stream))
 
 
 def mla_merge_states(out_a, dtype_a, lse_a, out_b, dtype_b, lse_b, rows, out, dtype_out, lse_out,

@@ -43,6 +43,7 @@ struct AttnArgs {
   const int32_t* cu_q; const int32_t* cu_k; const int32_t* row_ids;
   int batch; int n_qt; float scale_log2;
   void* out; int64_t out_rs; float* lse; int64_t lse_rs;
+  const float* prev; int64_t prev_rs; const float* prev_lse; int64_t prev_lse_rs;   // merge mode only
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -76,7 +77,7 @@ __device__ __forceinline__ uint8_t* lds_stage2() {
   }
 }
 
-template <int NW, bool kCausal, bool kRowIds, int kOutDt>
+template <int NW, bool kCausal, bool kRowIds, int kOutDt, bool kMerge>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
   constexpr int NB = (NW == 8) ? 3 : 2;    // LDS stages (tiles in flight)
@@ -210,6 +211,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
       }
     }
+    // keep the K fragment reads six ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     // masking only on tiles that cross the key end or the causal diagonal
     const bool edge = (kt0 + kTileK > n_k) || (kCausal && kt0 + kTileK - 1 > wave_first_lim);
     if (edge) {
@@ -277,6 +286,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[d], 0, 0, 0);
       }
     }
+    // V reads one 16-key step (8 reads) ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   };
 
   // Pipeline over key tiles with NB LDS stages: step t waits for its own DMA
@@ -320,15 +337,42 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
   const int64_t orow = (int64_t)(q0 + row);
+  // this state: out = O / l_tot, lse (log2 units) = m_ref + log2 l_tot
+  float lse2 = empty ? -INFINITY : m_ref + __builtin_amdgcn_logf(l_tot);
+  float c_this = empty ? 0.f : 1.f / l_tot;   // factor on O
+  float c_prev = 0.f;                         // factor on the previous out
+  const float* pp = nullptr;
+  if (kMerge) {
+    // Log-sum-exp merge with the previous state of this (row, head), as
+    // merge_attn_states does, in log2 units: m = max of the two lse, each
+    // side weighted by 2^(lse - m); a side at -inf contributes nothing.
+    pp = a.prev + orow * a.prev_rs + (int64_t)hs * kDv;
+    const float lp2 = a.prev_lse[orow * a.prev_lse_rs + hs] * kLog2e;
+    const float m2 = fmaxf(lse2, lp2);
+    if (m2 == -INFINITY) {
+      c_this = 0.f;
+    } else {
+      const float wp = (lp2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lp2 - m2);
+      const float wt = (lse2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lse2 - m2);
+      const float inv_s = 1.f / (wp + wt);
+      c_prev = wp * inv_s;
+      c_this *= wt * inv_s;
+      lse2 = m2 + __builtin_amdgcn_logf(wp + wt);
+    }
+  }
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int dv = d * 32 + 8 * qq + 4 * g;
-      const float o0 = O[d][4 * qq + 0] * inv, o1 = O[d][4 * qq + 1] * inv;
-      const float o2 = O[d][4 * qq + 2] * inv, o3 = O[d][4 * qq + 3] * inv;
+      float o0 = O[d][4 * qq + 0] * c_this, o1 = O[d][4 * qq + 1] * c_this;
+      float o2 = O[d][4 * qq + 2] * c_this, o3 = O[d][4 * qq + 3] * c_this;
+      if (kMerge && c_prev != 0.f) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(pp + dv);
+        o0 = fmaf(c_prev, pv.x, o0); o1 = fmaf(c_prev, pv.y, o1);
+        o2 = fmaf(c_prev, pv.z, o2); o3 = fmaf(c_prev, pv.w, o3);
+      }
       if (kOutDt == MLA_DTYPE_FP32) {
         float* op = static_cast<float*>(a.out) + orow * a.out_rs + (int64_t)hs * kDv + dv;
         *reinterpret_cast<f32x4*>(op) = f32x4{o0, o1, o2, o3};
@@ -337,60 +381,69 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<u32x2*>(op) = u32x2{cvt_pk_bf16(o0, o1), cvt_pk_bf16(o2, o3)};
       }
     }
-  if (g == 0)
-    a.lse[orow * a.lse_rs + hs] = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (g == 0) a.lse[orow * a.lse_rs + hs] = lse2 * kLn2;
 }
 
-template <int NW, bool kCausal, bool kRowIds>
-void launch3(int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
+template <int NW, bool kCausal, bool kRowIds, bool kMerge>
+void launch4(int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
   if (out_dt == MLA_DTYPE_FP32)
-    hipLaunchKernelGGL((attn_kernel<NW, kCausal, kRowIds, MLA_DTYPE_FP32>), g, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<NW, kCausal, kRowIds, MLA_DTYPE_FP32, kMerge>), g, dim3(NW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<NW, kCausal, kRowIds, MLA_DTYPE_BF16>), g, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((attn_kernel<NW, kCausal, kRowIds, MLA_DTYPE_BF16, kMerge>), g, dim3(NW * 64), 0, s, a);
+}
+template <int NW, bool kCausal, bool kRowIds>
+void launch3(bool merge, int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
+  if (merge) launch4<NW, kCausal, kRowIds, true>(out_dt, g, s, a);
+  else launch4<NW, kCausal, kRowIds, false>(out_dt, g, s, a);
 }
 template <int NW, bool kCausal>
-void launch2(bool rowids, int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
-  if (rowids) launch3<NW, kCausal, true>(out_dt, g, s, a);
-  else launch3<NW, kCausal, false>(out_dt, g, s, a);
+void launch2(bool rowids, bool merge, int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
+  if (rowids) launch3<NW, kCausal, true>(merge, out_dt, g, s, a);
+  else launch3<NW, kCausal, false>(merge, out_dt, g, s, a);
 }
 template <int NW>
-void launch1(bool causal, bool rowids, int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
-  if (causal) launch2<NW, true>(rowids, out_dt, g, s, a);
-  else launch2<NW, false>(rowids, out_dt, g, s, a);
+void launch1(bool causal, bool rowids, bool merge, int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
+  if (causal) launch2<NW, true>(rowids, merge, out_dt, g, s, a);
+  else launch2<NW, false>(rowids, merge, out_dt, g, s, a);
 }
 
-}  // namespace
-
-extern "C" int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
-                                const void* k_nope, int64_t k_head_stride,
-                                const void* v, int64_t v_head_stride,
-                                const void* latent, int64_t ld_latent,
-                                const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_row_ids,
-                                int batch, int max_q, float scale, int causal,
-                                void* out, int out_dtype, int64_t out_row_stride,
-                                float* lse, int64_t lse_row_stride, void* stream) {
+// validation and launch shared by mla_prefill_attn and mla_prefill_attn_merge
+int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                 const void* k_nope, int64_t k_head_stride, const void* v, int64_t v_head_stride,
+                 const void* latent, int64_t ld_latent, const int32_t* cu_q, const int32_t* cu_k,
+                 const int32_t* q_row_ids, int batch, int max_q, float scale, int causal, void* out,
+                 int out_dtype, int64_t out_row_stride, float* lse, int64_t lse_row_stride,
+                 const float* prev, int64_t prev_row_stride, const float* prev_lse, int64_t prev_lse_row_stride,
+                 bool merge, void* stream) {
   mla_clear_error();
-  MLA_REQUIRE(batch >= 0 && max_q >= 0, MLA_ERR_INVALID_ARG, "mla_prefill_attn: batch and max_q must be >= 0");
+  MLA_REQUIRE(batch >= 0 && max_q >= 0, MLA_ERR_INVALID_ARG, "%s: batch and max_q must be >= 0", fn);
   MLA_REQUIRE(H_q > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_q, MLA_ERR_INVALID_ARG,
-              "mla_prefill_attn: need 0 <= h_begin (%d) < h_end (%d) <= H_q (%d)", h_begin, h_end, H_q);
+              "%s: need 0 <= h_begin (%d) < h_end (%d) <= H_q (%d)", fn, h_begin, h_end, H_q);
   if (batch == 0 || max_q == 0) return MLA_OK;
   MLA_REQUIRE(q && k_nope && v && latent && cu_q && cu_k && out && lse, MLA_ERR_INVALID_ARG,
-              "mla_prefill_attn: null pointer argument");
+              "%s: null pointer argument", fn);
   MLA_REQUIRE(out_dtype == MLA_DTYPE_BF16 || out_dtype == MLA_DTYPE_FP32, MLA_ERR_UNSUPPORTED,
-              "mla_prefill_attn: out dtype %d not supported", out_dtype);
+              "%s: out dtype %d not supported", fn, out_dtype);
   MLA_REQUIRE(mla_aligned16(q) && mla_aligned16(k_nope) && mla_aligned16(v) && mla_aligned16(latent) &&
                   mla_aligned16(out),
-              MLA_ERR_INVALID_ARG, "mla_prefill_attn: tensor pointers must be 16-byte aligned");
+              MLA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   MLA_REQUIRE(q_row_stride % 8 == 0 && q_row_stride >= (int64_t)H_q * kDqk, MLA_ERR_INVALID_ARG,
-              "mla_prefill_attn: q_row_stride (%lld) must be a multiple of 8 and >= H_q*192", (long long)q_row_stride);
+              "%s: q_row_stride (%lld) must be a multiple of 8 and >= H_q*192", fn, (long long)q_row_stride);
   MLA_REQUIRE(ld_latent % 8 == 0 && ld_latent >= kDlat, MLA_ERR_INVALID_ARG,
-              "mla_prefill_attn: ld_latent (%lld) must be a multiple of 8 and >= 576", (long long)ld_latent);
+              "%s: ld_latent (%lld) must be a multiple of 8 and >= 576", fn, (long long)ld_latent);
   MLA_REQUIRE(k_head_stride % 8 == 0 && v_head_stride % 8 == 0, MLA_ERR_INVALID_ARG,
-              "mla_prefill_attn: head strides must be multiples of 8");
+              "%s: head strides must be multiples of 8", fn);
   const int Hsel = h_end - h_begin;
   MLA_REQUIRE(out_row_stride % 4 == 0 && out_row_stride >= (int64_t)Hsel * kDv && lse_row_stride >= Hsel,
-              MLA_ERR_INVALID_ARG, "mla_prefill_attn: out_row_stride must be >= Hsel*128 (multiple of 4), lse_row_stride >= Hsel");
-  MLA_REQUIRE(scale > 0.f && scale < 1e30f, MLA_ERR_INVALID_ARG, "mla_prefill_attn: scale must be positive and finite");
+              MLA_ERR_INVALID_ARG, "%s: out_row_stride must be >= Hsel*128 (multiple of 4), lse_row_stride >= Hsel", fn);
+  MLA_REQUIRE(scale > 0.f && scale < 1e30f, MLA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  if (merge) {
+    MLA_REQUIRE(prev && prev_lse, MLA_ERR_INVALID_ARG, "%s: null previous state", fn);
+    MLA_REQUIRE(mla_aligned16(prev) && prev_row_stride % 4 == 0 && prev_row_stride >= (int64_t)Hsel * kDv &&
+                    prev_lse_row_stride >= Hsel,
+                MLA_ERR_INVALID_ARG,
+                "%s: previous state must be 16-byte aligned with row stride >= Hsel*128 (multiple of 4)", fn);
+  }
 
   // rows per workgroup: 256 (8 wavefronts) for long query sets, fewer when
   // that would leave most wavefronts without rows or the grid too small.
@@ -405,18 +458,50 @@ extern "C" int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, in
   // (request, head) pairs rounded up to a multiple of the 8 XCDs (the
   // surplus workgroups exit at once)
   const int64_t total = ((int64_t)batch * Hsel + 7) / 8 * 8 * n_qt;
-  MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_prefill_attn: problem too large");
+  MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "%s: problem too large", fn);
   AttnArgs a{static_cast<const uint16_t*>(q), q_row_stride, h_begin, Hsel,
              static_cast<const uint16_t*>(k_nope), k_head_stride,
              static_cast<const uint16_t*>(v), v_head_stride,
              static_cast<const uint16_t*>(latent), ld_latent,
              cu_q, cu_k, q_row_ids, batch, n_qt, scale * kLog2e,
-             out, out_row_stride, lse, lse_row_stride};
+             out, out_row_stride, lse, lse_row_stride,
+             prev, prev_row_stride, prev_lse, prev_lse_row_stride};
   dim3 g((unsigned)total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool rid = q_row_ids != nullptr, c = causal != 0;
-  if (NW == 8) launch1<8>(c, rid, out_dtype, g, s, a);
-  else if (NW == 4) launch1<4>(c, rid, out_dtype, g, s, a);
-  else launch1<2>(c, rid, out_dtype, g, s, a);
-  return mla_check_launch("mla_prefill_attn");
+  if (NW == 8) launch1<8>(c, rid, merge, out_dtype, g, s, a);
+  else if (NW == 4) launch1<4>(c, rid, merge, out_dtype, g, s, a);
+  else launch1<2>(c, rid, merge, out_dtype, g, s, a);
+  return mla_check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                                const void* k_nope, int64_t k_head_stride,
+                                const void* v, int64_t v_head_stride,
+                                const void* latent, int64_t ld_latent,
+                                const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_row_ids,
+                                int batch, int max_q, float scale, int causal,
+                                void* out, int out_dtype, int64_t out_row_stride,
+                                float* lse, int64_t lse_row_stride, void* stream) {
+  return prefill_attn("mla_prefill_attn", q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,
+                      v_head_stride, latent, ld_latent, cu_q, cu_k, q_row_ids, batch, max_q, scale, causal,
+                      out, out_dtype, out_row_stride, lse, lse_row_stride, nullptr, 0, nullptr, 0, false, stream);
+}
+
+extern "C" int mla_prefill_attn_merge(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                                      const void* k_nope, int64_t k_head_stride,
+                                      const void* v, int64_t v_head_stride,
+                                      const void* latent, int64_t ld_latent,
+                                      const int32_t* cu_q, const int32_t* cu_k, const int32_t* q_row_ids,
+                                      int batch, int max_q, float scale, int causal,
+                                      const float* prev_out, int64_t prev_row_stride,
+                                      const float* prev_lse, int64_t prev_lse_row_stride,
+                                      void* out, int out_dtype, int64_t out_row_stride,
+                                      float* lse, int64_t lse_row_stride, void* stream) {
+  return prefill_attn("mla_prefill_attn_merge", q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride,
+                      v, v_head_stride, latent, ld_latent, cu_q, cu_k, q_row_ids, batch, max_q, scale, causal,
+                      out, out_dtype, out_row_stride, lse, lse_row_stride, prev_out, prev_row_stride, prev_lse,
+                      prev_lse_row_stride, true, stream);
 }

@@ -69,9 +69,11 @@ def upload_pool(prob, device) -> torch.Tensor:
 class ChunkedPrefill:
     """Configs with a paged context and new (extend) tokens per request."""
 
-    def __init__(self, prob, device="cuda", chunk=None):
+    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all"):
         self.prob = prob
         self.device = device
+        assert fuse_merge in ("none", "final", "all")
+        self.fuse_merge = fuse_merge
         H = self.H = prob.H
         self.B = prob.B
         self.S = int(chunk or prob.chunk)
@@ -100,10 +102,11 @@ class ChunkedPrefill:
         self.v_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
         self.hstride = self.max_tok * D_V
         T = max(self.T, 1)
-        self.tmp_o = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
-        self.tmp_l = torch.empty((T, H), dtype=torch.float32, device=device)
         self.acc_o = torch.empty((T, H, D_V), dtype=torch.float32, device=device)
         self.acc_l = torch.empty((T, H), dtype=torch.float32, device=device)
+        if fuse_merge != "all":
+            self.tmp_o = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
+            self.tmp_l = torch.empty((T, H), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
@@ -124,12 +127,28 @@ class ChunkedPrefill:
                            self.maxE, self.prob.scale, causal, out, out_dtype, self.H * D_V, lse,
                            self.H, stream)
 
+    def attend_merge(self, latent, cu_k, causal, out, out_dtype, lse, stream=None):
+        """Attention merged into the running fp32 state (acc_o, acc_l)."""
+        L.mla_prefill_attn_merge(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
+                                 self.v_ws, self.hstride, latent, D_LAT, self.cu_ext, cu_k, None,
+                                 self.B, self.maxE, self.prob.scale, causal, self.acc_o, self.H * D_V,
+                                 self.acc_l, self.H, out, out_dtype, self.H * D_V, lse, self.H, stream)
+
     def merge(self, a, da, la, b, db, lb, out, dout, lout, stream=None):
         L.mla_merge_states(a, da, la, b, db, lb, self.T * self.H, out, dout, lout, stream)
 
     def run(self, stream=None, timer=None):
+        """One pass of the chunk loop. Chunk 0's attention writes the running
+        fp32 state (acc). Each later chunk, and then the causal pass over the
+        new tokens, is merged into it, either by mla_merge_states after the
+        attention wrote a bf16 chunk state, or inside the attention kernel
+        (mla_prefill_attn_merge): fuse_merge selects which merges are fused
+        ("none", "final" = only the last, "all"). The last merge writes the
+        bf16 result."""
         if self.T == 0:
             return self.out, self.lse
+        fuse_mid = self.fuse_merge == "all"
+        fuse_last = self.fuse_merge in ("all", "final")
         for ci, ch in enumerate(self.chunks):
             with _span(timer, "gather"):
                 self.gather(ch, stream)
@@ -138,6 +157,10 @@ class ChunkedPrefill:
             if ci == 0:
                 with _span(timer, "attn_ctx"):
                     self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
+            elif fuse_mid:
+                with _span(timer, "attn_ctx"):
+                    self.attend_merge(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l,
+                                      stream)
             else:
                 with _span(timer, "attn_ctx"):
                     self.attend(self.lat_ws, ch["cu"], 0, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
@@ -149,6 +172,9 @@ class ChunkedPrefill:
         if not self.chunks:
             with _span(timer, "attn_ext"):
                 self.attend(self.ext, self.cu_ext, 1, self.out, L.DTYPE_BF16, self.lse, stream)
+        elif fuse_last:
+            with _span(timer, "attn_ext"):
+                self.attend_merge(self.ext, self.cu_ext, 1, self.out, L.DTYPE_BF16, self.lse, stream)
         else:
             with _span(timer, "attn_ext"):
                 self.attend(self.ext, self.cu_ext, 1, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
@@ -170,12 +196,7 @@ class ChunkedPrefill:
         ctx_pairs = int((C * E).sum())
         ext_pairs = int((E * (E + 1) // 2).sum())
         n_merge = max(len(self.chunks) - 1, 0) + (1 if self.chunks else 0)
-        # merge bytes per (row, head): fp32 acc read+write (2*516), bf16 chunk
-        # state read (260); the last merge writes bf16 (260) instead of fp32
-        merge_bytes = self.T * H * ((len(self.chunks) - 1) * (516 + 260 + 516) + (516 + 260 + 260)) \
-            if self.chunks else 0
         return dict(
-            merge_bytes=int(merge_bytes),
             dec_flops=2 * 512 * 256 * H * dec_tok,
             attn_flops=640 * H * (ctx_pairs + ext_pairs),
             ctx_attn_flops=640 * H * ctx_pairs,
@@ -326,13 +347,14 @@ class ReusePrefill:
         return self.y
 
     def work(self) -> dict:
-        """Algorithmic work of one run, in the same units as ChunkedPrefill.work
-        (merge bytes per (row, head): fp32 accumulator read + write, bf16 chunk
-        state read; the last merge writes bf16)."""
+        """Algorithmic work of one run, in the same units as ChunkedPrefill.work.
+        The merge tree makes n_pieces - 1 merges per (row, head); each reads
+        two fp32 states (2 * 516 B) and writes one (516 B), the last one in
+        bf16 (260 B)."""
         H, HL, HG, T, P, Ld = self.H, self.HL, self.HG, self.T, self.P, self.Ldoc
-        n = len(self.chunks)
+        n = self.n_pieces
         rows = T * HG + P * HL
-        merge_bytes = rows * ((n - 2) * (516 + 260 + 516) + (516 + 260 + 260)) if n > 1 else 0
+        merge_bytes = rows * ((n - 2) * 3 * 516 + (2 * 516 + 260)) if n > 1 else 0
         return dict(
             dec_flops=2 * 512 * 256 * H * Ld,
             attn_flops=640 * Ld * rows,

@@ -28,7 +28,7 @@ def test_chunked_prefill_bitwise_repeatable_with_poisoned_workspaces():
     pre.run()
     torch.cuda.synchronize()
     o1, l1 = bits(pre.out).copy(), pre.lse.cpu().numpy().copy()
-    _poison(pre.lat_ws, pre.k_ws, pre.v_ws, pre.tmp_o, pre.tmp_l, pre.acc_o, pre.acc_l, pre.out, pre.lse)
+    _poison(pre.lat_ws, pre.k_ws, pre.v_ws, pre.acc_o, pre.acc_l, pre.out, pre.lse)
     pre.run()
     torch.cuda.synchronize()
     assert np.array_equal(o1, bits(pre.out))

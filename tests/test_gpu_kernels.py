@@ -13,7 +13,8 @@ import mla_long_context_amd as mla
 from mla_long_context_amd import prefill as pf
 from oracle import mla_oracle as orc
 
-from gpu_util import (bf16_dev, bits, check_lse, check_out, f64, rel_l2, require_gpu, say)
+from gpu_util import (FEW_KEYS, LSE_FEW_KEYS, bf16_dev, bits, check_lse, check_out, f64, rel_l2,
+                      require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -221,6 +222,74 @@ def test_attention_row_ids_and_head_range(nq):
 def test_attention_empty_keys_give_zero_and_neg_inf():
     require_gpu()
     _attn_case(61, 2, 0, 2, [33, 5], [0, 0], 0, mla.DTYPE_BF16)
+
+
+# ---------------------------------------------------------------- attention merged into a state
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("in_place", [True, False])
+def test_attention_merge_into_previous_state(causal, in_place):
+    """Keys of every request split into a first segment (attended alone, fp32
+    state) and a second one attended with mla_prefill_attn_merge against that
+    state; the result must be the attention over all keys. With causal = 1 the
+    second segment is the request's own new tokens (bottom-right causal), as
+    in the chunk loop. Empty segments on either side exercise the -inf rules."""
+    require_gpu()
+    say(f"attn merge causal={causal} in_place={in_place}")
+    rng = np.random.default_rng(70 + causal)
+    H, h0, h1 = 3, 0, 3
+    Hs = h1 - h0
+    nq = [300, 5, 0, 77, 40]
+    if causal:
+        nA = [300, 0, 5, 130, 0]            # context keys
+        nB = list(nq)                       # the new tokens themselves
+    else:
+        nA = [0, 64, 3, 100, 0]
+        nB = [700, 0, 2, 0, 0]
+    B = len(nq)
+    cu_q = np.concatenate([[0], np.cumsum(nq)])
+    T = int(cu_q[-1])
+    q = mi.f32_to_bf16_bits(rng.standard_normal((T, H, 192)).astype(np.float32))
+    scale = 1 / math.sqrt(192)
+
+    def segment(n):
+        cu = np.concatenate([[0], np.cumsum(n)]); NK = max(int(cu[-1]), 1)
+        kn = mi.f32_to_bf16_bits(rng.standard_normal((Hs, NK, 128)).astype(np.float32))
+        v = mi.f32_to_bf16_bits(rng.standard_normal((Hs, NK, 128)).astype(np.float32))
+        lat = mi.f32_to_bf16_bits(rng.standard_normal((NK, 576)).astype(np.float32))
+        return cu, NK, kn, v, lat
+
+    cuA, NKA, knA, vA, latA = segment(nA)
+    cuB, NKB, knB, vB, latB = segment(nB)
+    acc = torch.full((T, Hs, 128), float("nan"), dtype=torch.float32, device="cuda")
+    accl = torch.full((T, Hs), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_prefill_attn(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knA), NKA * 128, bf16_dev(vA), NKA * 128,
+                         bf16_dev(latA), 576, _i32(cu_q), _i32(cuA), None, B, max(nq), scale, 0,
+                         acc, mla.DTYPE_FP32, Hs * 128, accl, Hs)
+    if in_place:
+        out, odt, lse = acc, mla.DTYPE_FP32, accl
+    else:
+        out = torch.full((T, Hs, 128), 9.0, dtype=torch.bfloat16, device="cuda")
+        odt = mla.DTYPE_BF16
+        lse = torch.full((T, Hs), 9.0, dtype=torch.float32, device="cuda")
+    mla.mla_prefill_attn_merge(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knB), NKB * 128, bf16_dev(vB),
+                               NKB * 128, bf16_dev(latB), 576, _i32(cu_q), _i32(cuB), None, B, max(nq),
+                               scale, causal, acc, Hs * 128, accl, Hs, out, odt, Hs * 128, lse, Hs)
+    torch.cuda.synchronize()
+    go, gl = f64(out), f64(lse)
+    for b in range(B):
+        rows = np.arange(cu_q[b], cu_q[b + 1])
+        ka = np.arange(cuA[b], cuA[b + 1]); kb = np.arange(cuB[b], cuB[b + 1])
+        vis = orc.causal_visible(nq[b], nA[b]) if causal else None
+        for hs in range(Hs):
+            kn = np.concatenate([knA[hs, ka], knB[hs, kb]]); vv = np.concatenate([vA[hs, ka], vB[hs, kb]])
+            kr = np.concatenate([latA[ka, 512:], latB[kb, 512:]])
+            ro, rl = orc.attend(orc.bf16_to_f64(q[rows, h0 + hs]), orc.bf16_to_f64(kn), orc.bf16_to_f64(kr),
+                                orc.bf16_to_f64(vv), scale, vis)
+            check_out(go[rows, hs], ro, what=f"b{b} h{hs} out")
+            n_keys = len(ka) + len(kb)
+            tol = LSE_FEW_KEYS if n_keys < FEW_KEYS else 1e-3
+            check_lse(gl[rows, hs], rl, tol=tol, what=f"b{b} h{hs} lse")
 
 
 # ---------------------------------------------------------------- head partition merge

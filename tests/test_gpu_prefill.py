@@ -66,13 +66,16 @@ def test_config1_tiny_all_outputs():
     assert np.array_equal(o1, bits(pre.out))
 
 
-@pytest.mark.parametrize("chunk", [64, 100, 4096])
-def test_ragged_multichunk_bf16(chunk):
+# every merge arrangement of the chunk loop: separate mla_merge_states, only
+# the last merge fused into the causal pass, or every merge fused
+@pytest.mark.parametrize("chunk,fuse", [(64, "all"), (100, "all"), (4096, "all"), (64, "none"),
+                                        (100, "final")])
+def test_ragged_multichunk_bf16(chunk, fuse):
     require_gpu()
-    say(f"ragged bf16 chunk={chunk}")
+    say(f"ragged bf16 chunk={chunk} fuse_merge={fuse}")
     prob = mi.make_problem(4, [320, 0, 64 * 9, 64], [70, 5, 300, 1], chunk, "bf16", seed=71,
                            extra_blocks=3, poison=True)
-    pre = ChunkedPrefill(prob)
+    pre = ChunkedPrefill(prob, fuse_merge=fuse)
     _run(pre)
     _compare_chunked(prob, pre)
 
