@@ -20,6 +20,10 @@ that definition states. Pages cited:
 * [REDKNOT] "RedKnot-MLA: Multi-Head Offline-Online Reuse for DeepSeek-V4
   Long-Context Serving": Abstract, section 1, section 2 (Equation 4,
   relocation, protected rows), section 3 (runtime consumer).
+* Cache write path: [PAGED] "Position independence beats prefix matching"
+  (records written into blocks that are sealed when full), [DSMLA] 2.2
+  (fp8 storage of the latent; its content is missing from the page, so the
+  per-token scale follows reading R14).
 
 Readings where the pages are silent are listed in the module docstrings of
 the functions that take them (R-numbers match the design doc).
@@ -141,6 +145,89 @@ def gather_fp8_expected_bits(pool, block_table, req, start, length) -> np.ndarra
     bits[:, :D_C] = f32_to_bf16_bits_rne(f64_to_f32_rne(x[:, :D_C]))
     bits[:, D_C:] = f32_to_bf16_bits_rne(f64_to_f32_rne(x[:, D_C:]))
     return bits
+
+
+# --------------------------------------------------------------------------
+# Cache write path: append new tokens' records into their blocks
+# --------------------------------------------------------------------------
+
+def e4m3fn_encode_rne(x32: np.ndarray) -> np.ndarray:
+    """fp32 values with |x| <= 448 -> OCP E4M3FN codes, round to nearest even,
+    from the bit definition (reading R13): a normal value is (1 + m/8) 2^e
+    with e in [-6, 8] and exponent field e + 7; below 2^-6 the code is the
+    subnormal m with value m/8 * 2^-6, m = round(|x| * 2^9). A mantissa that
+    rounds up to 8 carries into the exponent (for subnormals, m = 8 is the
+    smallest normal, code 0x08). The sign bit is the fp32 sign bit, so -0.0
+    encodes as 0x80."""
+    x = np.asarray(x32, dtype=np.float32)
+    assert np.all(np.abs(x) <= 448.0), "encode expects |x| <= 448"
+    sign = (x.view(np.uint32) >> np.uint32(31)).astype(np.int64)
+    a = np.abs(x).astype(np.float64)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)        # 0..8, exact scaling
+    nz = ~sub
+    if nz.any():
+        e = np.floor(np.log2(a[nz])).astype(np.int64)
+        # guard the log2 rounding at exact powers of two
+        e = np.where(2.0 ** e > a[nz], e - 1, e)
+        e = np.where(2.0 ** (e + 1) <= a[nz], e + 1, e)
+        m = np.rint((a[nz] / 2.0 ** e - 1.0) * 8.0).astype(np.int64)  # exact in fp64, then RNE
+        carry = m == 8
+        e = np.where(carry, e + 1, e)
+        m = np.where(carry, 0, m)
+        code[nz] = ((e + 7) << 3) | m
+    return (code | (sign << 7)).astype(np.uint8)
+
+
+def quantize_token_e4m3(c_kv_bits: np.ndarray):
+    """One fp8 record per token (reading R14): scale = fp32(max|x|) / 448
+    rounded once to fp32; code = e4m3_rne(clamp(fp32(x / scale), +-448)).
+    Division in fp64 then one rounding to fp32 equals the correctly rounded
+    fp32 division (53 >= 2*24 + 2 bits). A row of zeros gets scale 0 and
+    +0 codes. Returns (codes uint8 [n, 512], scale fp32 [n])."""
+    x = (np.asarray(c_kv_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    amax = np.max(np.abs(x.astype(np.float64)), axis=-1)
+    scale = (amax / 448.0).astype(np.float32)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    nz = scale > 0
+    if nz.any():
+        y = (x[nz].astype(np.float64) / scale[nz].astype(np.float64)[:, None]).astype(np.float32)
+        codes[nz] = e4m3fn_encode_rne(np.clip(y, np.float32(-448.0), np.float32(448.0)))
+    return codes, scale
+
+
+def cache_append_expected(pool: np.ndarray, block_table: np.ndarray, pos0, lengths,
+                          new_bits: np.ndarray, cache_dtype: str) -> np.ndarray:
+    """The pool after appending new tokens ([PAGED] "Position independence
+    beats prefix matching": records are written into blocks that are sealed
+    once full; [DSMLA] 2.2 fp8 storage; reading R16 for the fp8 block
+    layout). Token i of request r (rows cu[r] + i of new_bits [n, 576], bf16
+    bits) goes to position pos0[r] + i, i.e. block block_table[r][t // 64],
+    slot t % 64. bf16 pool [NB, 64, 576]: the record is copied. fp8 pool
+    [NB, 41216] bytes: codes and scale from quantize_token_e4m3, rope copied
+    as bf16. Nothing else of the pool changes."""
+    out = pool.copy()
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    for r in range(len(lengths)):
+        n = int(lengths[r])
+        if n == 0:
+            continue
+        t = int(pos0[r]) + np.arange(n)
+        blk, slot = token_to_slot(block_table, r, t)
+        rec = new_bits[cu[r]:cu[r] + n]
+        if cache_dtype == "bf16":
+            out[blk, slot, :] = rec
+            continue
+        codes, scale = quantize_token_e4m3(rec[:, :D_C])
+        for j in range(n):
+            b, sl = int(blk[j]), int(slot[j])
+            out[b, sl * D_C:(sl + 1) * D_C] = codes[j]
+            out[b, FP8_ROPE_OFF + sl * D_ROPE * 2:FP8_ROPE_OFF + (sl + 1) * D_ROPE * 2] = \
+                np.ascontiguousarray(rec[j, D_C:]).view(np.uint8)
+            out[b, FP8_SCALE_OFF + sl * 4:FP8_SCALE_OFF + (sl + 1) * 4] = \
+                np.ascontiguousarray(scale[j:j + 1]).view(np.uint8)
+    return out
 
 
 def context_latent_f64(prob, req: int, start: int, length: int) -> np.ndarray:

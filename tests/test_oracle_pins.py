@@ -469,3 +469,96 @@ def test_latent_record_layout_and_kv_size_table():
         mla_exact_gib = tokens * 61 * 1152 / 1024 ** 3
         assert float(mla_p) == pytest.approx(mla_exact_gib, rel=0.015)
         assert float(ratio_p) == pytest.approx(65536 / 1152, rel=0.015)
+
+
+# ---------------------------------------------------------------- cache write path (fp8 encode)
+
+def _e4m3_finite_values():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    return codes, orc.e4m3fn_to_f64(codes)
+
+
+def test_e4m3_encode_matches_torch_cast_on_ties_and_neighbours():
+    """Every midpoint between adjacent E4M3FN values (the round-to-even ties),
+    one fp32 ulp either side of it, every value itself and random values,
+    against torch's float8_e4m3fn cast (a library routine)."""
+    _, vals = _e4m3_finite_values()
+    pos = np.unique(vals[vals >= 0])
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    x = np.concatenate([pos, mids]).astype(np.float32)
+    x = np.concatenate([x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(-np.inf))])
+    rng = np.random.default_rng(90)
+    x = np.concatenate([x, (rng.standard_normal(20000) * 40).astype(np.float32),
+                        (rng.standard_normal(20000) * 1e-3).astype(np.float32)])
+    x = np.clip(x, -448.0, 448.0).astype(np.float32)
+    x = np.concatenate([x, -x])
+    got = orc.e4m3fn_encode_rne(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_decode_round_trip_every_code():
+    codes, vals = _e4m3_finite_values()
+    assert np.array_equal(orc.e4m3fn_encode_rne(vals.astype(np.float32)), codes)
+
+
+def test_quantize_token_closed_form_record():
+    """c_kv = (1, -2, 0.5, 0, ...): max |x| = 2, scale = fp32(2/448); x/scale
+    = 224, -448, 112 -> codes 0x76 (1.75 * 2^7), 0xFE (-1.75 * 2^8), 0x6E
+    (1.75 * 2^6), zeros -> 0x00. An all-zero record gets scale 0 and zero
+    codes."""
+    rec = np.zeros((2, 512), dtype=np.float32)
+    rec[0, :3] = [1.0, -2.0, 0.5]
+    bits = (rec.view(np.uint32) >> 16).astype(np.uint16)
+    codes, scale = orc.quantize_token_e4m3(bits)
+    assert scale[0] == np.float32(2.0) / np.float32(448.0) and scale[1] == 0
+    assert list(codes[0, :4]) == [0x76, 0xFE, 0x6E, 0x00] and not codes[0, 4:].any()
+    assert not codes[1].any()
+
+
+def test_quantize_token_matches_the_generator_quantiser():
+    """The generator's own quantiser (torch's cast) on random records, plus
+    records whose maximum sits at a tie: identical codes and scales."""
+    rng = np.random.default_rng(91)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    x[5] = 0.0
+    x[6, 7] = 9.0
+    bits = mi.f32_to_bf16_bits(x)
+    c1, s1 = orc.quantize_token_e4m3(bits)
+    c2, s2 = mi.quantize_rows_e4m3(bits)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(c1, c2)
+    # the largest magnitude of a nonzero record maps to +-448 exactly
+    amax_code = c1[np.arange(64), np.argmax(np.abs(orc.bf16_to_f64(bits)), axis=1)]
+    assert np.all((amax_code[np.arange(64) != 5] & 0x7F) == 0x7E)
+
+
+def test_cache_append_expected_places_records_and_touches_nothing_else():
+    """Hand-built pools: request 0 appends 3 tokens at position 62 (crossing
+    into its second block), request 1 one token at position 0. Each record
+    lands in block_table[r][t // 64], slot t % 64, the gather of the written
+    range returns it, and every other byte keeps its value."""
+    rng = np.random.default_rng(92)
+    bt = np.array([[3, 1], [0, 2]], dtype=np.int32)
+    new = mi.f32_to_bf16_bits(rng.standard_normal((4, 576)).astype(np.float32))
+    pos0, lens = [62, 0], [3, 1]
+    pool = np.full((4, 64, 576), 0x7FC0, dtype=np.uint16)
+    out = orc.cache_append_expected(pool, bt, pos0, lens, new, "bf16")
+    assert np.array_equal(out[3, 62], new[0]) and np.array_equal(out[3, 63], new[1])
+    assert np.array_equal(out[1, 0], new[2]) and np.array_equal(out[0, 0], new[3])
+    assert np.array_equal(orc.gather_bf16_bits(out, bt, 0, 62, 3), new[:3])
+    changed = np.any(out != pool, axis=-1)
+    assert changed.sum() == 4
+    fp = np.full((4, orc.fp8_block_bytes()), 0xA5, dtype=np.uint8)
+    out8 = orc.cache_append_expected(fp, bt, pos0, lens, new, "fp8")
+    codes, scale = orc.quantize_token_e4m3(new[:, :512])
+    back = orc.gather_fp8_f64(out8, bt, 0, 62, 3)
+    assert np.array_equal(back[:, :512], orc.e4m3fn_to_f64(codes[:3]) * scale[:3, None].astype(np.float64))
+    assert np.array_equal(back[:, 512:], orc.bf16_to_f64(new[:3, 512:]))
+    # bytes of blocks/slots not written are untouched
+    written = np.zeros_like(fp, dtype=bool)
+    for b, sl in [(3, 62), (3, 63), (1, 0), (0, 0)]:
+        written[b, sl * 512:(sl + 1) * 512] = True
+        written[b, 32768 + sl * 128:32768 + (sl + 1) * 128] = True
+        written[b, 40960 + sl * 4:40960 + (sl + 1) * 4] = True
+    assert np.all(out8[~written] == 0xA5)
