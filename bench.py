@@ -190,6 +190,58 @@ def cpu_baseline_reuse(prob, budget_s=15.0):
                       f"decoding the document once, not counted); NumPy/OpenBLAS with {blas_threads} BLAS threads"}
 
 
+def bench_append(args, torch, mla, mla_inputs):
+    """mla_cache_append over every context token of the workload, written
+    through the workload's own block table into a fresh pool of its dtype;
+    algorithmic bytes per token: the 1152-byte bf16 record read plus the
+    record written (1152 B bf16, 644 B fp8)."""
+    import numpy as np
+    prob = mla_inputs.make_config(args.workload)
+    fp8 = prob.cache_dtype == "fp8"
+    C = prob.ctx_len.astype(np.int64)
+    n = int(C.sum())
+    rng = np.random.default_rng(1000 + args.workload)
+    src = torch.from_numpy(mla_inputs.f32_to_bf16_bits(
+        rng.standard_normal((n, 576), dtype=np.float32)).view(np.int16)).view(torch.bfloat16).cuda()
+    if fp8:
+        pool = torch.zeros((prob.num_blocks, 41216), dtype=torch.uint8, device="cuda")
+    else:
+        pool = torch.zeros((prob.num_blocks, 64, 576), dtype=torch.bfloat16, device="cuda")
+    bt = torch.from_numpy(np.ascontiguousarray(prob.block_table, dtype=np.int32)).cuda()
+    pos0 = torch.zeros(prob.B, dtype=torch.int32, device="cuda")
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(C)]).astype(np.int32)).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cdt = mla.DTYPE_FP8_E4M3 if fp8 else mla.DTYPE_BF16
+
+    def run():
+        mla.mla_cache_append(pool, cdt, prob.num_blocks, bt, bt.shape[1], pos0, cu, prob.B, int(C.max()),
+                             src, 576, status)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(args.steps, 1)
+    per_tok = 1152 + (644 if fp8 else 1152)
+    gbs = n * per_tok / (ms * 1e-3) / 1e9
+    res = {"metric": "MLA cache append GB/s (cache write path)", "value": round(gbs, 1), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8" if fp8 else "bf16", "data": "synthetic",
+           "config": {"workload": mla_inputs.CONFIG_NAMES[args.workload] + " (context tokens appended)",
+                      "tokens": n, "bytes_per_token": per_tok},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "kernel": "mla_cache_append", "bytes_per_launch": n * per_tok,
+                        "avg_launch_ms": round(ms, 4)}}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +252,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="context chunk override (tokens)")
     ap.add_argument("--split", type=int, default=None,
                     help="reuse workload: keys per attention piece (default: the driver's)")
+    ap.add_argument("--append", action="store_true",
+                    help="time the cache write path instead: every context token of the workload "
+                         "appended into its blocks (fp8-quantised for the fp8 workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
@@ -233,6 +288,10 @@ def main():
     import mla_inputs
     import mla_long_context_amd as mla
     from mla_long_context_amd.prefill import ChunkedPrefill, ReusePrefill
+
+    if args.append:
+        bench_append(args, torch, mla, mla_inputs)
+        return
 
     mla.load()                       # fails loudly if libmla.so is missing
     t_gen = time.time()

@@ -115,6 +115,35 @@ int mla_gather_context(const void* pool, int cache_dtype, int num_blocks,
 int mla_pack_weight_t(const void* w, int K, int N, void* out, void* stream);
 
 /*
+ * mla_cache_append -- the cache write path ([PAGED] "Position independence
+ * beats prefix matching": new records are written into 64-token blocks that
+ * are sealed once full; [DSMLA] 2.2: fp8 storage of the latent).
+ *
+ * Token i < n_b = cu_new[b+1] - cu_new[b] of request b (record row
+ * cu_new[b] + i of latent_new, [c_kv 512 | k_rope 64] bf16, row stride
+ * ld_latent elements) is written at position t = pos0[b] + i: block
+ * block_table[b * bt_stride + t / 64], slot t % 64.
+ *   cache_dtype = MLA_DTYPE_BF16: pool [num_blocks][64][576] bf16, the
+ *     record is copied.
+ *   cache_dtype = MLA_DTYPE_FP8_E4M3: pool blocks of 41216 bytes, codes
+ *     [64][512] | k_rope [64][64] bf16 | scale [64] fp32. scale =
+ *     fp32(max|c_kv|) / 448 and code = E4M3FN(clamp(c_kv / scale, +-448)),
+ *     each division correctly rounded and the encoding round-to-nearest-
+ *     even (reading R14); a record of zeros gets scale 0 and +0 codes. k_rope
+ *     is copied as bf16.
+ * A position with t < 0 or t / 64 >= bt_stride, or a block id outside
+ * [0, num_blocks), is skipped and sets *dev_status = MLA_ERR_OUT_OF_RANGE
+ * (dev_status may be NULL). No other byte of the pool is written. All
+ * pointers are device memory; pool, block_table, pos0 and cu_new are int32
+ * or byte arrays owned by the caller; max_new (host) >= every n_b sizes the
+ * launch. Positions of one call must be distinct.
+ */
+int mla_cache_append(void* pool, int cache_dtype, int num_blocks, const int32_t* block_table,
+                     int64_t bt_stride, const int32_t* pos0, const int32_t* cu_new, int batch,
+                     int max_new, const void* latent_new, int64_t ld_latent, int32_t* dev_status,
+                     void* stream);
+
+/*
  * mla_decompress -- [DSMLA] 4.4 step 2: kv = c_kv . kv_b_proj, split into
  * per-head k_nope and v.
  *

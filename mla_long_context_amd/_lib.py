@@ -26,7 +26,7 @@ ROPE_INTERLEAVED = 0
 ROPE_HALF = 1
 
 EXPORTS = (
-    "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_pack_weight_t",
+    "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_cache_append", "mla_pack_weight_t",
     "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_merge_states",
     "mla_rope_relocate_q",
     "mla_head_partition_merge",
@@ -49,6 +49,7 @@ F64 = ctypes.c_double
 
 _SIGS = {
     "mla_gather_context": [P, I32, I32, P, I64, P, P, P, I32, I32, P, P, P],
+    "mla_cache_append": [P, I32, I32, P, I64, P, P, I32, I32, P, I64, P, P],
     "mla_pack_weight_t": [P, I32, I32, P, P],
     "mla_decompress": [P, I64, I32, P, I32, I32, I32, P, I64, P, I64, P],
     "mla_prefill_attn": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
@@ -109,6 +110,13 @@ def mla_gather_context(pool, cache_dtype, num_blocks, block_table, bt_stride, ch
     return _call("mla_gather_context", _ptr(pool), cache_dtype, num_blocks, _ptr(block_table),
                  bt_stride, _ptr(chunk_start), _ptr(chunk_len), _ptr(cu_out), batch, max_len,
                  _ptr(out_latent), _ptr(dev_status), _stream(stream))
+
+
+def mla_cache_append(pool, cache_dtype, num_blocks, block_table, bt_stride, pos0, cu_new, batch,
+                     max_new, latent_new, ld_latent, dev_status=None, stream=None):
+    return _call("mla_cache_append", _ptr(pool), cache_dtype, num_blocks, _ptr(block_table),
+                 bt_stride, _ptr(pos0), _ptr(cu_new), batch, max_new, _ptr(latent_new), ld_latent,
+                 _ptr(dev_status), _stream(stream))
 
 
 def mla_pack_weight_t(w, K, N, out, stream=None):

@@ -73,6 +73,81 @@ def test_gather_out_of_range_block_sets_status_and_writes_zeros():
     assert np.all(got[64:] == 0)
 
 
+# ---------------------------------------------------------------- cache append
+
+def _append_case(dtype, seed):
+    """Four requests append ragged runs of new records into a shuffled pool:
+    an unaligned start crossing two block boundaries, a run ending exactly at
+    a block end, an empty request and a single token. Unused blocks are
+    poisoned; the result must equal the oracle's pool byte for byte."""
+    rng = np.random.default_rng(seed)
+    nb_req = [4, 2, 1, 3]
+    NB = sum(nb_req) + 3
+    perm = rng.permutation(NB).astype(np.int32)
+    bt = np.full((4, 5), -1, dtype=np.int32)
+    k = 0
+    for r, n in enumerate(nb_req):
+        bt[r, :n] = perm[k:k + n]; k += n
+    pos0 = np.array([61, 64, 5, 130], dtype=np.int32)
+    lens = np.array([133, 64, 0, 1], dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    new = mi.f32_to_bf16_bits(rng.standard_normal((int(cu[-1]) + 2, 576)).astype(np.float32) * 3)
+    new[7, :512] = 0                      # a record of zeros: scale 0
+    new[9, 100] = mi.f32_to_bf16_bits(np.array([1e-30], np.float32))[0]   # tiny value next to normal ones
+    if dtype == "bf16":
+        pool = np.full((NB, 64, 576), 0x7FC0, dtype=np.uint16)
+        dpool = bf16_dev(pool)
+        cdt = mla.DTYPE_BF16
+    else:
+        pool = np.full((NB, orc.fp8_block_bytes()), 0xA5, dtype=np.uint8)
+        dpool = torch.from_numpy(pool.copy()).to("cuda")
+        cdt = mla.DTYPE_FP8_E4M3
+    return rng, bt, pos0, lens, cu, new, pool, dpool, cdt, NB
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_cache_append_bit_exact(dtype):
+    require_gpu()
+    say(f"cache append {dtype}")
+    rng, bt, pos0, lens, cu, new, pool, dpool, cdt, NB = _append_case(dtype, 80)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_cache_append(dpool, cdt, NB, _i32(bt), bt.shape[1], _i32(pos0), _i32(cu), 4, int(lens.max()),
+                         bf16_dev(new), 576, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = orc.cache_append_expected(pool, bt, pos0, lens, new, dtype)
+    got = bits(dpool) if dtype == "bf16" else dpool.cpu().numpy()
+    assert np.array_equal(got, ref)
+    # the gather reads back exactly what the oracle stored (fp8: dequantised)
+    out = torch.empty((int(lens[0]), 576), dtype=torch.bfloat16, device="cuda")
+    mla.mla_gather_context(dpool, cdt, NB, _i32(bt), bt.shape[1], _i32([pos0[0]]), _i32([lens[0]]),
+                           _i32([0, lens[0]]), 1, int(lens[0]), out, status)
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        assert np.array_equal(bits(out), new[:lens[0]])
+    else:
+        assert np.array_equal(bits(out), orc.gather_fp8_expected_bits(ref, bt, 0, int(pos0[0]), int(lens[0])))
+
+
+def test_cache_append_out_of_range_is_reported_and_skipped():
+    require_gpu()
+    rng, bt, pos0, lens, cu, new, pool, dpool, cdt, NB = _append_case("fp8", 81)
+    bt[0, 2] = NB + 5                     # positions 128..191 of request 0 -> invalid block id
+    pos_bad = pos0.copy(); pos_bad[3] = 5 * 64 - 1 + 1   # request 3 runs past its block-table row
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_cache_append(dpool, cdt, NB, _i32(bt), bt.shape[1], _i32(pos_bad), _i32(cu), 4,
+                         int(lens.max()), bf16_dev(new), 576, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == mla._lib.MLA_ERR_OUT_OF_RANGE
+    # valid positions are written as usual; the skipped ones leave the pool
+    # as it was: request 0 keeps positions 61..127 and 192..193, request 1 is
+    # whole, request 3 is skipped
+    ref = orc.cache_append_expected(pool, bt[0:1], [61], [67], new[0:67], "fp8")
+    ref = orc.cache_append_expected(ref, bt[0:1], [192], [2], new[131:133], "fp8")
+    ref = orc.cache_append_expected(ref, bt[1:2], [pos0[1]], [lens[1]], new[cu[1]:cu[2]], "fp8")
+    assert np.array_equal(dpool.cpu().numpy(), ref)
+
+
 # ---------------------------------------------------------------- merge
 
 @pytest.mark.parametrize("da,db,do", [(2, 0, 2), (2, 0, 0), (0, 0, 0), (2, 2, 2)])
