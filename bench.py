@@ -252,6 +252,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="context chunk override (tokens)")
     ap.add_argument("--split", type=int, default=None,
                     help="reuse workload: keys per attention piece (default: the driver's)")
+    ap.add_argument("--local-path", choices=["absorbed", "decompressed"], default="absorbed",
+                    help="reuse workload: form of the Local heads' protected-row attention")
     ap.add_argument("--append", action="store_true",
                     help="time the cache write path instead: every context token of the workload "
                          "appended into its blocks (fp8-quantised for the fp8 workload)")
@@ -299,7 +301,7 @@ def main():
     reuse = bool(getattr(prob, "is_reuse", False))
     if reuse:
         kw = {} if args.split is None else {"split": args.split}
-        pre = ReusePrefill(prob, chunk=args.chunk, **kw)
+        pre = ReusePrefill(prob, chunk=args.chunk, local_path=args.local_path, **kw)
     else:
         pre = ChunkedPrefill(prob, chunk=args.chunk)
     work = pre.work()
@@ -332,13 +334,14 @@ def main():
     torch.cuda.synchronize()
     kern = timer.summary()
 
-    flops = work["dec_flops"] + work["attn_flops"] + work.get("proj_flops", 0)
+    flops = work["dec_flops"] + work["attn_flops"] + work.get("proj_flops", 0) + work.get("absorb_flops", 0)
     tflops = flops / (ms * 1e-3) / 1e12
     # algorithmic work per step of each timed kernel: flops for the MFMA
     # kernels, bytes for the HBM-bound ones
     mfma_work = {"attn_ctx": work.get("ctx_attn_flops"), "attn_ext": work.get("ext_attn_flops"),
                  "decompress": work["dec_flops"], "attn_global": work.get("global_attn_flops"),
-                 "attn_local": work.get("local_attn_flops"), "projection": work.get("proj_flops")}
+                 "attn_local": work.get("local_attn_flops"), "projection": work.get("proj_flops"),
+                 "absorb": work.get("absorb_flops")}
     hbm_work = {"gather": work["gather_bytes"], "merge": work.get("merge_bytes"),
                 "relocate": work.get("relocate_bytes")}
     per_step_launch = {k: c / args.steps for k, (c, _) in kern.items()}
@@ -364,8 +367,10 @@ def main():
         traffic = traffic_for(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip"))
     kname = {"attn_ctx": "mla_prefill_attn (context pass)", "attn_ext": "mla_prefill_attn (causal pass)",
              "decompress": "mla_decompress", "attn_global": "mla_prefill_attn (Global heads)",
-             "attn_local": "mla_prefill_attn (protected Local rows)",
-             "projection": "mla_head_partition_merge"}[dom]
+             "attn_local": ("mla_absorbed_attn (protected Local rows)" if getattr(pre, "absorbed", False)
+                            else "mla_prefill_attn (protected Local rows)"),
+             "projection": "mla_head_partition_merge",
+             "absorb": "mla_absorb_q / mla_absorb_out"}[dom]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": kname,
@@ -373,7 +378,8 @@ def main():
 
     if reuse:
         cfg = {"workload": mla_inputs.CONFIG_NAMES[args.workload], "heads": prob.H,
-               "local_heads": pre.HL, "global_heads": pre.HG, "document_tokens": pre.Ldoc,
+               "local_heads": pre.HL, "global_heads": pre.HG, "local_path": pre.local_path,
+               "document_tokens": pre.Ldoc,
                "query_rows": pre.T, "protected_rows": pre.P, "chunk": pre.S, "split": pre.split,
                "cache": "bf16"}
     else:

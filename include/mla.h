@@ -223,6 +223,52 @@ int mla_prefill_attn_merge(const void* q, int64_t q_row_stride, int H_q, int h_b
                            float* lse, int64_t lse_row_stride, void* stream);
 
 /*
+ * Absorbed-form attention ([DSMLA] section 3: W_UK folded into the query,
+ * W_UV applied after the attention, every head attends to the shared
+ * 576-wide latent), for query sets small next to the key count: the
+ * protected rows of the Local heads in [REDKNOT] section 2. Three calls:
+ *
+ * mla_absorb_q -- for head h in [h_begin, h_end) (hs = h - h_begin) and row
+ * i < n_rows (query row p = row_ids[i]):
+ *   q_abs[(hs * n_rows + i) * 576 + j] = sum_d q[p][h][d] * kv_b_proj[j][h * 128 + d]
+ *                                        for j < 512 (d < 128, nope part)
+ *   q_abs[(hs * n_rows + i) * 576 + 512 + r] = q[p][h][128 + r]   (rope part, copied)
+ * with q[p][h][e] = q[p * q_row_stride + h * 192 + e], kv_b_proj the bf16
+ * [512][H_total * 256] weight in its original layout (W_UK columns first).
+ * Accumulation in fp32, q_abs rounded to bf16.
+ */
+int mla_absorb_q(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                 const int32_t* row_ids, int n_rows, const void* kv_b_proj, int H_total,
+                 void* q_abs, void* stream);
+
+/*
+ * mla_absorbed_attn -- multi-query attention of R absorbed query rows
+ * (q_abs [R][576] bf16) over latent keys, separately for each of `pieces` key
+ * ranges [cu_k[b], cu_k[b+1]) of latent (rows of ld_latent elements):
+ *   s_t = scale * (q_abs[i] . latent[t][0..575])
+ *   o_lat[(b * R + i) * 512 + d] = sum_t softmax(s)_t latent[t][d]     (d < 512)
+ *   lse4[(b * R + i) * 4 + k]   = ln sum_t e^{s_t}                     (k < 4)
+ * The lse is written four times so that each 512-wide state is also four
+ * 128-wide states with their own lse, as mla_merge_states reads them: the
+ * pieces of a row merge with mla_merge_states over 4 * R rows. An empty piece
+ * gives o_lat = 0 and lse = -inf. out_dtype MLA_DTYPE_BF16 or
+ * MLA_DTYPE_FP32.
+ */
+int mla_absorbed_attn(const void* q_abs, int R, const void* latent, int64_t ld_latent,
+                      const int32_t* cu_k, int pieces, float scale, void* out_lat, int out_dtype,
+                      float* lse4, void* stream);
+
+/*
+ * mla_absorb_out -- out[i * out_row_stride + hs * 128 + e] =
+ *   sum_d o_lat[(hs * n_rows + i) * 512 + d] * kv_b_proj[d][H_total * 128 + h * 128 + e]
+ * for head h = h_begin + hs, with o_lat bf16 and the weight given packed as
+ * by mla_pack_weight_t (w_t [H_total * 256][512]). fp32 accumulation, bf16
+ * out.
+ */
+int mla_absorb_out(const void* o_lat, int n_rows, const void* w_t, int H_total, int h_begin, int h_end,
+                   void* out, int64_t out_row_stride, void* stream);
+
+/*
  * mla_merge_states -- [DSMLA] 4.3 (merge_attn_states), with the merged lse
  * m + ln(e^{la-m} + e^{lb-m}) that the chunk loop of 4.4 consumes.
  *

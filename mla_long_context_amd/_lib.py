@@ -27,7 +27,8 @@ ROPE_HALF = 1
 
 EXPORTS = (
     "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_cache_append", "mla_pack_weight_t",
-    "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_merge_states",
+    "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_absorb_q",
+    "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states",
     "mla_rope_relocate_q",
     "mla_head_partition_merge",
 )
@@ -56,6 +57,9 @@ _SIGS = {
                          I32, I32, F32, I32, P, I32, I64, P, I64, P],
     "mla_prefill_attn_merge": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
                                I32, I32, F32, I32, P, I64, P, I64, P, I32, I64, P, I64, P],
+    "mla_absorb_q": [P, I64, I32, I32, I32, P, I32, P, I32, P, P],
+    "mla_absorbed_attn": [P, I32, P, I64, P, I32, F32, P, I32, P, P],
+    "mla_absorb_out": [P, I32, P, I32, I32, I32, P, I64, P],
     "mla_merge_states": [P, I32, P, P, I32, P, I64, P, I32, P, P],
     "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
     "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
@@ -148,6 +152,23 @@ def mla_prefill_attn_merge(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_
                  _ptr(cu_k), _ptr(q_row_ids), batch, max_q, float(scale), int(causal), _ptr(prev_out),
                  prev_row_stride, _ptr(prev_lse), prev_lse_row_stride, _ptr(out), out_dtype,
                  out_row_stride, _ptr(lse), lse_row_stride, _stream(stream))
+
+
+def mla_absorb_q(q, q_row_stride, H_q, h_begin, h_end, row_ids, n_rows, kv_b_proj, H_total, q_abs,
+                 stream=None):
+    return _call("mla_absorb_q", _ptr(q), q_row_stride, H_q, h_begin, h_end, _ptr(row_ids), n_rows,
+                 _ptr(kv_b_proj), H_total, _ptr(q_abs), _stream(stream))
+
+
+def mla_absorbed_attn(q_abs, R, latent, ld_latent, cu_k, pieces, scale, out_lat, out_dtype, lse4,
+                      stream=None):
+    return _call("mla_absorbed_attn", _ptr(q_abs), R, _ptr(latent), ld_latent, _ptr(cu_k), pieces,
+                 float(scale), _ptr(out_lat), out_dtype, _ptr(lse4), _stream(stream))
+
+
+def mla_absorb_out(o_lat, n_rows, w_t, H_total, h_begin, h_end, out, out_row_stride, stream=None):
+    return _call("mla_absorb_out", _ptr(o_lat), n_rows, _ptr(w_t), H_total, h_begin, h_end, _ptr(out),
+                 out_row_stride, _stream(stream))
 
 
 def mla_merge_states(out_a, dtype_a, lse_a, out_b, dtype_b, lse_b, rows, out, dtype_out, lse_out,

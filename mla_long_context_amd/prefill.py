@@ -210,6 +210,11 @@ class ChunkedPrefill:
 class ReusePrefill:
     """Head-partitioned reuse over one document at canonical positions.
 
+    Local heads (protected rows only) take the absorbed form by default
+    (local_path="absorbed"): W_UK is folded into their queries and they
+    attend to the gathered latent directly, so only the Global heads are
+    decompressed; local_path="decompressed" decompresses every head instead.
+
     Per document chunk: gather, decompression of every head, then attention
     of the Global heads (all query rows) and of the Local heads (protected
     rows only). There are few query rows, so one (head, row tile) per
@@ -220,14 +225,21 @@ class ReusePrefill:
     a log-depth tree of mla_merge_states calls. By the merge identity this
     equals the chunk-by-chunk merge."""
 
-    def __init__(self, prob, device="cuda", chunk=None, split=2048):
+    def __init__(self, prob, device="cuda", chunk=None, split=2048, local_path="absorbed",
+                 split_local=8192):
         assert prob.is_reuse
+        assert local_path in ("absorbed", "decompressed")
         self.prob = prob
         self.device = device
+        self.local_path = local_path
+        self.absorbed = local_path == "absorbed"
         H = self.H = prob.H
         self.HL, self.HG = prob.n_local, H - prob.n_local
         self.S = int(chunk or prob.chunk)
         self.split = max(64, int(split) // 64 * 64)
+        # the absorbed Local rows fill the GPU with fewer, longer pieces (56
+        # row tiles per piece at 56 heads x 64 rows): fewer partial states
+        self.split_L = max(64, int(split_local) // 64 * 64) if local_path == "absorbed" else self.split
         self.Ldoc = int(prob.ctx_len[0])
         self.T = prob.T
         self.P = int(len(prob.prot_rows))
@@ -238,6 +250,9 @@ class ReusePrefill:
         self.q = _bf16(prob.q, device)
         self.q_rel = torch.empty_like(self.q)
         self.w_t = pack_weight(prob.W, device)
+        # the original kv_b_proj layout (W_UK columns K-contiguous per output
+        # row) for the query absorption of the Local heads
+        self.W = _bf16(prob.W, device) if self.absorbed else None
         self.art = _bf16(prob.art_out, device)
         self.prot = _i32(prob.prot_rows, device)
         self.wa_t = pack_weight(np.concatenate([prob.WaL, prob.WaG], axis=0), device)
@@ -246,59 +261,102 @@ class ReusePrefill:
         prot = np.asarray(prob.prot_rows, dtype=np.int64)
         # chunk plan; piece i of the document is split (chunk c, piece j)
         self.chunks = []
-        n_pieces = 0
+        n_pieces = n_pieces_L = 0
         for s0 in range(0, self.Ldoc, self.S):
             n = min(self.S, self.Ldoc - s0)
             bounds = list(range(0, n, self.split)) + [n]
             k = len(bounds) - 1
+            bounds_L = list(range(0, n, self.split_L)) + [n]
+            kL = len(bounds_L) - 1
             self.chunks.append(dict(
                 start=_i32([s0], device), len=_i32([n], device), cu=_i32([0, n], device), n=n,
                 pieces=k, first=n_pieces, cu_k=_i32(bounds, device),
+                pieces_L=kL, first_L=n_pieces_L, cu_kL=_i32(bounds_L, device),
                 cu_qG=_i32(np.arange(k + 1) * T, device), rid_G=_i32(np.tile(np.arange(T), k), device),
-                cu_qL=_i32(np.arange(k + 1) * P, device), rid_L=_i32(np.tile(prot, k), device)))
+                cu_qL=_i32(np.arange(kL + 1) * P, device), rid_L=_i32(np.tile(prot, kL), device)))
             n_pieces += k
+            n_pieces_L += kL
         self.n_pieces = n_pieces
+        self.n_pieces_L = n_pieces_L
         S = self.S
-        self.lat_ws = torch.empty((S, D_LAT), dtype=torch.bfloat16, device=device)
-        self.k_ws = torch.empty((H, S, D_V), dtype=torch.bfloat16, device=device)
-        self.v_ws = torch.empty((H, S, D_V), dtype=torch.bfloat16, device=device)
-        self.hstride = S * D_V
         HL, HG = self.HL, self.HG
+        # heads whose k_nope / v are decompressed: all of them, or only the
+        # Global ones when the Local rows take the absorbed form
+        self.kv_h0 = HL if self.absorbed else 0
+        n_kv = H - self.kv_h0
+        self.lat_ws = torch.empty((S, D_LAT), dtype=torch.bfloat16, device=device)
+        self.k_ws = torch.empty((max(n_kv, 1), S, D_V), dtype=torch.bfloat16, device=device)
+        self.v_ws = torch.empty((max(n_kv, 1), S, D_V), dtype=torch.bfloat16, device=device)
+        self.hstride = S * D_V
         f32, bf = torch.float32, torch.bfloat16
         # partial states of every piece, fp32: [pieces * rows, heads, 128]
         self.part_G = torch.empty((max(n_pieces * T, 1), max(HG, 1), D_V), dtype=f32, device=device)
         self.partl_G = torch.empty((max(n_pieces * T, 1), max(HG, 1)), dtype=f32, device=device)
-        self.part_L = torch.empty((max(n_pieces * P, 1), max(HL, 1), D_V), dtype=f32, device=device)
-        self.partl_L = torch.empty((max(n_pieces * P, 1), max(HL, 1)), dtype=f32, device=device)
+        if self.absorbed:
+            # absorbed Local rows: R = HL * P query rows (head-major), 512-wide
+            # latent states viewed as four 128-wide states for the merges
+            R = HL * P
+            self.q_abs = torch.empty((max(R, 1), D_LAT), dtype=bf, device=device)
+            self.part_L = torch.empty((max(n_pieces_L * R, 1), 4, D_V), dtype=f32, device=device)
+            self.partl_L = torch.empty((max(n_pieces_L * R, 1), 4), dtype=f32, device=device)
+            self.olat_L = torch.empty((max(R, 1), 4, D_V), dtype=bf, device=device)
+            self.lse4_L = torch.empty((max(R, 1), 4), dtype=f32, device=device)
+        else:
+            self.part_L = torch.empty((max(n_pieces_L * P, 1), max(HL, 1), D_V), dtype=f32, device=device)
+            self.partl_L = torch.empty((max(n_pieces_L * P, 1), max(HL, 1)), dtype=f32, device=device)
         self.glob_out = torch.empty((T, HG, D_V), dtype=bf, device=device)
         self.lse_G = torch.empty((T, HG), dtype=f32, device=device)
         self.rec_out = torch.empty((max(P, 1), HL, D_V), dtype=bf, device=device)
-        self.lse_L = torch.empty((max(P, 1), HL), dtype=f32, device=device)
+        if not self.absorbed:
+            self._lse_L = torch.empty((max(P, 1), HL), dtype=f32, device=device)
         self.z = torch.empty((T, self.d_mid), dtype=bf, device=device)
         self.y = torch.empty((T, self.d_model), dtype=bf, device=device)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
 
-    def _attn_pieces(self, ch, h0, h1, n_rows, cu_q, rid, part, partl, fin, finl, stream):
+    @property
+    def lse_L(self):
+        """lse of the protected rows of the Local heads, [P, HL]."""
+        if self.absorbed:
+            return self.lse4_L[:, 0].reshape(self.HL, self.P).t()
+        return self._lse_L
+
+    def _attn_pieces(self, ch, h0, h1, n_rows, cu_q, rid, part, partl, fin, finl, stream, local=False):
         """Attention of heads [h0, h1) for the query rows rid over every piece
         of chunk ch: piece j's state goes to rows (first + j) * n_rows of the
         fp32 partial buffers, or straight to the bf16 result when the whole
         document is one piece."""
         Hs = h1 - h0
-        if self.n_pieces == 1:
+        pieces, first, cu_k, total = ((ch["pieces_L"], ch["first_L"], ch["cu_kL"], self.n_pieces_L) if local
+                                      else (ch["pieces"], ch["first"], ch["cu_k"], self.n_pieces))
+        if total == 1:
             out, odt, lse = fin, L.DTYPE_BF16, finl
         else:
-            row0 = ch["first"] * n_rows
+            row0 = first * n_rows
             out, odt, lse = part[row0:], L.DTYPE_FP32, partl[row0:]
-        L.mla_prefill_attn(self.q_rel, self.H * D_QK, self.H, h0, h1, self.k_ws[h0], self.hstride,
-                           self.v_ws[h0], self.hstride, self.lat_ws, D_LAT, cu_q, ch["cu_k"], rid,
-                           ch["pieces"], n_rows, self.prob.scale, 0, out, odt, Hs * D_V, lse, Hs, stream)
+        slab = h0 - self.kv_h0
+        L.mla_prefill_attn(self.q_rel, self.H * D_QK, self.H, h0, h1, self.k_ws[slab], self.hstride,
+                           self.v_ws[slab], self.hstride, self.lat_ws, D_LAT, cu_q, cu_k, rid,
+                           pieces, n_rows, self.prob.scale, 0, out, odt, Hs * D_V, lse, Hs, stream)
 
-    def _merge_tree(self, part, partl, n_rows, fin, finl, stream):
+    def _absorbed_pieces(self, ch, stream):
+        """Absorbed-form attention of the HL * P Local query rows over every
+        Local piece of chunk ch (fp32 partial states, or the bf16 result when
+        the whole document is one piece)."""
+        R = self.HL * self.P
+        if self.n_pieces_L == 1:
+            out, odt, lse = self.olat_L, L.DTYPE_BF16, self.lse4_L
+        else:
+            row0 = ch["first_L"] * R
+            out, odt, lse = self.part_L[row0:], L.DTYPE_FP32, self.partl_L[row0:]
+        L.mla_absorbed_attn(self.q_abs, R, self.lat_ws, D_LAT, ch["cu_kL"], ch["pieces_L"], self.prob.scale,
+                            out, odt, lse, stream)
+
+    def _merge_tree(self, part, partl, n_rows, fin, finl, stream, n_pieces=None):
         """Merge the partial states of all pieces into (fin, finl). Each level
         merges the first half of the remaining pieces with the last half in
         place (fp32; an odd middle piece waits for the next level); the last
         level writes the bf16 result."""
-        n = self.n_pieces
+        n = self.n_pieces if n_pieces is None else n_pieces
         heads = part.shape[1]
         while n > 1:
             h = n // 2
@@ -319,27 +377,42 @@ class ReusePrefill:
         with _span(timer, "relocate"):
             L.mla_rope_relocate_q(self.q, self.q_rel, H * D_QK, T, H, p.delta, p.rope_base,
                                   L.ROPE_INTERLEAVED, stream)
+        if self.absorbed and HL > 0 and P > 0:
+            with _span(timer, "absorb"):
+                L.mla_absorb_q(self.q_rel, H * D_QK, H, 0, HL, self.prot, P, self.W, H, self.q_abs, stream)
         for ch in self.chunks:
             with _span(timer, "gather"):
                 L.mla_gather_context(self.pool, L.DTYPE_BF16, p.num_blocks, self.bt, self.bt.shape[1],
                                      ch["start"], ch["len"], ch["cu"], 1, ch["n"], self.lat_ws,
                                      self.dev_status, stream)
-            with _span(timer, "decompress"):
-                L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, H, 0, H, self.k_ws, self.hstride,
-                                 self.v_ws, self.hstride, stream)
+            if self.kv_h0 < H:
+                with _span(timer, "decompress"):
+                    L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, H, self.kv_h0, H, self.k_ws,
+                                     self.hstride, self.v_ws, self.hstride, stream)
             if HG > 0 and T > 0:
                 with _span(timer, "attn_global"):
                     self._attn_pieces(ch, HL, H, T, ch["cu_qG"], ch["rid_G"], self.part_G, self.partl_G,
                                       self.glob_out, self.lse_G, stream)
             if HL > 0 and P > 0:
                 with _span(timer, "attn_local"):
-                    self._attn_pieces(ch, 0, HL, P, ch["cu_qL"], ch["rid_L"], self.part_L, self.partl_L,
-                                      self.rec_out, self.lse_L, stream)
+                    if self.absorbed:
+                        self._absorbed_pieces(ch, stream)
+                    else:
+                        self._attn_pieces(ch, 0, HL, P, ch["cu_qL"], ch["rid_L"], self.part_L,
+                                          self.partl_L, self.rec_out, self._lse_L, stream, local=True)
         with _span(timer, "merge"):
             if HG > 0 and T > 0:
                 self._merge_tree(self.part_G, self.partl_G, T, self.glob_out, self.lse_G, stream)
             if HL > 0 and P > 0:
-                self._merge_tree(self.part_L, self.partl_L, P, self.rec_out, self.lse_L, stream)
+                if self.absorbed:
+                    self._merge_tree(self.part_L, self.partl_L, HL * P, self.olat_L, self.lse4_L, stream,
+                                     self.n_pieces_L)
+                else:
+                    self._merge_tree(self.part_L, self.partl_L, P, self.rec_out, self._lse_L, stream,
+                                     self.n_pieces_L)
+        if self.absorbed and HL > 0 and P > 0:
+            with _span(timer, "absorb"):
+                L.mla_absorb_out(self.olat_L, P, self.w_t, H, 0, HL, self.rec_out, HL * D_V, stream)
         with _span(timer, "projection"):
             L.mla_head_partition_merge(self.art, self.rec_out, self.prot, P, self.glob_out, self.wa_t,
                                        self.wb_t, T, HL, HG, self.d_mid, self.d_model, self.z, self.y,
@@ -353,13 +426,30 @@ class ReusePrefill:
         bf16 (260 B)."""
         H, HL, HG, T, P, Ld = self.H, self.HL, self.HG, self.T, self.P, self.Ldoc
         n = self.n_pieces
-        rows = T * HG + P * HL
-        merge_bytes = rows * ((n - 2) * 3 * 516 + (2 * 516 + 260)) if n > 1 else 0
+        if self.absorbed:
+            # Global rows: decompressed form; Local protected rows: absorbed
+            # form, 2 * 576 + 2 * 512 flop per (row, key, head), plus the
+            # query absorption and the W_UV product (2 * 128 * 512 each per
+            # (row, head)); merges of 512-wide states (4 x 128)
+            merge_rows = T * HG + 4 * P * HL
+            dec_heads = HG
+            local = 2176 * Ld * P * HL
+            absorb = 2 * (2 * 128 * 512) * P * HL
+        else:
+            merge_rows = T * HG + P * HL
+            dec_heads = H
+            local = 640 * Ld * P * HL
+            absorb = 0
+        def tree(rows, k):
+            return rows * ((k - 2) * 3 * 516 + (2 * 516 + 260)) if k > 1 else 0
+        merge_bytes = tree(T * HG, n) + tree(merge_rows - T * HG, self.n_pieces_L)
+        glob = 640 * Ld * T * HG
         return dict(
-            dec_flops=2 * 512 * 256 * H * Ld,
-            attn_flops=640 * Ld * rows,
-            global_attn_flops=640 * Ld * T * HG,
-            local_attn_flops=640 * Ld * P * HL,
+            dec_flops=2 * 512 * 256 * dec_heads * Ld,
+            attn_flops=glob + local,
+            global_attn_flops=glob,
+            local_attn_flops=local,
+            absorb_flops=absorb,
             proj_flops=2 * T * ((HL + HG) * 128 * self.d_mid + self.d_mid * self.d_model),
             relocate_bytes=T * H * 768,   # out of place: q head row read (384 B) + written
             merge_bytes=int(merge_bytes),

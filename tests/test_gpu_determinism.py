@@ -35,15 +35,19 @@ def test_chunked_prefill_bitwise_repeatable_with_poisoned_workspaces():
     assert np.array_equal(l1.view(np.uint32), pre.lse.cpu().numpy().view(np.uint32))
 
 
-def test_reuse_prefill_bitwise_repeatable_with_poisoned_workspaces():
+@pytest.mark.parametrize("local", ["absorbed", "decompressed"])
+def test_reuse_prefill_bitwise_repeatable_with_poisoned_workspaces(local):
     require_gpu()
-    say("determinism: reuse prefill")
+    say(f"determinism: reuse prefill, Local rows {local}")
     prob = mi.make_reuse_problem(H=8, n_local=7, L=512 + 64, T=100, delta=4096, P=7,
                                  d_mid=256, d_model=256, chunk=256, seed=82)
-    pre = ReusePrefill(prob)
+    pre = ReusePrefill(prob, local_path=local)
     y1 = bits(pre.run()).copy()
-    _poison(pre.q_rel, pre.lat_ws, pre.k_ws, pre.v_ws, pre.part_G, pre.partl_G, pre.part_L, pre.partl_L,
-            pre.glob_out, pre.rec_out, pre.z, pre.y)
+    ws = [pre.q_rel, pre.lat_ws, pre.k_ws, pre.v_ws, pre.part_G, pre.partl_G, pre.part_L, pre.partl_L,
+          pre.glob_out, pre.rec_out, pre.z, pre.y]
+    if pre.absorbed:
+        ws += [pre.q_abs, pre.olat_L, pre.lse4_L]
+    _poison(*ws)
     y2 = bits(pre.run())
     torch.cuda.synchronize()
     assert np.array_equal(y1, y2)

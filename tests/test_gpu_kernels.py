@@ -367,6 +367,86 @@ def test_attention_merge_into_previous_state(causal, in_place):
             check_lse(gl[rows, hs], rl, tol=tol, what=f"b{b} h{hs} lse")
 
 
+# ---------------------------------------------------------------- absorbed-form attention
+
+@pytest.mark.parametrize("n_rows,pieces", [(37, [0, 300, 364, 1000, 1000]), (64, [0, 2048]), (130, [0, 31, 97])])
+def test_absorbed_path(n_rows, pieces):
+    """mla_absorb_q -> mla_absorbed_attn over key pieces (ragged, a 64-key
+    piece, an empty one) -> the pieces merged with mla_merge_states as four
+    128-wide states per row -> mla_absorb_out, against the oracle's absorbed
+    definition per head over all keys; each piece's (o_lat, lse) is also
+    checked against the plain softmax over that piece."""
+    require_gpu()
+    say(f"absorbed path rows={n_rows} pieces={pieces}")
+    rng = np.random.default_rng(75 + n_rows)
+    H, h0, h1, Tphys = 8, 2, 7, max(200, n_rows + 10)
+    Hs = h1 - h0
+    NK = pieces[-1]
+    q = mi.f32_to_bf16_bits(rng.standard_normal((Tphys, H, 192)).astype(np.float32))
+    lat = mi.f32_to_bf16_bits(rng.standard_normal((max(NK, 1) + 3, 576)).astype(np.float32))
+    W = mi.f32_to_bf16_bits((rng.standard_normal((512, H * 256)) / math.sqrt(512)).astype(np.float32))
+    rid = np.sort(rng.choice(Tphys, n_rows, replace=False)).astype(np.int32)
+    scale = 1 / math.sqrt(192)
+    R = Hs * n_rows
+    qa = torch.empty((R, 576), dtype=torch.bfloat16, device="cuda")
+    mla.mla_absorb_q(bf16_dev(q), H * 192, H, h0, h1, _i32(rid), n_rows, bf16_dev(W), H, qa)
+    P = len(pieces) - 1
+    o_lat = torch.full((P * R, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse4 = torch.full((P * R, 4), float("nan"), dtype=torch.float32, device="cuda")
+    dlat = bf16_dev(lat)
+    mla.mla_absorbed_attn(qa, R, dlat, 576, _i32(pieces), P, scale, o_lat, mla.DTYPE_FP32, lse4)
+    torch.cuda.synchronize()
+    qa_h = bits(qa)
+    Wf = orc.bf16_to_f64(W)
+    # q_abs against the definition
+    for hs, h in enumerate(range(h0, h1)):
+        ref = orc.bf16_to_f64(q[rid, h, :128]) @ Wf[:, h * 128:(h + 1) * 128].T
+        check_out(orc.bf16_to_f64(qa_h[hs * n_rows:(hs + 1) * n_rows, :512]), ref, what=f"q_abs head {h}")
+        assert np.array_equal(qa_h[hs * n_rows:(hs + 1) * n_rows, 512:], q[rid, h, 128:])
+    # every piece is a plain softmax over its keys, with the kernel's own q_abs
+    L = orc.bf16_to_f64(lat)
+    QA = orc.bf16_to_f64(qa_h)
+    go, gl = f64(o_lat), f64(lse4)
+    for b in range(P):
+        keys = np.arange(pieces[b], pieces[b + 1])
+        if len(keys):
+            sc = scale * (QA @ L[keys].T)
+            m = sc.max(axis=1)
+            e = np.exp(sc - m[:, None])
+            ro, rl = (e @ L[keys, :512]) / e.sum(axis=1)[:, None], m + np.log(e.sum(axis=1))
+        else:
+            ro, rl = np.zeros((R, 512)), np.full(R, -np.inf)
+        check_out(go[b * R:(b + 1) * R], ro, what=f"piece {b} o_lat")
+        for k4 in range(4):
+            check_lse(gl[b * R:(b + 1) * R, k4], rl, tol=LSE_FEW_KEYS if len(keys) < FEW_KEYS else 1e-3,
+                      what=f"piece {b} lse[{k4}]")
+    # merge the pieces (first half with last half, in place; the last level to bf16)
+    n = P
+    fin = torch.empty((R, 512), dtype=torch.bfloat16, device="cuda")
+    finl = torch.empty((R, 4), dtype=torch.float32, device="cuda")
+    if n == 1:   # a single piece: the attention writes the bf16 state itself
+        mla.mla_absorbed_attn(qa, R, dlat, 576, _i32(pieces), 1, scale, fin, mla.DTYPE_BF16, finl)
+    while n > 1:
+        hh = n // 2; m0 = n - hh
+        a, al = o_lat[:hh * R], lse4[:hh * R]
+        bb, bl = o_lat[m0 * R:], lse4[m0 * R:]
+        if n == 2:
+            mla.mla_merge_states(a, mla.DTYPE_FP32, al, bb, mla.DTYPE_FP32, bl, hh * R * 4, fin, mla.DTYPE_BF16, finl)
+        else:
+            mla.mla_merge_states(a, mla.DTYPE_FP32, al, bb, mla.DTYPE_FP32, bl, hh * R * 4, a, mla.DTYPE_FP32, al)
+        n = m0
+    wt = pf.pack_weight(W, "cuda")
+    out = torch.full((n_rows, Hs * 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    mla.mla_absorb_out(fin, n_rows, wt, H, h0, h1, out, Hs * 128)
+    torch.cuda.synchronize()
+    got = f64(out)
+    for hs, h in enumerate(range(h0, h1)):
+        ro, rl = orc.attend_absorbed(orc.bf16_to_f64(q[rid, h]), L[:NK], Wf, H, h, scale)
+        check_out(got[:, hs * 128:(hs + 1) * 128], ro, what=f"out head {h}")
+        check_lse(f64(finl)[hs * n_rows:(hs + 1) * n_rows, 0], rl,
+                  tol=LSE_FEW_KEYS if NK < FEW_KEYS else 1e-3, what=f"lse head {h}")
+
+
 # ---------------------------------------------------------------- head partition merge
 
 def test_head_partition_merge():

@@ -92,14 +92,19 @@ def test_ragged_multichunk_fp8():
 
 # key splits: one piece per chunk (5 pieces, odd merge tree), four pieces per
 # chunk with a ragged last one, and the whole document as a single piece
-@pytest.mark.parametrize("split,chunk", [(2048, 256), (64, 256), (4096, 2048)])
-def test_reuse_small_all_outputs(split, chunk):
+# split / split_local: keys per Global / Local piece (one piece per chunk,
+# four per chunk with a ragged last one, the whole document as one piece)
+@pytest.mark.parametrize("split,split_local,chunk,local", [
+    (2048, 8192, 256, "absorbed"), (64, 64, 256, "absorbed"), (64, 128, 256, "absorbed"),
+    (4096, 8192, 2048, "absorbed"), (2048, 2048, 256, "decompressed"), (64, 64, 256, "decompressed"),
+    (4096, 4096, 2048, "decompressed")])
+def test_reuse_small_all_outputs(split, split_local, chunk, local):
     require_gpu()
-    say(f"reuse small split={split} chunk={chunk}")
+    say(f"reuse small split={split}/{split_local} chunk={chunk} local={local}")
     prob = mi.make_reuse_problem(H=8, n_local=7, L=1024 + 64, T=300, delta=4096, P=9,
                                  d_mid=256, d_model=384, chunk=chunk, seed=73)
-    pre = ReusePrefill(prob, split=split)
-    say(f"  {pre.n_pieces} pieces")
+    pre = ReusePrefill(prob, split=split, local_path=local, split_local=split_local)
+    say(f"  {pre.n_pieces} / {pre.n_pieces_L} pieces")
     y = pre.run()
     torch.cuda.synchronize()
     ref = orc.reuse_reference(prob)
@@ -155,12 +160,13 @@ def test_full_size_workload_sampled(k):
         assert worst[1] <= FP8_REL_L2
 
 
-def test_full_size_reuse_sampled():
+@pytest.mark.parametrize("local", ["absorbed", "decompressed"])
+def test_full_size_reuse_sampled(local):
     require_gpu()
-    say("config 5 full size")
+    say(f"config 5 full size, Local rows {local}")
     t0 = time.time()
     prob = mi.make_config(5)
-    pre = ReusePrefill(prob)
+    pre = ReusePrefill(prob, local_path=local)
     y = pre.run()
     torch.cuda.synchronize()
     say(f"  gpu done {time.time() - t0:.1f}s")
