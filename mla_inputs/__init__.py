@@ -116,6 +116,17 @@ class Problem:
     WaL: Optional[np.ndarray] = None         # bf16 bits [HL*128, d_mid]
     WaG: Optional[np.ndarray] = None         # bf16 bits [HG*128, d_mid]
     Wb: Optional[np.ndarray] = None          # bf16 bits [d_mid, d_model]
+    # several documents (each its own pool and block table, canonical
+    # positions 0..L_d-1, placed at request offset delta_d); None = the one
+    # document given by pool / block_table / ctx_len[0] / delta
+    docs: Optional[list] = None
+
+    def documents(self) -> list:
+        """[dict(pool, block_table, L, delta)] of a reuse problem."""
+        if self.docs is not None:
+            return self.docs
+        return [dict(pool=self.pool, block_table=self.block_table, L=int(self.ctx_len[0]),
+                     delta=int(self.delta))]
 
     @property
     def B(self) -> int:
@@ -227,6 +238,40 @@ def make_reuse_problem(H=64, n_local=56, L=262144, T=512, delta=4096, P=64,
                    scale=float(1.0 / np.sqrt(D_QK)), seed=seed, delta=int(delta),
                    n_local=HL, art_out=art_out, art_lse=art_lse, prot_rows=prot,
                    WaL=WaL, WaG=WaG, Wb=Wb)
+
+
+def make_multidoc_problem(H=8, n_local=7, doc_lens=(512, 192, 1088), T=100, delta=4096, P=7,
+                          d_mid=256, d_model=256, chunk=256, seed=6, name="multidoc") -> Problem:
+    """Segmented reuse: documents d = 0..n-1, each built at canonical
+    positions 0..L_d-1 in a pool of its own, placed one after another in the
+    request (document d at offset delta_d = delta + L_0 + ... + L_{d-1});
+    T query rows at request positions delta_{n-1} + L_{n-1} + i (their rope
+    part is given rotated there). Artifact, protected rows and projections
+    as in make_reuse_problem."""
+    rng = np.random.default_rng(seed)
+    docs = []
+    off = int(delta)
+    for L in doc_lens:
+        pool, bt = _build_pool(rng, np.array([L], dtype=np.int64), "bf16")
+        docs.append(dict(pool=pool, block_table=bt, L=int(L), delta=off))
+        off += int(L)
+    Ltot = int(sum(doc_lens))
+    q = _normal_bf16(rng, (T, H, D_QK))
+    W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
+    HL, HG = n_local, H - n_local
+    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / Ltot)))
+    art_lse = (np.log(Ltot) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
+    prot = np.sort(rng.choice(T, size=P, replace=False)).astype(np.int32)
+    WaL = _normal_bf16(rng, (HL * D_V, d_mid), std=1.0 / np.sqrt(HL * D_V))
+    WaG = _normal_bf16(rng, (HG * D_V, d_mid), std=1.0 / np.sqrt(HG * D_V))
+    Wb = _normal_bf16(rng, (d_mid, d_model), std=1.0 / np.sqrt(d_mid))
+    return Problem(name=name, H=H, ctx_len=np.array([Ltot], dtype=np.int64),
+                   ext_len=np.array([0], dtype=np.int64), chunk=chunk, cache_dtype="bf16",
+                   pool=docs[0]["pool"], block_table=docs[0]["block_table"],
+                   ext_latent=np.zeros((0, D_LAT), dtype=np.uint16), q=q, W=W,
+                   scale=float(1.0 / np.sqrt(D_QK)), seed=seed, delta=int(delta),
+                   n_local=HL, art_out=art_out, art_lse=art_lse, prot_rows=prot,
+                   WaL=WaL, WaG=WaG, Wb=Wb, docs=docs)
 
 
 def ragged_lengths(rng, B=16, ctx_lo=1024, ctx_hi=32768, ext_lo=256, ext_hi=2048):

@@ -264,18 +264,27 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) my[i4 * 64 + lane] = f32x4{S[4 * i4], S[4 * i4 + 1], S[4 * i4 + 2], S[4 * i4 + 3]};
     __syncthreads();
-    // the group's four partial sums, added in quarter order
+    // the group's four partial sums, added in quarter order (this
+    // wavefront's own term from its registers, the others from LDS), so the
+    // four quarters hold bit-identical scores
+    f32x16 St;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+    for (int i = 0; i < 16; ++i) St[i] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const f32x4* ps = reinterpret_cast<const f32x4*>(spart + (rg * 4 + q) * 4096);
+      if (q == qd) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v = ps[i4 * 64 + lane];
-        S[4 * i4] += v.x; S[4 * i4 + 1] += v.y; S[4 * i4 + 2] += v.z; S[4 * i4 + 3] += v.w;
+        for (int i = 0; i < 16; ++i) St[i] += S[i];
+      } else {
+        const f32x4* ps = reinterpret_cast<const f32x4*>(spart + (rg * 4 + q) * 4096);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 v = ps[i4 * 64 + lane];
+          St[4 * i4] += v.x; St[4 * i4 + 1] += v.y; St[4 * i4 + 2] += v.z; St[4 * i4 + 3] += v.w;
+        }
       }
     }
+    S = St;
     // keys past the piece end
     if (kt0 + kAT > n_k) {
 #pragma unroll

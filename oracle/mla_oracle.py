@@ -481,35 +481,49 @@ def head_partition_merge(O_L: np.ndarray, O_G: np.ndarray, WaL: np.ndarray,
     return z @ Wb
 
 
+def _doc_keys_at_request_positions(prob):
+    """All documents' keys at their request positions: document d's
+    canonical latents with the rope part rotated by +delta_d (direct
+    placement), concatenated in document order. Returns (c_kv [N, 512],
+    k_rope [N, 64]) in fp64."""
+    ckv, kr = [], []
+    for d in prob.documents():
+        L = int(d["L"])
+        lat = bf16_to_f64(gather_bf16_bits(d["pool"], d["block_table"], 0, 0, L))
+        ckv.append(lat[:, :D_C])
+        kr.append(rope_rotate(lat[:, D_C:], float(d["delta"]), prob.rope_base))
+    return np.concatenate(ckv), np.concatenate(kr)
+
+
 def reuse_reference(prob, global_rows: Optional[np.ndarray] = None):
     """Head-partitioned reuse prefill by definition ([REDKNOT] Abstract,
     sections 2-3; readings R20-R23). Direct placement: each canonical
-    document key's rope part is rotated by +delta, which puts the document
-    at request positions delta..delta+L-1 where the queries' rope parts
-    already are; no query rotation. Global heads attend all rows over the
-    whole document; Local heads recompute only protected rows; the result is
-    Equation 4 over artifact rows with protected rows replaced.
+    document key's rope part is rotated by +delta of its document, which
+    puts the document at request positions delta..delta+L-1 where the
+    queries' rope parts already are; no query rotation. With several
+    documents ([REDKNOT] section 2, segmented merging) the keys of all of
+    them, each at its own offset, form one softmax. Global heads attend all
+    rows over all keys; Local heads recompute only protected rows; the result
+    is Equation 4 over artifact rows with protected rows replaced.
 
     Returns dict with O_G [T,HG,128], lse_G, rec [P,HL,128], rec_lse, y [T,d_model].
     """
     H, HL = prob.H, prob.n_local
-    L = int(prob.ctx_len[0])
     T = prob.T
     W = bf16_to_f64(prob.W)
-    lat = context_latent_f64(prob, 0, 0, L)
-    k_rope = rope_rotate(lat[:, D_C:], float(prob.delta), prob.rope_base)
+    c_kv, k_rope = _doc_keys_at_request_positions(prob)
     q = bf16_to_f64(prob.q)
     prot = np.asarray(prob.prot_rows, dtype=np.int64)
     rows_g = np.arange(T) if global_rows is None else np.asarray(global_rows)
     O_G = np.zeros((len(rows_g), H - HL, D_V))
     l_G = np.zeros((len(rows_g), H - HL))
     for gi, h in enumerate(range(HL, H)):
-        kn, v = decompress_head(lat[:, :D_C], W, H, h)
+        kn, v = decompress_head(c_kv, W, H, h)
         O_G[:, gi], l_G[:, gi] = attend(q[rows_g, h], kn, k_rope, v, prob.scale)
     rec = np.zeros((len(prot), HL, D_V))
     rec_l = np.zeros((len(prot), HL))
     for h in range(HL):
-        kn, v = decompress_head(lat[:, :D_C], W, H, h)
+        kn, v = decompress_head(c_kv, W, H, h)
         rec[:, h], rec_l[:, h] = attend(q[prot, h], kn, k_rope, v, prob.scale)
     res = dict(O_G=O_G, lse_G=l_G, rec=rec, rec_lse=rec_l)
     if global_rows is None:
@@ -517,6 +531,29 @@ def reuse_reference(prob, global_rows: Optional[np.ndarray] = None):
         res["y"] = head_partition_merge(O_L, O_G, bf16_to_f64(prob.WaL),
                                         bf16_to_f64(prob.WaG), bf16_to_f64(prob.Wb))
     return res
+
+
+def segmented_attention(prob, h: int, rows: np.ndarray):
+    """The runtime form of multi-document reuse ([REDKNOT] section 2: online
+    relocation rotates queries into each document's canonical frame, attends
+    to the canonical latents, and the segment statistics are merged): for
+    each document d, q_rope rotated by -delta_d attends to d's canonical keys
+    (rope at canonical positions); the per-document (out, lse) are merged
+    with merge_states. Equal to the direct placement of reuse_reference by
+    RoPE's relative-position property and the merge identity."""
+    W = bf16_to_f64(prob.W)
+    q = bf16_to_f64(prob.q)[rows, h]
+    out = np.zeros((len(rows), D_V))
+    lse = np.full(len(rows), NEG_INF)
+    for d in prob.documents():
+        L = int(d["L"])
+        lat = bf16_to_f64(gather_bf16_bits(d["pool"], d["block_table"], 0, 0, L))
+        qd = q.copy()
+        qd[:, D_NOPE:] = relocate_q(q[:, D_NOPE:], int(d["delta"]), prob.rope_base)
+        kn, v = decompress_head(lat[:, :D_C], W, prob.H, h)
+        o, l = attend(qd, kn, lat[:, D_C:], v, prob.scale)
+        out, lse = merge_states(out, lse, o, l)
+    return out, lse
 
 
 # --------------------------------------------------------------------------

@@ -2,6 +2,7 @@
 other than itself (brute force, closed forms, identities the pages state,
 library routines, page-printed values), chosen so that a dropped term, a
 wrong sign, index or operand order fails at least one of them."""
+import dataclasses
 import math
 
 import numpy as np
@@ -562,3 +563,40 @@ def test_cache_append_expected_places_records_and_touches_nothing_else():
         written[b, 32768 + sl * 128:32768 + (sl + 1) * 128] = True
         written[b, 40960 + sl * 4:40960 + (sl + 1) * 4] = True
     assert np.all(out8[~written] == 0xA5)
+
+
+# ---------------------------------------------------------------- multi-document (segmented) reuse
+
+def test_segmented_runtime_form_equals_direct_placement():
+    """Per-document relocation + canonical attention + LSE merge (the runtime
+    form) equals one softmax over all documents' keys at their request
+    positions (the definition), for Global and protected Local rows."""
+    prob = mi.make_multidoc_problem(H=4, n_local=3, doc_lens=(128, 64, 192), T=12, P=3, seed=93,
+                                    d_mid=128, d_model=128)
+    ref = orc.reuse_reference(prob)
+    rows = np.arange(prob.T)
+    o, l = orc.segmented_attention(prob, 3, rows)
+    assert np.allclose(o, ref["O_G"][:, 0], rtol=1e-10, atol=1e-12)
+    assert np.allclose(l, ref["lse_G"][:, 0], rtol=0, atol=1e-10)
+    prot = np.asarray(prob.prot_rows)
+    for h in range(3):
+        o, l = orc.segmented_attention(prob, h, prot)
+        assert np.allclose(o, ref["rec"][:, h], rtol=1e-10, atol=1e-12)
+        assert np.allclose(l, ref["rec_lse"][:, h], rtol=0, atol=1e-10)
+
+
+def test_each_document_uses_its_own_offset():
+    """A stored k_rope is the key rotated at its canonical position inside its
+    own document, so each document must be placed by its own delta_d: moving
+    one document by one position, or placing every document at the first
+    one's offset, changes the result far beyond the parity tolerance."""
+    prob = mi.make_multidoc_problem(H=4, n_local=3, doc_lens=(64, 128, 64), T=10, P=2, seed=94,
+                                    d_mid=128, d_model=128)
+    base = orc.reuse_reference(prob)["O_G"]
+    docs = [dict(d) for d in prob.documents()]
+    docs[1]["delta"] += 1
+    moved = orc.reuse_reference(dataclasses.replace(prob, docs=docs))["O_G"]
+    same = [dict(d, delta=prob.documents()[0]["delta"]) for d in prob.documents()]
+    flat = orc.reuse_reference(dataclasses.replace(prob, docs=same))["O_G"]
+    for other in (moved, flat):
+        assert np.linalg.norm(other - base) / np.linalg.norm(base) > 0.02
