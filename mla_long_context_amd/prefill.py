@@ -208,14 +208,17 @@ class ChunkedPrefill:
 
 
 class ReusePrefill:
-    """Head-partitioned reuse over one document at canonical positions.
+    """Head-partitioned reuse over one or more documents stored at canonical
+    positions. Each document is visited in turn: the queries are relocated by
+    its request offset (and re-absorbed for the Local rows), then its chunks
+    run as below; the pieces of all documents join one merge tree.
 
     Local heads (protected rows only) take the absorbed form by default
     (local_path="absorbed"): W_UK is folded into their queries and they
     attend to the gathered latent directly, so only the Global heads are
     decompressed; local_path="decompressed" decompresses every head instead.
 
-    Per document chunk: gather, decompression of every head, then attention
+    Per document chunk: gather, decompression of the heads that need it, then attention
     of the Global heads (all query rows) and of the Local heads (protected
     rows only). There are few query rows, so one (head, row tile) per
     workgroup would leave most of the GPU idle: every chunk's keys are split
@@ -240,13 +243,17 @@ class ReusePrefill:
         # the absorbed Local rows fill the GPU with fewer, longer pieces (56
         # row tiles per piece at 56 heads x 64 rows): fewer partial states
         self.split_L = max(64, int(split_local) // 64 * 64) if local_path == "absorbed" else self.split
-        self.Ldoc = int(prob.ctx_len[0])
+        # documents: each its own pool and block table, canonical positions,
+        # request offset delta (RedKnot-MLA section 2: segmented reuse; the
+        # per-document states merge like the pieces of one document)
+        self.docs = [dict(pool=_bf16(d["pool"], device), bt=_i32(d["block_table"], device),
+                          num_blocks=int(d["pool"].shape[0]), L=int(d["L"]), delta=int(d["delta"]))
+                     for d in prob.documents()]
+        self.Ldoc = sum(d["L"] for d in self.docs)
         self.T = prob.T
         self.P = int(len(prob.prot_rows))
         self.d_mid = prob.WaL.shape[1]
         self.d_model = prob.Wb.shape[1]
-        self.pool = upload_pool(prob, device)
-        self.bt = _i32(prob.block_table, device)
         self.q = _bf16(prob.q, device)
         self.q_rel = torch.empty_like(self.q)
         self.w_t = pack_weight(prob.W, device)
@@ -262,28 +269,30 @@ class ReusePrefill:
         # chunk plan; piece i of the document is split (chunk c, piece j)
         self.chunks = []
         n_pieces = n_pieces_L = 0
-        for s0 in range(0, self.Ldoc, self.S):
-            n = min(self.S, self.Ldoc - s0)
+        for di, doc in enumerate(self.docs):
+          for s0 in range(0, doc["L"], self.S):
+            n = min(self.S, doc["L"] - s0)
             bounds = list(range(0, n, self.split)) + [n]
             k = len(bounds) - 1
             bounds_L = list(range(0, n, self.split_L)) + [n]
             kL = len(bounds_L) - 1
             self.chunks.append(dict(
-                start=_i32([s0], device), len=_i32([n], device), cu=_i32([0, n], device), n=n,
+                doc=di, start=_i32([s0], device), len=_i32([n], device), cu=_i32([0, n], device), n=n,
                 pieces=k, first=n_pieces, cu_k=_i32(bounds, device),
                 pieces_L=kL, first_L=n_pieces_L, cu_kL=_i32(bounds_L, device),
                 cu_qG=_i32(np.arange(k + 1) * T, device), rid_G=_i32(np.tile(np.arange(T), k), device),
                 cu_qL=_i32(np.arange(kL + 1) * P, device), rid_L=_i32(np.tile(prot, kL), device)))
             n_pieces += k
             n_pieces_L += kL
+        self.max_chunk = max([c["n"] for c in self.chunks] + [1])
         self.n_pieces = n_pieces
         self.n_pieces_L = n_pieces_L
-        S = self.S
         HL, HG = self.HL, self.HG
         # heads whose k_nope / v are decompressed: all of them, or only the
         # Global ones when the Local rows take the absorbed form
         self.kv_h0 = HL if self.absorbed else 0
         n_kv = H - self.kv_h0
+        S = self.max_chunk
         self.lat_ws = torch.empty((S, D_LAT), dtype=torch.bfloat16, device=device)
         self.k_ws = torch.empty((max(n_kv, 1), S, D_V), dtype=torch.bfloat16, device=device)
         self.v_ws = torch.empty((max(n_kv, 1), S, D_V), dtype=torch.bfloat16, device=device)
@@ -374,15 +383,23 @@ class ReusePrefill:
     def run(self, stream=None, timer=None):
         p = self.prob
         H, HL, HG, T, P = self.H, self.HL, self.HG, self.T, self.P
-        with _span(timer, "relocate"):
-            L.mla_rope_relocate_q(self.q, self.q_rel, H * D_QK, T, H, p.delta, p.rope_base,
-                                  L.ROPE_INTERLEAVED, stream)
-        if self.absorbed and HL > 0 and P > 0:
-            with _span(timer, "absorb"):
-                L.mla_absorb_q(self.q_rel, H * D_QK, H, 0, HL, self.prot, P, self.W, H, self.q_abs, stream)
+        cur_doc = -1
         for ch in self.chunks:
+            doc = self.docs[ch["doc"]]
+            if ch["doc"] != cur_doc:
+                # queries into this document's canonical frame (and, for the
+                # absorbed Local rows, their absorbed form from the relocated
+                # rope part)
+                cur_doc = ch["doc"]
+                with _span(timer, "relocate"):
+                    L.mla_rope_relocate_q(self.q, self.q_rel, H * D_QK, T, H, doc["delta"], p.rope_base,
+                                          L.ROPE_INTERLEAVED, stream)
+                if self.absorbed and HL > 0 and P > 0:
+                    with _span(timer, "absorb"):
+                        L.mla_absorb_q(self.q_rel, H * D_QK, H, 0, HL, self.prot, P, self.W, H, self.q_abs,
+                                       stream)
             with _span(timer, "gather"):
-                L.mla_gather_context(self.pool, L.DTYPE_BF16, p.num_blocks, self.bt, self.bt.shape[1],
+                L.mla_gather_context(doc["pool"], L.DTYPE_BF16, doc["num_blocks"], doc["bt"], doc["bt"].shape[1],
                                      ch["start"], ch["len"], ch["cu"], 1, ch["n"], self.lat_ws,
                                      self.dev_status, stream)
             if self.kv_h0 < H:
@@ -451,7 +468,7 @@ class ReusePrefill:
             local_attn_flops=local,
             absorb_flops=absorb,
             proj_flops=2 * T * ((HL + HG) * 128 * self.d_mid + self.d_mid * self.d_model),
-            relocate_bytes=T * H * 768,   # out of place: q head row read (384 B) + written
+            relocate_bytes=T * H * 768 * len(self.docs),   # per document, out of place: q head row read + written
             merge_bytes=int(merge_bytes),
             gather_tokens=Ld, gather_bytes=Ld * 2304, new_tokens=T, ctx_tokens=Ld,
         )

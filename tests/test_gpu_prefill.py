@@ -116,6 +116,45 @@ def test_reuse_small_all_outputs(split, split_local, chunk, local):
     say(f"  y max-abs {ma:.2e} rel-L2 {r:.2e}")
 
 
+# several documents, each in a pool of its own at canonical positions and
+# placed back to back in the request: a two-chunk, a short ragged one-chunk
+# (192 keys) and a five-chunk document with a ragged tail; chunk 2048 makes
+# every document a single chunk
+@pytest.mark.parametrize("split,split_local,chunk,local", [
+    (64, 128, 256, "absorbed"), (2048, 8192, 256, "absorbed"), (4096, 8192, 2048, "absorbed"),
+    (64, 64, 256, "decompressed"), (2048, 2048, 2048, "decompressed")])
+def test_multidoc_reuse_all_outputs(split, split_local, chunk, local):
+    require_gpu()
+    say(f"multi-document reuse split={split}/{split_local} chunk={chunk} local={local}")
+    prob = mi.make_multidoc_problem(chunk=chunk)
+    pre = ReusePrefill(prob, split=split, local_path=local, split_local=split_local)
+    say(f"  {len(pre.docs)} documents, {len(pre.chunks)} chunks, {pre.n_pieces} / {pre.n_pieces_L} pieces")
+    y = pre.run()
+    torch.cuda.synchronize()
+    ref = orc.reuse_reference(prob)
+    check_out(f64(pre.glob_out), ref["O_G"], what="O_G")
+    check_lse(f64(pre.lse_G), ref["lse_G"], what="lse_G")
+    check_out(f64(pre.rec_out), ref["rec"], what="rec")
+    check_lse(f64(pre.lse_L), ref["rec_lse"], what="rec_lse")
+    ma, r = check_out(f64(y), ref["y"], what="y")
+    say(f"  y max-abs {ma:.2e} rel-L2 {r:.2e}")
+
+
+def test_multidoc_offsets_are_per_document():
+    """Relocating every document by the first one's offset must miss the
+    oracle: each document's queries are rotated by its own offset."""
+    require_gpu()
+    prob = mi.make_multidoc_problem(chunk=256)
+    ref = orc.reuse_reference(prob)
+    for d in prob.docs[1:]:
+        d["delta"] = prob.docs[0]["delta"]
+    pre = ReusePrefill(prob)
+    pre.run()
+    torch.cuda.synchronize()
+    from gpu_util import rel_l2
+    assert rel_l2(f64(pre.glob_out), ref["O_G"]) > 0.05
+
+
 def test_reuse_without_relocation_is_caught():
     """Relocating by the wrong offset shifts every relative position; the
     Global-head outputs must then miss the oracle by far more than the bar."""
