@@ -18,6 +18,8 @@ same number of steps, since events between launches add fences to the step),
 and the fp64 CPU oracle timed on a bounded sample on this host.
 
     python bench.py --workload {1..5}   # the other standard workloads
+    python bench.py --append            # the cache write path
+    python bench.py --artifact          # the offline Local-head artifact build
 """
 from __future__ import annotations
 
@@ -242,6 +244,105 @@ def bench_append(args, torch, mla, mla_inputs):
     print(json.dumps(res))
 
 
+def cpu_baseline_artifact(ap, budget_s=15.0):
+    """The fp64 oracle as it stands on the artifact build: Local heads one at
+    a time (decompression of the whole document for that head, then 1024
+    document rows spread over it, each over its causal prefix), until about
+    budget_s seconds are spent."""
+    import numpy as np
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    t_dec = time.time()
+    lat = np.array([orc.bf16_to_f64(ap.pool[ap.block_table[0, t // 64], t % 64]) for t in range(ap.L)])
+    W = orc.bf16_to_f64(ap.W)
+    rows = np.linspace(0, ap.R - 1, 1024).astype(np.int64)
+    q = orc.bf16_to_f64(ap.q[rows])
+    t0 = time.time()
+    t_dec = t0 - t_dec
+    heads = 0
+    while heads < ap.n_local and (heads == 0 or time.time() - t0 < budget_s):
+        orc.build_artifact(lat, q, W, ap.H, ap.n_local, ap.scale, ap.doc_rows, row_ids=rows, heads=[heads])
+        heads += 1
+    dt = time.time() - t0
+    pos = orc.artifact_row_positions(ap.L, rows, ap.doc_rows)
+    pairs = int(np.minimum(pos + 1, ap.L).sum())
+    flops = heads * (2 * 512 * 256 * ap.L + 640 * pairs)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"Local heads 0..{heads - 1}: decompression of the {ap.L}-token document and 1024 "
+                      f"document rows spread over it (causal prefixes), {flops / 1e9:.1f} GFLOP fp64 in "
+                      f"{dt:.1f} s (plus {t_dec:.1f} s decoding once, not counted); NumPy/OpenBLAS with "
+                      f"{blas_threads} BLAS threads"}
+
+
+def bench_artifact(args, torch, mla, mla_inputs):
+    """The offline Local-head artifact build of one document (ArtifactBuilder):
+    gather, decompression of the 56 Local heads, causal attention of every
+    document row; TFLOP/s of algorithmic work."""
+    from mla_long_context_amd.prefill import ArtifactBuilder
+    t_gen = time.time()
+    ap = mla_inputs.make_artifact_config()
+    b = ArtifactBuilder.from_problem(ap)
+    work = b.work()
+    print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.ARTIFACT_CONFIG_NAME}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        b.run()
+    torch.cuda.synchronize()
+    assert int(b.dev_status.item()) == 0
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        b.run()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / max(args.steps, 1)
+    timer = KernelTimer()
+    for _ in range(args.steps):
+        b.run(timer=timer)
+    kern = timer.summary()
+    flops = work["dec_flops"] + work["attn_flops"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    per_kind = {"decompress": work["dec_flops"], "attn_causal": work["causal_attn_flops"],
+                "attn_full": work["full_attn_flops"]}
+    kernels = {}
+    for name, (c, tot) in kern.items():
+        entry = {"launches_per_step": c / args.steps, "avg_ms": round(tot / c, 4),
+                 "ms_per_step": round(tot / args.steps, 4)}
+        if name in per_kind:
+            entry["tflops"] = round(per_kind[name] / (tot / args.steps * 1e-3) / 1e12, 2)
+        else:
+            entry["gbs"] = round(work["gather_bytes"] / (tot / args.steps * 1e-3) / 1e9, 1)
+        kernels[name] = entry
+    dom = max((k for k in kern if k in per_kind), key=lambda k: kern[k][1])
+    c_ms = kern[dom][1] / kern[dom][0]
+    c_unit = per_kind[dom] / (kern[dom][0] / args.steps)
+    achieved = c_unit / (c_ms * 1e-3) / 1e12
+    kname = {"decompress": "mla_decompress", "attn_causal": "mla_prefill_attn (causal, document rows)",
+             "attn_full": "mla_prefill_attn (rows past the chunk)"}[dom]
+    res = {"metric": "MLA-Off artifact build TFLOP/s (offline Local-head pass)", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": mla_inputs.ARTIFACT_CONFIG_NAME, "heads": ap.H, "local_heads": ap.n_local,
+                      "document_tokens": ap.L, "rows": ap.R, "chunk": b.S},
+           "algorithmic_flop_per_step": flops,
+           "document_tokens_per_s": round(ap.L / (ms * 1e-3), 1),
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": kname, "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)},
+           "kernels": kernels,
+           "kernel_timing": "a second pass of the same number of steps with HIP events around every launch"}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_artifact(ap)
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +358,9 @@ def main():
     ap.add_argument("--append", action="store_true",
                     help="time the cache write path instead: every context token of the workload "
                          "appended into its blocks (fp8-quantised for the fp8 workload)")
+    ap.add_argument("--artifact", action="store_true",
+                    help="time the offline Local-head artifact build instead (65536-token document, "
+                         "56 Local heads of 64, every document row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
@@ -293,6 +397,10 @@ def main():
 
     if args.append:
         bench_append(args, torch, mla, mla_inputs)
+        return
+    if args.artifact:
+        mla.load()
+        bench_artifact(args, torch, mla, mla_inputs)
         return
 
     mla.load()                       # fails loudly if libmla.so is missing

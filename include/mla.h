@@ -322,6 +322,73 @@ int mla_head_partition_merge(const void* art_out, const void* rec_out,
                              const void* wa_t, const void* wb_t, int T, int HL, int HG,
                              int d_mid, int d_model, void* z, void* y, void* stream);
 
+/*
+ * Validation of an offline Local-head artifact before it is reused
+ * ([REDKNOT] section 2, "Canonical offline artifacts": each document is
+ * processed alone at canonical position zero and its Local-head results are
+ * kept; reuse falls back to full recomputation when validation finds missing
+ * layers, a token or profile mismatch or a stale generation). The binding of
+ * tensor-parallel geometry and the agreement between ranks are not checked
+ * here (one device). Host-only functions: no device memory, no stream.
+ *
+ * mla_artifact_meta describes an artifact (as built) or what a request
+ * needs (as served). All fields are plain values:
+ *   generation   version of the document's content the artifact was built
+ *                from; the request's current version must be equal;
+ *   token_hash   mla_token_hash of the document's token ids;
+ *   n_tokens     document length in tokens;
+ *   n_heads, n_local
+ *                logical heads and Local heads (heads 0..n_local-1);
+ *   d_c, d_rope, d_nope, d_v
+ *                latent, rope, per-head key and value widths;
+ *   rope_base    RoPE base of the query/key rotation;
+ *   n_layers     reusable layers of the profile (<= 64);
+ *   layer_mask   bit l set: layer l's results are present. The request's
+ *                value lists the layers it needs.
+ */
+typedef struct mla_artifact_meta {
+  uint64_t generation;
+  uint64_t token_hash;
+  int64_t n_tokens;
+  int32_t n_heads;
+  int32_t n_local;
+  int32_t d_c;
+  int32_t d_rope;
+  int32_t d_nope;
+  int32_t d_v;
+  double rope_base;
+  int32_t n_layers;
+  int32_t reserved;
+  uint64_t layer_mask;
+} mla_artifact_meta;
+
+typedef enum {
+  MLA_ARTIFACT_VALID = 0,
+  MLA_ARTIFACT_MISSING_LAYER = 1,    /* a needed layer is absent            */
+  MLA_ARTIFACT_TOKEN_MISMATCH = 2,   /* length or token hash differs        */
+  MLA_ARTIFACT_PROFILE_MISMATCH = 3, /* heads, Local split, widths, rope, layer count */
+  MLA_ARTIFACT_STALE = 4             /* generation differs                  */
+} mla_artifact_reason;
+
+/*
+ * mla_token_hash -- 64-bit FNV-1a (Fowler-Noll-Vo, offset basis
+ * 0xcbf29ce484222325, prime 0x100000001b3) over the n token ids, each taken
+ * as its 4 little-endian bytes. tokens: host int32 [n] (NULL allowed when
+ * n == 0). Returns the hash (the offset basis for n == 0).
+ */
+uint64_t mla_token_hash(const int32_t* tokens, int64_t n);
+
+/*
+ * mla_artifact_check -- compares an artifact's description with the
+ * request's and writes the first failing check to *reason, in this order:
+ * missing layer, token mismatch, profile mismatch, stale generation; else
+ * MLA_ARTIFACT_VALID. Returns MLA_OK, or MLA_ERR_INVALID_ARG for a null
+ * pointer or a layer count outside 0..64 (then *reason is not written).
+ * The caller falls back to full recomputation of the Local heads on any
+ * reason other than MLA_ARTIFACT_VALID, before launching the reuse path.
+ */
+int mla_artifact_check(const mla_artifact_meta* artifact, const mla_artifact_meta* request, int* reason);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,28 @@ def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarra
     return f32_to_bf16_bits(x)
 
 
+def _normal_bf16_blocks(seed, shape, std: float = 1.0, block: int = 1 << 23) -> np.ndarray:
+    """N(0, std^2) bf16 bits for large arrays: the flat array is cut into
+    fixed blocks, block i drawn from child i of SeedSequence(seed), so the
+    values do not depend on how many threads fill them."""
+    import concurrent.futures as cf
+    import os
+    n = int(np.prod(shape))
+    kids = np.random.SeedSequence(seed).spawn(max(1, (n + block - 1) // block))
+    out = np.empty(n, dtype=np.uint16)
+
+    def fill(i):
+        m = min(block, n - i * block)
+        x = np.random.default_rng(kids[i]).standard_normal(size=m, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[i * block:i * block + m] = f32_to_bf16_bits(x)
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(len(kids))))
+    return out.reshape(shape)
+
+
 def _bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
@@ -272,6 +294,72 @@ def make_multidoc_problem(H=8, n_local=7, doc_lens=(512, 192, 1088), T=100, delt
                    scale=float(1.0 / np.sqrt(D_QK)), seed=seed, delta=int(delta),
                    n_local=HL, art_out=art_out, art_lse=art_lse, prot_rows=prot,
                    WaL=WaL, WaG=WaG, Wb=Wb, docs=docs)
+
+
+@dataclasses.dataclass
+class ArtifactProblem:
+    """Inputs of an offline Local-head artifact build: one document at
+    canonical positions 0..L-1 in a pool of its own, the query rows of the
+    artifact with their rope parts at canonical positions (document rows
+    first when doc_rows, then rows after the document), kv_b_proj, and the
+    document's token ids and content generation for its description."""
+    name: str
+    H: int
+    n_local: int
+    L: int
+    doc_rows: bool
+    pool: np.ndarray             # bf16 bits [NB, 64, 576]
+    block_table: np.ndarray      # int32 [1, max_blocks]
+    q: np.ndarray                # bf16 bits [R, H, 192]
+    W: np.ndarray                # bf16 bits [512, H*256]
+    scale: float
+    tokens: np.ndarray           # int32 [L] token ids
+    generation: int
+    seed: int
+    chunk: int
+    rope_base: float = 10000.0
+
+    @property
+    def R(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.pool.shape[0])
+
+
+def make_artifact_problem(H=8, n_local=7, L=1088, extra_rows=50, doc_rows=True, chunk=256, seed=7,
+                          generation=3, vocab=129280, name="artifact") -> ArtifactProblem:
+    """A document to build an artifact for: L tokens in a shuffled pool,
+    R = (L if doc_rows else 0) + extra_rows query rows (N(0,1), rope part at
+    the rows' canonical positions; drawn from SeedSequence([seed, 1]) in
+    blocks), kv_b_proj N(0, 1/512), token ids uniform in [0, vocab)."""
+    rng = np.random.default_rng(seed)
+    pool, bt = _build_pool(rng, np.array([L], dtype=np.int64), "bf16")
+    R = (L if doc_rows else 0) + int(extra_rows)
+    # the query rows of a long document are large: drawn in parallel blocks
+    q = _normal_bf16_blocks([seed, 1], (R, H, D_QK))
+    W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
+    tokens = rng.integers(0, vocab, size=L).astype(np.int32)
+    return ArtifactProblem(name=name, H=H, n_local=n_local, L=int(L), doc_rows=bool(doc_rows), pool=pool,
+                           block_table=bt, q=q, W=W, scale=float(1.0 / np.sqrt(D_QK)), tokens=tokens,
+                           generation=int(generation), seed=seed, chunk=int(chunk))
+
+
+ARTIFACT_CONFIG_NAME = ("MLA-Off artifact build: one 65536-token document at canonical position zero, "
+                        "64 heads (56 Local built), every document row causal, one chunk")
+
+
+def make_artifact_config() -> ArtifactProblem:
+    """The offline build measured by the benchmark: the reuse geometry's
+    heads (64, Local 0..55), a 65536-token document, every document row."""
+    return make_artifact_problem(H=64, n_local=56, L=65536, extra_rows=0, doc_rows=True, chunk=65536, seed=8,
+                                 name="artifact")
+
+
+def document_tokens(L: int, seed: int, vocab: int = 129280) -> np.ndarray:
+    """Seeded token ids of a document (int32, uniform in [0, vocab))."""
+    return np.random.default_rng(seed).integers(0, vocab, size=L).astype(np.int32)
 
 
 def ragged_lengths(rng, B=16, ctx_lo=1024, ctx_hi=32768, ext_lo=256, ext_hi=2048):

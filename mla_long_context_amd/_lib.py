@@ -30,8 +30,27 @@ EXPORTS = (
     "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_absorb_q",
     "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states",
     "mla_rope_relocate_q",
-    "mla_head_partition_merge",
+    "mla_head_partition_merge", "mla_token_hash", "mla_artifact_check",
 )
+
+# reasons written by mla_artifact_check
+ARTIFACT_VALID = 0
+ARTIFACT_MISSING_LAYER = 1
+ARTIFACT_TOKEN_MISMATCH = 2
+ARTIFACT_PROFILE_MISMATCH = 3
+ARTIFACT_STALE = 4
+ARTIFACT_REASONS = {0: "valid", 1: "missing layer", 2: "token mismatch", 3: "profile mismatch",
+                    4: "stale generation"}
+
+
+class ArtifactMeta(ctypes.Structure):
+    """mla_artifact_meta: description of an offline Local-head artifact, or
+    of what a request needs from one (field meanings as in mla.h)."""
+    _fields_ = [("generation", ctypes.c_uint64), ("token_hash", ctypes.c_uint64),
+                ("n_tokens", ctypes.c_int64), ("n_heads", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("d_c", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("rope_base", ctypes.c_double), ("n_layers", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("layer_mask", ctypes.c_uint64)]
 
 
 class MlaError(RuntimeError):
@@ -63,6 +82,7 @@ _SIGS = {
     "mla_merge_states": [P, I32, P, P, I32, P, I64, P, I32, P, P],
     "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
     "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
+    "mla_artifact_check": [ctypes.POINTER(ArtifactMeta), ctypes.POINTER(ArtifactMeta), ctypes.POINTER(I32)],
 }
 
 
@@ -78,6 +98,8 @@ def load(path: str = LIB_PATH):
     lib.mla_last_error.argtypes = []
     lib.mla_abi_version.restype = I32
     lib.mla_abi_version.argtypes = []
+    lib.mla_token_hash.restype = ctypes.c_uint64
+    lib.mla_token_hash.argtypes = [P, I64]
     for name, args in _SIGS.items():
         f = getattr(lib, name)
         f.argtypes = args
@@ -188,3 +210,17 @@ def mla_head_partition_merge(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_
     return _call("mla_head_partition_merge", _ptr(art_out), _ptr(rec_out), _ptr(prot_rows), P,
                  _ptr(glob_out), _ptr(wa_t), _ptr(wb_t), T, HL, HG, d_mid, d_model, _ptr(z),
                  _ptr(y), _stream(stream))
+
+
+def mla_token_hash(tokens) -> int:
+    """64-bit FNV-1a of int32 token ids (a host array-like)."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    return int(load().mla_token_hash(a.ctypes.data if a.size else None, a.size))
+
+
+def mla_artifact_check(artifact: ArtifactMeta, request: ArtifactMeta) -> int:
+    """First failing validation check (ARTIFACT_* reason), host only."""
+    reason = I32(-1)
+    _call("mla_artifact_check", ctypes.byref(artifact), ctypes.byref(request), ctypes.byref(reason))
+    return reason.value

@@ -14,6 +14,13 @@ the protected rows; Local rows come from the artifact with protected rows
 replaced, and the sliced first projection plus the shared second projection
 give the layer output (Equation 4).
 
+ArtifactBuilder -- the offline step before that reuse (RedKnot-MLA Abstract
+and section 2, "Canonical offline artifacts"): one document processed alone
+at canonical position zero, Local heads only, its (out, lse) kept with a
+description (tokens, profile, generation, layers) that the reuse path checks
+with mla_artifact_check before it trusts the artifact; on any mismatch it
+recomputes the Local heads for every row instead.
+
 PyTorch provides device memory and the stream; nothing here computes.
 """
 from __future__ import annotations
@@ -229,10 +236,29 @@ class ReusePrefill:
     equals the chunk-by-chunk merge."""
 
     def __init__(self, prob, device="cuda", chunk=None, split=2048, local_path="absorbed",
-                 split_local=8192):
+                 split_local=8192, artifact=None, request=None):
         assert prob.is_reuse
         assert local_path in ("absorbed", "decompressed")
         self.prob = prob
+        prot_rows = np.asarray(prob.prot_rows, dtype=np.int64)
+        # An artifact built offline (ArtifactBuilder) replaces the problem's
+        # Local-head rows once its description passes the check against what
+        # the request needs; otherwise the Local heads are recomputed for
+        # every row (all rows protected, every head decompressed) and the
+        # artifact is never read. The decision precedes every launch.
+        self.fallback = None
+        if artifact is not None:
+            if request is None:
+                raise ValueError("ReusePrefill: an artifact needs the request's description to be checked against")
+            reason = L.mla_artifact_check(artifact.meta, request)
+            if reason != L.ARTIFACT_VALID:
+                self.fallback = L.ARTIFACT_REASONS[reason]
+            elif tuple(artifact.out.shape) != (prob.T, prob.n_local, D_V):
+                raise ValueError(f"ReusePrefill: artifact rows {tuple(artifact.out.shape)} do not match "
+                                 f"({prob.T}, {prob.n_local}, {D_V})")
+        if self.fallback is not None:
+            prot_rows = np.arange(prob.T, dtype=np.int64)
+            local_path = "decompressed"
         self.device = device
         self.local_path = local_path
         self.absorbed = local_path == "absorbed"
@@ -251,7 +277,7 @@ class ReusePrefill:
                      for d in prob.documents()]
         self.Ldoc = sum(d["L"] for d in self.docs)
         self.T = prob.T
-        self.P = int(len(prob.prot_rows))
+        self.P = int(len(prot_rows))
         self.d_mid = prob.WaL.shape[1]
         self.d_model = prob.Wb.shape[1]
         self.q = _bf16(prob.q, device)
@@ -260,12 +286,17 @@ class ReusePrefill:
         # the original kv_b_proj layout (W_UK columns K-contiguous per output
         # row) for the query absorption of the Local heads
         self.W = _bf16(prob.W, device) if self.absorbed else None
-        self.art = _bf16(prob.art_out, device)
-        self.prot = _i32(prob.prot_rows, device)
+        if self.fallback is not None:
+            self.art = torch.zeros((max(self.T, 1), max(self.HL, 1), D_V), dtype=torch.bfloat16, device=device)
+        elif artifact is not None:
+            self.art = artifact.out
+        else:
+            self.art = _bf16(prob.art_out, device)
+        self.prot = _i32(prot_rows, device)
         self.wa_t = pack_weight(np.concatenate([prob.WaL, prob.WaG], axis=0), device)
         self.wb_t = pack_weight(prob.Wb, device)
         T, P = self.T, self.P
-        prot = np.asarray(prob.prot_rows, dtype=np.int64)
+        prot = prot_rows
         # chunk plan; piece i of the document is split (chunk c, piece j)
         self.chunks = []
         n_pieces = n_pieces_L = 0
@@ -472,3 +503,135 @@ class ReusePrefill:
             merge_bytes=int(merge_bytes),
             gather_tokens=Ld, gather_bytes=Ld * 2304, new_tokens=T, ctx_tokens=Ld,
         )
+
+
+class Artifact:
+    """An offline Local-head artifact: out [R, HL, 128] bf16 and lse [R, HL]
+    fp32 on the device, with its description (ArtifactMeta)."""
+
+    def __init__(self, out, lse, meta):
+        self.out, self.lse, self.meta = out, lse, meta
+
+
+def artifact_meta(tokens, generation, H, n_local, rope_base=10000.0, n_layers=1, layers=(0,)):
+    """Description of a document's artifact, or of what a request needs from
+    it: the token binding (mla_token_hash), the profile and the layers."""
+    mask = 0
+    for l in layers:
+        mask |= 1 << int(l)
+    return L.ArtifactMeta(generation=int(generation), token_hash=L.mla_token_hash(tokens),
+                          n_tokens=int(len(tokens)), n_heads=int(H), n_local=int(n_local), d_c=512,
+                          d_rope=64, d_nope=128, d_v=D_V, rope_base=float(rope_base), n_layers=int(n_layers),
+                          reserved=0, layer_mask=mask)
+
+
+class ArtifactBuilder:
+    """MLA-Off: one document processed alone at canonical position zero,
+    Local heads only (RedKnot-MLA Abstract and section 2).
+
+    Rows: q [R, H, 192] bf16 with rope parts at canonical positions. With
+    doc_rows, rows 0..L-1 are the document's own tokens (row t sees keys
+    0..t) and later rows follow the document (they see all of it); without,
+    every row follows the document.
+
+    Per key chunk [s0, s0 + n): gather, decompression of the Local heads,
+    then two attention passes over the chunk's keys. Rows past the chunk
+    (document rows from s0 + n on, then the following rows) attend to all of
+    it, merged into an fp32 running state (the last chunk writes their bf16
+    result). The chunk's own document rows attend causally (n_q = n_k = n,
+    bottom-right aligned, so row s0 + i sees keys s0..s0 + i), merged with
+    their running state and written as the final bf16 result: no later chunk
+    reaches them. One chunk holding the whole document needs no merges.
+    """
+
+    def __init__(self, pool, block_table, L_doc, q, W_bits, H, n_local, scale, doc_rows=True, chunk=None,
+                 device="cuda", tokens=None, generation=0, rope_base=10000.0, n_layers=1, layer=0):
+        self.device = device
+        self.H, self.HL = int(H), int(n_local)
+        self.L = int(L_doc)
+        self.doc_rows = bool(doc_rows)
+        self.scale = float(scale)
+        self.pool = pool if isinstance(pool, torch.Tensor) else _bf16(pool, device)
+        self.bt = block_table if isinstance(block_table, torch.Tensor) else _i32(block_table, device)
+        self.q = q if isinstance(q, torch.Tensor) else _bf16(q, device)
+        self.R = int(self.q.shape[0])
+        if self.doc_rows and self.R < self.L:
+            raise ValueError("ArtifactBuilder: with doc_rows the first L rows are the document's tokens")
+        self.w_t = pack_weight(W_bits, device)
+        self.S = max(1, min(int(chunk or self.L), max(self.L, 1)))
+        self.chunks = []
+        for s0 in range(0, self.L, self.S):
+            n = min(self.S, self.L - s0)
+            a0 = s0 + n if self.doc_rows else 0          # first row past the chunk
+            self.chunks.append(dict(s0=s0, n=n, a0=a0, start=_i32([s0], device), len=_i32([n], device),
+                                    cu=_i32([0, n], device), cu_after=_i32([0, self.R - a0], device)))
+        S, HL = self.S, self.HL
+        bf, f32 = torch.bfloat16, torch.float32
+        self.lat_ws = torch.empty((S, D_LAT), dtype=bf, device=device)
+        self.k_ws = torch.empty((max(HL, 1), S, D_V), dtype=bf, device=device)
+        self.v_ws = torch.empty((max(HL, 1), S, D_V), dtype=bf, device=device)
+        self.hstride = S * D_V
+        self.out = torch.empty((max(self.R, 1), max(HL, 1), D_V), dtype=bf, device=device)
+        self.lse = torch.empty((max(self.R, 1), max(HL, 1)), dtype=f32, device=device)
+        if len(self.chunks) > 1:
+            self.acc = torch.empty((self.R, HL, D_V), dtype=f32, device=device)
+            self.acc_lse = torch.empty((self.R, HL), dtype=f32, device=device)
+        self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.meta = artifact_meta(tokens if tokens is not None else np.zeros(0, np.int32), generation, H,
+                                  n_local, rope_base, n_layers, (layer,))
+        if tokens is not None and len(tokens) != self.L:
+            raise ValueError("ArtifactBuilder: tokens must hold the document's L ids")
+
+    @classmethod
+    def from_problem(cls, ap, device="cuda", chunk=None):
+        return cls(ap.pool, ap.block_table, ap.L, ap.q, ap.W, ap.H, ap.n_local, ap.scale, ap.doc_rows,
+                   chunk or ap.chunk, device, ap.tokens, ap.generation, ap.rope_base)
+
+    def _attn(self, r0, n_rows, cu_q, cu_k, causal, merge, final, stream):
+        H, HL = self.H, self.HL
+        q = self.q[r0:]
+        out, odt, lse = ((self.out[r0:], L.DTYPE_BF16, self.lse[r0:]) if final
+                         else (self.acc[r0:], L.DTYPE_FP32, self.acc_lse[r0:]))
+        common = (q, H * D_QK, H, 0, HL, self.k_ws, self.hstride, self.v_ws, self.hstride, self.lat_ws, D_LAT,
+                  cu_q, cu_k, None, 1, n_rows, self.scale, int(causal))
+        if merge:
+            L.mla_prefill_attn_merge(*common, self.acc[r0:], HL * D_V, self.acc_lse[r0:], HL, out, odt, HL * D_V,
+                                     lse, HL, stream)
+        else:
+            L.mla_prefill_attn(*common, out, odt, HL * D_V, lse, HL, stream)
+
+    def run(self, stream=None, timer=None) -> Artifact:
+        n_ch = len(self.chunks)
+        for ci, ch in enumerate(self.chunks):
+            first, last = ci == 0, ci == n_ch - 1
+            with _span(timer, "gather"):
+                L.mla_gather_context(self.pool, L.DTYPE_BF16, int(self.pool.shape[0]), self.bt, self.bt.shape[1],
+                                     ch["start"], ch["len"], ch["cu"], 1, ch["n"], self.lat_ws, self.dev_status,
+                                     stream)
+            if self.HL == 0:
+                continue
+            with _span(timer, "decompress"):
+                L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, self.H, 0, self.HL, self.k_ws,
+                                 self.hstride, self.v_ws, self.hstride, stream)
+            n_after = self.R - ch["a0"]
+            if n_after > 0:
+                with _span(timer, "attn_full"):
+                    self._attn(ch["a0"], n_after, ch["cu_after"], ch["cu"], False, merge=not first,
+                               final=last, stream=stream)
+            if self.doc_rows:
+                with _span(timer, "attn_causal"):
+                    self._attn(ch["s0"], ch["n"], ch["cu"], ch["cu"], True, merge=not first, final=True,
+                               stream=stream)
+        return Artifact(self.out[:self.R], self.lse[:self.R], self.meta)
+
+    def work(self) -> dict:
+        """Algorithmic work of one build: decompression of the Local heads
+        over the document (2 * 512 * 256 flop per (token, head)) and 640 flop
+        per visible (row, key, head)."""
+        L_, HL = self.L, self.HL
+        n_doc = L_ if self.doc_rows else 0
+        pairs = n_doc * (n_doc + 1) // 2 + (self.R - n_doc) * L_
+        causal = sum(c["n"] * (c["n"] + 1) // 2 for c in self.chunks) if self.doc_rows else 0
+        return dict(dec_flops=2 * 512 * 256 * HL * L_, attn_flops=640 * HL * pairs,
+                    causal_attn_flops=640 * HL * causal, full_attn_flops=640 * HL * (pairs - causal),
+                    gather_bytes=L_ * 2304, rows=self.R, doc_tokens=L_)

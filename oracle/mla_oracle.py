@@ -557,6 +557,91 @@ def segmented_attention(prob, h: int, rows: np.ndarray):
 
 
 # --------------------------------------------------------------------------
+# Offline Local-head artifact ([REDKNOT] Abstract; section 2, "Canonical
+# offline artifacts")
+# --------------------------------------------------------------------------
+
+def artifact_row_positions(L: int, row_ids, doc_rows: bool) -> np.ndarray:
+    """Canonical positions of an artifact's rows (reading R31): with
+    doc_rows, rows 0..L-1 are the document's own tokens at positions 0..L-1
+    and any further rows follow the document at L, L+1, ... (row i at i);
+    without, every row follows the document (row i at L + i)."""
+    i = np.asarray(row_ids, dtype=np.int64)
+    return i if doc_rows else L + i
+
+
+def build_artifact(latent: np.ndarray, q: np.ndarray, W: np.ndarray, H: int, n_local: int,
+                   scale: float, doc_rows: bool, row_ids=None, heads=None):
+    """MLA-Off: the document processed alone at canonical position zero, its
+    Local-head results kept ([REDKNOT] Abstract and section 2; reading R31).
+    latent [L, 576] (fp64) are the document's records with the rope part at
+    canonical positions 0..L-1; q [R, H, 192] (fp64) are the queries of
+    artifact rows row_ids (default 0..R-1), rope part at the rows' canonical
+    positions (artifact_row_positions). Row r at position p_r sees key t iff
+    t <= p_r: a document row attends to itself and the tokens before it, a
+    row after the document to all of it. Heads default to the Local heads
+    0..n_local-1. Returns (out [R, n_heads, 128], lse [R, n_heads])."""
+    L = latent.shape[0]
+    R = q.shape[0]
+    rows = np.arange(R) if row_ids is None else np.asarray(row_ids, dtype=np.int64)
+    hs = list(range(n_local)) if heads is None else list(heads)
+    assert all(0 <= h < n_local for h in hs)
+    pos = artifact_row_positions(L, rows, doc_rows)
+    visible = np.arange(L)[None, :] <= pos[:, None]
+    out = np.zeros((R, len(hs), D_V))
+    lse = np.zeros((R, len(hs)))
+    for j, h in enumerate(hs):
+        kn, v = decompress_head(latent[:, :D_C], W, H, h)
+        out[:, j], lse[:, j] = attend(q[:, h], kn, latent[:, D_C:], v, scale, visible)
+    return out, lse
+
+
+def fnv1a64(data: bytes) -> int:
+    """64-bit FNV-1a (Fowler-Noll-Vo): start at the offset basis
+    14695981039346656037; for each byte, xor it in, then multiply by the
+    prime 1099511628211 modulo 2^64."""
+    h = 14695981039346656037
+    for b in data:
+        h = ((h ^ b) * 1099511628211) % (1 << 64)
+    return h
+
+
+def token_bytes(tokens) -> bytes:
+    """Token ids as the bytes that are hashed: each id's four little-endian
+    bytes (as a 32-bit two's-complement integer), in order."""
+    return b"".join((int(t) & 0xFFFFFFFF).to_bytes(4, "little")
+                    for t in np.asarray(tokens, dtype=np.int64).tolist())
+
+
+def artifact_token_hash(tokens) -> int:
+    """The token binding of an artifact's description (reading R32):
+    fnv1a64 of token_bytes."""
+    return fnv1a64(token_bytes(tokens))
+
+
+ARTIFACT_PROFILE_FIELDS = ("n_heads", "n_local", "d_c", "d_rope", "d_nope", "d_v", "rope_base", "n_layers")
+
+
+def artifact_check_reason(artifact: dict, request: dict) -> int:
+    """Validation before reuse ([REDKNOT] section 2: fall back to full
+    recomputation on missing layers, token or profile mismatch, or a stale
+    generation; reading R32 fixes the order of the checks as the page lists
+    them and leaves out the tensor-parallel and rank checks). Returns 0
+    (valid), 1 (a layer the request needs is absent from the artifact's
+    layer_mask), 2 (token count or token hash differ), 3 (a profile field
+    differs), 4 (generation differs)."""
+    if request["layer_mask"] & ~artifact["layer_mask"]:
+        return 1
+    if artifact["n_tokens"] != request["n_tokens"] or artifact["token_hash"] != request["token_hash"]:
+        return 2
+    if any(artifact[f] != request[f] for f in ARTIFACT_PROFILE_FIELDS):
+        return 3
+    if artifact["generation"] != request["generation"]:
+        return 4
+    return 0
+
+
+# --------------------------------------------------------------------------
 # Layout constants ([DSMLA] 5.2; [PAGED] KV accounting table)
 # --------------------------------------------------------------------------
 

@@ -106,3 +106,63 @@ def test_last_error_is_thread_local_and_cleared(lib):
     assert b"multiples of 8" in lib.mla_last_error()
     assert mla.mla_merge_states(None, 0, None, None, 0, None, 0, None, 0, None, stream=0) == 0
     assert lib.mla_last_error() == b""
+
+
+# ---------------------------------------------------------------- artifact validation (host only)
+
+def test_token_hash_matches_the_oracle(lib):
+    import numpy as np
+    from oracle import mla_oracle as orc
+    rng = np.random.default_rng(11)
+    assert mla.mla_token_hash([]) == orc.artifact_token_hash([]) == 0xcbf29ce484222325
+    for n in (1, 2, 7, 1000):
+        t = rng.integers(-(1 << 31), 1 << 31, size=n).astype(np.int32)
+        assert mla.mla_token_hash(t) == orc.artifact_token_hash(t)
+
+
+def _meta_pair(rng):
+    keys = ("generation", "token_hash", "n_tokens", "n_heads", "n_local", "d_c", "d_rope", "d_nope", "d_v",
+            "rope_base", "n_layers", "layer_mask")
+    a = dict(generation=int(rng.integers(1, 9)), token_hash=int(rng.integers(0, 1 << 63)),
+             n_tokens=int(rng.integers(1, 1 << 20)), n_heads=64, n_local=56, d_c=512, d_rope=64, d_nope=128,
+             d_v=128, rope_base=10000.0, n_layers=37, layer_mask=(1 << 37) - 1)
+    r = dict(a)
+    # perturb a random subset of fields
+    for k in keys:
+        if rng.random() < 0.15:
+            if k == "rope_base":
+                r[k] = 50000.0
+            elif k == "layer_mask":
+                which = int(rng.integers(0, 64))
+                if rng.random() < 0.5:
+                    a[k] = a[k] & ~(1 << which)
+                else:
+                    r[k] = r[k] | (1 << which)
+            else:
+                r[k] = r[k] + 1
+    return a, r
+
+
+def test_artifact_check_matches_the_oracle(lib):
+    import numpy as np
+    from oracle import mla_oracle as orc
+    rng = np.random.default_rng(12)
+    seen = set()
+    for _ in range(400):
+        a, r = _meta_pair(rng)
+        want = orc.artifact_check_reason(a, r)
+        got = mla.mla_artifact_check(mla.ArtifactMeta(**a), mla.ArtifactMeta(**r))
+        assert got == want, (a, r)
+        seen.add(want)
+    assert seen == {0, 1, 2, 3, 4}
+
+
+def test_artifact_check_rejects_bad_arguments(lib):
+    m = mla.ArtifactMeta(n_layers=65)
+    with pytest.raises(mla.MlaError) as ei:
+        mla.mla_artifact_check(m, mla.ArtifactMeta())
+    assert ei.value.code == _lib.MLA_ERR_INVALID_ARG
+    reason = ctypes.c_int(-7)
+    assert lib.mla_artifact_check(None, ctypes.byref(mla.ArtifactMeta()), ctypes.byref(reason)) == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert reason.value == -7

@@ -600,3 +600,118 @@ def test_each_document_uses_its_own_offset():
     flat = orc.reuse_reference(dataclasses.replace(prob, docs=same))["O_G"]
     for other in (moved, flat):
         assert np.linalg.norm(other - base) / np.linalg.norm(base) > 0.02
+
+
+# ---------------------------------------------------------------- offline artifact (MLA-Off)
+
+def test_fnv1a64_published_vectors_and_token_framing():
+    """FNV-1a 64 against the published test vectors of its authors, and the
+    token framing: each id as 4 little-endian bytes."""
+    assert orc.fnv1a64(b"") == 0xcbf29ce484222325
+    assert orc.fnv1a64(b"a") == 0xaf63dc4c8601ec8c
+    assert orc.fnv1a64(b"foobar") == 0x85944171f73967e8
+    assert orc.token_bytes([0x64636261, -1, 7]) == b"abcd" + b"\xff" * 4 + b"\x07\x00\x00\x00"
+    assert orc.artifact_token_hash([]) == 0xcbf29ce484222325
+    # order matters, and a single changed id changes the hash
+    assert orc.artifact_token_hash([1, 2]) != orc.artifact_token_hash([2, 1])
+    assert orc.artifact_token_hash([5, 9, 11]) != orc.artifact_token_hash([5, 9, 12])
+
+
+def _meta(**kw):
+    m = dict(generation=3, token_hash=0x1234, n_tokens=1088, n_heads=64, n_local=56, d_c=512, d_rope=64,
+             d_nope=128, d_v=128, rope_base=10000.0, n_layers=37, layer_mask=(1 << 37) - 1)
+    m.update(kw)
+    return m
+
+
+def test_artifact_check_reasons_and_their_order():
+    """Each single mismatch gives its own reason; with several, the first in
+    the page's list (layers, tokens, profile, generation) wins; a request
+    that needs fewer layers than the artifact holds is valid."""
+    a = _meta()
+    assert orc.artifact_check_reason(a, _meta()) == 0
+    assert orc.artifact_check_reason(a, _meta(layer_mask=1 << 3)) == 0
+    assert orc.artifact_check_reason(_meta(layer_mask=a["layer_mask"] & ~(1 << 20)), _meta()) == 1
+    assert orc.artifact_check_reason(a, _meta(token_hash=0x1235)) == 2
+    assert orc.artifact_check_reason(a, _meta(n_tokens=1089)) == 2
+    for f, v in [("n_heads", 128), ("n_local", 48), ("d_c", 256), ("d_rope", 32), ("d_nope", 64),
+                 ("d_v", 64), ("rope_base", 50000.0), ("n_layers", 55)]:
+        assert orc.artifact_check_reason(a, _meta(**{f: v})) == 3, f
+    assert orc.artifact_check_reason(a, _meta(generation=4)) == 4
+    assert orc.artifact_check_reason(a, _meta(generation=2)) == 4
+    assert orc.artifact_check_reason(_meta(layer_mask=0), _meta(token_hash=1, n_heads=1, generation=9)) == 1
+    assert orc.artifact_check_reason(a, _meta(token_hash=1, n_heads=1, generation=9)) == 2
+    assert orc.artifact_check_reason(a, _meta(n_heads=1, generation=9)) == 3
+
+
+def _art_inputs(prob):
+    lat = np.array([orc.bf16_to_f64(prob.pool[prob.block_table[0, t // 64], t % 64]) for t in range(prob.L)])
+    return lat, orc.bf16_to_f64(prob.q), orc.bf16_to_f64(prob.W)
+
+
+def test_artifact_first_document_row_sees_one_key():
+    """Document row 0 sees only key 0: out = v_0 (its W_UV product) and
+    lse = its one score, s_0 = scale (q_nope . c W_UK + q_rope . k_rope)."""
+    prob = mi.make_artifact_problem(H=3, n_local=2, L=70, extra_rows=2, seed=41)
+    lat, q, W = _art_inputs(prob)
+    out, lse = orc.build_artifact(lat, q, W, 3, 2, prob.scale, doc_rows=True)
+    for h in range(2):
+        k = lat[0, :512] @ W[:, h * 128:(h + 1) * 128]
+        v = lat[0, :512] @ W[:, 3 * 128 + h * 128:3 * 128 + (h + 1) * 128]
+        s0 = prob.scale * (q[0, h, :128] @ k + q[0, h, 128:] @ lat[0, 512:])
+        np.testing.assert_allclose(out[0, h], v, rtol=1e-12, atol=1e-14)
+        assert lse[0, h] == pytest.approx(s0, abs=1e-12)
+
+
+def test_artifact_bruteforce_loops():
+    """Every row and Local head of a tiny artifact against per-element fsum
+    loops: document row t over keys 0..t, rows after the document over every
+    key; heads >= n_local are not part of the artifact."""
+    prob = mi.make_artifact_problem(H=3, n_local=2, L=9, extra_rows=3, seed=42)
+    lat, q, W = _art_inputs(prob)
+    out, lse = orc.build_artifact(lat, q, W, 3, 2, prob.scale, doc_rows=True)
+    assert out.shape == (12, 2, 128) and lse.shape == (12, 2)
+    for h in range(2):
+        K = [[math.fsum(lat[t, c] * W[c, h * 128 + d] for c in range(512)) for d in range(128)] for t in range(9)]
+        V = [[math.fsum(lat[t, c] * W[c, 3 * 128 + h * 128 + d] for c in range(512)) for d in range(128)]
+             for t in range(9)]
+        for r in range(12):
+            keys = range(r + 1) if r < 9 else range(9)
+            s = [prob.scale * math.fsum([q[r, h, d] * K[t][d] for d in range(128)] +
+                                        [q[r, h, 128 + j] * lat[t, 512 + j] for j in range(64)]) for t in keys]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            Z = math.fsum(e)
+            o = [math.fsum(e[i] * V[t][d] for i, t in enumerate(keys)) / Z for d in range(128)]
+            np.testing.assert_allclose(out[r, h], o, rtol=1e-10, atol=1e-12)
+            assert lse[r, h] == pytest.approx(m + math.log(Z), abs=1e-10)
+    # rows after the document alone (doc_rows=False) are the same rows
+    out2, lse2 = orc.build_artifact(lat, q[9:], W, 3, 2, prob.scale, doc_rows=False)
+    np.testing.assert_allclose(out2, out[9:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse[9:], rtol=0, atol=1e-12)
+    # selected rows (a document row and a row after it) and one head
+    out3, lse3 = orc.build_artifact(lat, q[[2, 10]], W, 3, 2, prob.scale, doc_rows=True, row_ids=[2, 10],
+                                    heads=[1])
+    np.testing.assert_allclose(out3[:, 0], out[[2, 10], 1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse3[:, 0], lse[[2, 10], 1], rtol=0, atol=1e-12)
+
+
+def test_artifact_for_request_rows_equals_their_full_recompute():
+    """Built at canonical position zero with the request rows' queries moved
+    into the canonical frame, the artifact of rows after the document is the
+    Local heads' full recomputation in the request (keys placed at +delta),
+    so Equation 4 with it and no protected row gives the full-recompute y."""
+    prob = mi.make_reuse_problem(H=4, n_local=3, L=192, T=10, delta=4096, P=10,
+                                 d_mid=16, d_model=24, chunk=64, seed=43)
+    full = orc.reuse_reference(prob)            # P = T: every Local row recomputed
+    lat = np.array([orc.bf16_to_f64(prob.pool[prob.block_table[0, t // 64], t % 64]) for t in range(192)])
+    q = orc.bf16_to_f64(prob.q)
+    qc = q.copy()
+    qc[..., 128:] = orc.relocate_q(q[..., 128:], prob.delta, prob.rope_base)
+    out, lse = orc.build_artifact(lat, qc, orc.bf16_to_f64(prob.W), 4, 3, prob.scale, doc_rows=False)
+    np.testing.assert_allclose(out, full["rec"], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(lse, full["rec_lse"], rtol=0, atol=1e-9)
+    O_L = orc.replace_protected(out, out[:0], np.zeros(0, dtype=np.int64))
+    WaL, WaG, Wb = (orc.bf16_to_f64(x) for x in (prob.WaL, prob.WaG, prob.Wb))
+    y = orc.head_partition_merge(O_L, full["O_G"], WaL, WaG, Wb)
+    np.testing.assert_allclose(y, full["y"], rtol=1e-9, atol=1e-12)
