@@ -123,26 +123,29 @@ __global__ __launch_bounds__(256) void absorb_out_kernel(AbsorbOutArgs a, int n_
 
 // ---------------------------------------------------------------- absorbed flash attention
 //
-// Workgroup = 64 query rows of one key piece, 8 wavefronts: row group rg
-// (32 rows) x quarter qd. Per 32-key tile:
-//   scores    wavefront (rg, qd) holds the query dims 144 qd .. 144 qd + 143
-//             in VGPRs (9 k steps) and computes their part of S^T[32 keys][32
-//             rows]; the four partial sums of a row group meet in LDS and
-//             every wavefront of the group adds them in the same order, so
-//             all four hold the identical S and run the same online softmax.
-//   values    wavefront (rg, qd) accumulates O^T for the value dims
-//             128 qd .. 128 qd + 127 of its 32 rows (4 blocks of 32 x 32).
+// Workgroup = 128 query rows of one key piece, 4 wavefronts, one per SIMD;
+// each wavefront owns 32 rows for all 576 query dims and all 512 value dims,
+// so no partial sums cross wavefronts. Per 32-key tile:
+//   scores    S^T[32 keys][32 rows] = K . Q^T over 36 k steps (Q in VGPRs,
+//             two accumulator chains for the even and odd steps)
+//   values    O^T[512 value dims][32 rows] += V^T P^T, 16 blocks of 32 x 32
+//             (O, 256 registers, in the accumulation registers; one wavefront
+//             per SIMD leaves them free)
+// Every key and value fragment read from LDS feeds one product of 32 rows:
+// 1 KB of LDS reads per 64 K flop, as in the decompressed-form attention.
 // LDS per stage (36 KB): c_kv rows of 1024 B, 16-byte chunk c of key r at
 // position c ^ f(r & 15), f(x) = ((x & 3) << 2) | (x >> 2), which keeps both
 // the 16-byte key reads (16 keys, same chunk) and the transposing value reads
 // free of bank conflicts; rope rows of 128 B, chunk c at c ^ ((r >> 1) & 7).
-// Three stages go round; DMA as in the attention kernel (global_load_lds,
+// Four stages; the DMA of tile t+3 is issued at step t (global_load_lds,
 // keys past the piece end clamped to its last key and masked).
 constexpr int kAT = 32;                         // keys per tile
 constexpr int kACkv = kAT * 1024;               // c_kv region of a stage
 constexpr int kAStage = kACkv + kAT * 128;      // + rope region = 36 KB
-constexpr int kANB = 3;                         // stages
-constexpr int kASpart = 8 * 32 * 32 * 4;        // partial scores: 8 wavefronts x 32 x 32 fp32
+constexpr int kANB = 4;                         // stages
+constexpr int kAW = 4;                          // wavefronts per workgroup
+constexpr int kARows = 32 * kAW;                // query rows per workgroup
+constexpr int kADma = 9;                        // DMA instructions per wavefront per tile
 
 struct AbsAttnArgs {
   const uint16_t* qa; int R;                    // q_abs [R][576]
@@ -154,13 +157,11 @@ struct AbsAttnArgs {
 __device__ __forceinline__ int akv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 template <int kOutDt>
-__global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kANB * kAStage + kASpart];
-  uint8_t* const spart = lds + kANB * kAStage;
+__global__ __launch_bounds__(kAW * 64, 1) void absorbed_attn_kernel(AbsAttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kANB * kAStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int rg = wave >> 2, qd = wave & 3;
 
   // row tiles of one piece stay on one XCD (they share the piece's keys);
   // pieces are dealt to the XCDs round-robin
@@ -170,21 +171,21 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
   const int rt = j % a.n_rt;
   const int k0 = a.cu_k[pc];
   const int n_k = a.cu_k[pc + 1] - k0;
-  const int row = rt * 64 + rg * 32 + l32;
+  const int row = rt * kARows + wave * 32 + l32;
   const bool row_ok = row < a.R;
   const int ntiles = (n_k + kAT - 1) / kAT;
 
-  // query dims 144 qd .. 144 qd + 143 of this lane's row as B fragments
-  bf16x8 qf[9];
+  // the 576 query dims of this lane's row as B fragments
+  bf16x8 qf[kDlat / 16];
   {
-    const uint16_t* qp = a.qa + (int64_t)(row_ok ? row : 0) * kDlat + 144 * qd + 8 * g;
+    const uint16_t* qp = a.qa + (int64_t)(row_ok ? row : 0) * kDlat + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 9; ++s) qf[s] = row_ok ? ld16(qp + 16 * s) : bf16x8{};
+    for (int s = 0; s < kDlat / 16; ++s) qf[s] = row_ok ? ld16(qp + 16 * s) : bf16x8{};
   }
 
-  // DMA: wavefront w moves c_kv rows w, w+8, w+16, w+24 (1 KB each) and, for
-  // w < 4, rope rows 8w .. 8w+7; a lane's position is fixed, the global chunk
-  // it fetches is the inverse swizzle (XOR is its own inverse)
+  // DMA: wavefront w moves c_kv rows w, w+4, ..., w+28 (1 KB each) and rope
+  // rows 8w .. 8w+7; a lane's position is fixed, the global chunk it fetches
+  // is the inverse swizzle (XOR is its own inverse)
   const int klast = n_k - 1;
   const uint16_t* base = a.lat + (int64_t)k0 * a.ld;
   // DMA of tile t into stage `stage`; the stage follows the step, not the
@@ -194,13 +195,13 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
     uint8_t* st = lds + stage * kAStage;
     const int kt0 = t * kAT;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = i * 8 + wave;
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * kAW + wave;
       const int c = lane ^ akv_swz(r & 15);
       const int key = min(kt0 + r, klast);
       dma16(base + (int64_t)key * a.ld + c * 8, st + r * 1024);
     }
-    if (wave < 4) {
+    {
       const int r = 8 * wave + (lane >> 3);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int key = min(kt0 + r, klast);
@@ -208,83 +209,75 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
     }
   };
 
-  f32x16 O[4];
+  f32x16 O[16];
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < 16; ++d)
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[d][i] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
-  // value reads (transposing, 8 keys of one value column per lane over two
-  // reads): row 16 mm + 8 hi + 4 g + a4, value dims 128 qd + 32 d + 16 g16 + 4 b4
-  const int a4 = (lane & 15) >> 2, b4 = lane & 3, g16 = (lane >> 4) & 1;
-  auto voff = [&](int mm, int hi, int d) __attribute__((always_inline)) {
-    const int r = 16 * mm + 8 * hi + 4 * g + a4;
-    const int chunk = 16 * qd + 4 * d + 2 * g16 + (b4 >> 1);
-    return r * 1024 + ((chunk ^ akv_swz(r & 15)) << 4) + 8 * (b4 & 1);
-  };
-  // key reads: key l32, query-dim step s (global step 9 qd + s), chunk 2 step + g
-  auto koff = [&](int s) __attribute__((always_inline)) {
-    const int step = 9 * qd + s;
-    if (step < 32) {
-      const int chunk = 2 * step + g;
-      return l32 * 1024 + ((chunk ^ akv_swz(l32 & 15)) << 4);
+  // Fragment read offsets. Swizzles only touch the low four chunk bits, so
+  // the offset of a read is one of a few per-lane bases plus a constant:
+  //   key reads (key l32, query-dim step s, chunk 2 s + g): c_kv steps
+  //   s < 32 use kb[s & 7] + 256 (s >> 3), rope steps kr[s - 32];
+  //   value reads (transposing, 8 keys of one value column per lane over two
+  //   reads; row 16 mm + 8 hi + 4 g + a4, value dims 32 d + 16 g16 + 4 b4)
+  //   use vb[hi][d & 3] + 16384 mm + 256 (d >> 2).
+  int kb[8], kr[4], vb[2][4];
+  {
+    const int sw = akv_swz(l32 & 15);
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) kb[s8] = l32 * 1024 + (((2 * s8 + g) ^ sw) << 4);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) kr[s4] = kACkv + l32 * 128 + (((2 * s4 + g) ^ ((l32 >> 1) & 7)) << 4);
+    const int a4 = (lane & 15) >> 2, b4 = lane & 3, g16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hi + 4 * g + a4;
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+        vb[hi][d4] = r * 1024 + (((4 * d4 + 2 * g16 + (b4 >> 1)) ^ akv_swz(r)) << 4) + 8 * (b4 & 1);
     }
-    const int chunk = 2 * (step - 32) + g;
-    return kACkv + l32 * 128 + ((chunk ^ ((l32 >> 1) & 7)) << 4);
+  }
+  auto koff = [&](int s) __attribute__((always_inline)) { return s < 32 ? kb[s & 7] + 256 * (s >> 3) : kr[s - 32]; };
+  auto voff = [&](int mm, int hi, int d) __attribute__((always_inline)) {
+    return vb[hi][d & 3] + 16384 * mm + 256 * (d >> 2);
   };
 
-  if (ntiles > 0) {
-    dma(0, 0);
-    dma(min(1, ntiles - 1), 1);
-  }
+  for (int t = 0; t < kANB - 1; ++t) dma(min(t, max(ntiles - 1, 0)), t);
   wait_vmcnt<0>();
   for (int t = 0; t < ntiles; ++t) {
-    // own DMA of tile t done (tile t+1 may be in flight); then the barrier
-    // publishes tile t, and the stage of tile t-1 and the partial-score
-    // buffer are free again
-    if (wave < 4) wait_vmcnt<5>();
-    else wait_vmcnt<4>();
+    // own DMA of tile t done (tiles t+1, t+2 may be in flight); then the
+    // barrier publishes tile t and frees the stage of tile t-1
+    wait_vmcnt<2 * kADma>();
     __syncthreads();
-    dma(min(t + 2, ntiles - 1), (t + 2) % kANB);
+    dma(min(t + kANB - 1, ntiles - 1), (t + kANB - 1) % kANB);
     const uint8_t* st = lds + (t % kANB) * kAStage;
     const int kt0 = t * kAT;
 
-    // partial scores over this wavefront's query dims
+    // scores: two chains (even and odd k steps), added at the end
+    f32x16 S0, S1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { S0[i] = 0.f; S1[i] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < kDlat / 16; s += 2) {
+      const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(st + koff(s));
+      const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(st + koff(s + 1));
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[s], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[s + 1], S1, 0, 0, 0);
+    }
+    // key fragment reads two ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 17; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     f32x16 S;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 9; ++s) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + koff(s));
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S, 0, 0, 0);
-    }
-    f32x4* my = reinterpret_cast<f32x4*>(spart + wave * 4096);
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) my[i4 * 64 + lane] = f32x4{S[4 * i4], S[4 * i4 + 1], S[4 * i4 + 2], S[4 * i4 + 3]};
-    __syncthreads();
-    // the group's four partial sums, added in quarter order (this
-    // wavefront's own term from its registers, the others from LDS), so the
-    // four quarters hold bit-identical scores
-    f32x16 St;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) St[i] = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q == qd) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) St[i] += S[i];
-      } else {
-        const f32x4* ps = reinterpret_cast<const f32x4*>(spart + (rg * 4 + q) * 4096);
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 v = ps[i4 * 64 + lane];
-          St[4 * i4] += v.x; St[4 * i4 + 1] += v.y; St[4 * i4 + 2] += v.z; St[4 * i4 + 3] += v.w;
-        }
-      }
-    }
-    S = St;
+    for (int i = 0; i < 16; ++i) S[i] = S0[i] + S1[i];
     // keys past the piece end
     if (kt0 + kAT > n_k) {
 #pragma unroll
@@ -316,13 +309,20 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
       ps += p;
     }
     l_run = fmaf(l_run, alpha, ps);
-    if (__any(bump)) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
-    }
     m_ref = m_new;
+    if (__any(bump)) {
+      // O stays in the accumulation registers: the factor is applied there
+      // in place (plain code would keep a second copy of O alive)
+#pragma unroll
+      for (int d = 0; d < 16; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(O[d][i]), "=&v"(tmp)
+                       : "v"(alpha));
+        }
+    }
     // O^T[value dims][rows] += V^T P^T over keys 16 mm .. 16 mm + 15
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
@@ -331,28 +331,36 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
                        cvt_pk_bf16(S[i0 + 4], S[i0 + 5]), cvt_pk_bf16(S[i0 + 6], S[i0 + 7])};
       const bf16x8 pf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < 16; ++d) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + voff(mm, 0, d)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + voff(mm, 1, d)));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[d], 0, 0, 0);
       }
     }
+    // value fragment reads four ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 30; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue: row sums of the two lane halves; every quarter writes its
-  // 128 value dims and its own copy of the lse
+  // ---- epilogue: row sums of the two lane halves; the 512 value dims and
+  // four copies of the lse
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const int64_t orow = (int64_t)pc * a.R + row;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < 16; ++d)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int dv = 128 * qd + 32 * d + 8 * q4 + 4 * g;
+      const int dv = 32 * d + 8 * q4 + 4 * g;
       const float o0 = O[d][4 * q4] * inv, o1 = O[d][4 * q4 + 1] * inv;
       const float o2 = O[d][4 * q4 + 2] * inv, o3 = O[d][4 * q4 + 3] * inv;
       if (kOutDt == MLA_DTYPE_FP32) {
@@ -362,7 +370,11 @@ __global__ __launch_bounds__(512) void absorbed_attn_kernel(AbsAttnArgs a) {
             u32x2{cvt_pk_bf16(o0, o1), cvt_pk_bf16(o2, o3)};
       }
     }
-  if (g == 0) a.lse4[orow * 4 + qd] = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (g == 0) {
+    const float lse = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a.lse4[orow * 4 + k] = lse;
+  }
 }
 
 }  // namespace
@@ -408,16 +420,16 @@ extern "C" int mla_absorbed_attn(const void* q_abs, int R, const void* latent, i
   MLA_REQUIRE(ld_latent % 8 == 0 && ld_latent >= kDlat, MLA_ERR_INVALID_ARG,
               "mla_absorbed_attn: ld_latent (%lld) must be a multiple of 8 and >= 576", (long long)ld_latent);
   MLA_REQUIRE(scale > 0.f && scale < 1e30f, MLA_ERR_INVALID_ARG, "mla_absorbed_attn: scale must be positive");
-  const int n_rt = (R + 63) / 64;
+  const int n_rt = (R + kARows - 1) / kARows;
   const int64_t total = ((int64_t)pieces + 7) / 8 * 8 * n_rt;
   MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_absorbed_attn: problem too large");
   AbsAttnArgs a{static_cast<const uint16_t*>(q_abs), R, static_cast<const uint16_t*>(latent), ld_latent,
                 cu_k, pieces, n_rt, scale * kLog2e, out_lat, lse4};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (out_dtype == MLA_DTYPE_FP32)
-    hipLaunchKernelGGL(absorbed_attn_kernel<MLA_DTYPE_FP32>, dim3((unsigned)total), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(absorbed_attn_kernel<MLA_DTYPE_FP32>, dim3((unsigned)total), dim3(kAW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(absorbed_attn_kernel<MLA_DTYPE_BF16>, dim3((unsigned)total), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(absorbed_attn_kernel<MLA_DTYPE_BF16>, dim3((unsigned)total), dim3(kAW * 64), 0, s, a);
   return mla_check_launch("mla_absorbed_attn");
 }
 

@@ -66,32 +66,24 @@ constexpr int kVRow = 256;                 // bytes per V row in LDS
 constexpr int kKTile = kTileK * kKRow;     // 24576
 constexpr int kVTile = kTileK * kVRow;     // 16384
 
-// third LDS stage, allocated only by kernels that use three stages
-template <int NB>
-__device__ __forceinline__ uint8_t* lds_stage2() {
-  if constexpr (NB == 3) {
-    __shared__ __attribute__((aligned(1024))) uint8_t S2[kKTile + kVTile];
-    return S2;
-  } else {
-    return nullptr;
-  }
-}
+constexpr int kStage = kKTile + kVTile;   // one LDS stage: K tile then V tile
 
 template <int NW, bool kCausal, bool kRowIds, int kOutDt, bool kMerge>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
-  constexpr int NB = (NW == 8) ? 3 : 2;    // LDS stages (tiles in flight)
+  constexpr int NB = (NW == 8) ? 3 : 2;   // LDS stages (tiles in flight)
   constexpr int kKj = (kTileK * 24) / (64 * NW);   // K DMA instructions per wavefront per tile
   constexpr int kVj = (kTileK * 16) / (64 * NW);   // V DMA instructions per wavefront per tile
   constexpr int kDma = kKj + kVj;
   static_assert(kKj * 64 * NW == kTileK * 24 && kVj * 64 * NW == kTileK * 16, "tile split");
+  // LDS fragment reads issued ahead of their products (K: of 24 per tile, V:
+  // of 32)
+  constexpr int kKAhead = 6;
+  constexpr int kVAhead = 8;
 
   // one array per stage (K tile then V tile); two stages take 80 KB, so two
   // 4-wavefront workgroups fit in one CU's 160 KB
-  __shared__ __attribute__((aligned(1024))) uint8_t S0[kKTile + kVTile], S1[kKTile + kVTile];
-  uint8_t* S2 = lds_stage2<NB>();
-  uint8_t *K0 = S0, *V0 = S0 + kKTile, *K1 = S1, *V1 = S1 + kKTile;
-  uint8_t *K2 = S2, *V2 = S2 + kKTile;
+  __shared__ __attribute__((aligned(1024))) uint8_t Sm[NB * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,28 +137,68 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint16_t* vbase = a.v + (int64_t)hs * a.vhs + (int64_t)k0 * kDv;
   const uint16_t* rbase = a.lat + (int64_t)k0 * a.ld_lat + kDc;
 
-  // DMA sources of this lane: chunk slot -> (key row, global chunk); keys at
-  // or past n_k are clamped to the last key (masked scores, p = 0 values), so
-  // no load needs a predicate.
+  // DMA sources of this lane: chunk slot -> (key row r, global chunk). For a
+  // tile inside the keys, a K chunk is read from base + off, where base is
+  // the tile's k_nope or k_rope start (two wavefront-uniform addresses) and
+  // off a per-lane byte offset fixed for the whole kernel; a V chunk from the
+  // tile's v start plus its offset. K offsets carry the chunk's row in bits
+  // 25-30 and a k_rope flag in bit 31 (the host keeps ld_lat <= 2^17, so the
+  // offset fits 25 bits); a V offset is row * 256 + chunk bytes. In the last,
+  // partial tile keys at or past n_k are clamped to the last key (masked
+  // scores, p = 0 values), so no load needs a predicate.
   const int klast = n_k - 1;
-  auto dma = [&](uint8_t* Kd, uint8_t* Vd, int kt0) {
+  uint32_t koffd[kKj], voffd[kVj];
 #pragma unroll
-    for (int j = 0; j < kKj; ++j) {
-      const int slot = (j * NW + wave) * 64 + lane;
-      const int r = slot / 24, c = slot % 24;
-      const int gc = (c & ~7) | ((c ^ (r >> 1)) & 7);
-      const int key = min(kt0 + r, klast);
-      const uint16_t* src = gc < 16 ? kbase + (int64_t)key * kDnope + gc * 8
-                                    : rbase + (int64_t)key * a.ld_lat + (gc - 16) * 8;
-      dma16(src, Kd + (j * NW + wave) * 1024);
-    }
+  for (int jj = 0; jj < kKj; ++jj) {
+    const int slot = (jj * NW + wave) * 64 + lane;
+    const int r = slot / 24, c = slot % 24;
+    const int gc = (c & ~7) | ((c ^ (r >> 1)) & 7);
+    koffd[jj] = (gc < 16 ? (uint32_t)(r * kDnope + gc * 8) * 2u
+                         : ((uint32_t)(r * a.ld_lat + (gc - 16) * 8) * 2u) | 0x80000000u) |
+                ((uint32_t)r << 25);
+  }
 #pragma unroll
-    for (int j = 0; j < kVj; ++j) {
-      const int slot = (j * NW + wave) * 64 + lane;
-      const int r = slot >> 4, c = slot & 15;
-      const int gc = c ^ ((r & 3) << 2);
-      const int key = min(kt0 + r, klast);
-      dma16(vbase + (int64_t)key * kDv + gc * 8, Vd + (j * NW + wave) * 1024);
+  for (int jj = 0; jj < kVj; ++jj) {
+    const int slot = (jj * NW + wave) * 64 + lane;
+    const int r = slot >> 4, c = slot & 15;
+    voffd[jj] = (uint32_t)(r * kDv + (c ^ ((r & 3) << 2)) * 8) * 2u;
+  }
+  auto dma = [&](uint8_t* St, int kt0) {
+    uint8_t* Kd = St;
+    uint8_t* Vd = St + kKTile;
+    const uint8_t* nb = reinterpret_cast<const uint8_t*>(kbase + (int64_t)kt0 * kDnope);
+    const uint8_t* rb = reinterpret_cast<const uint8_t*>(rbase + (int64_t)kt0 * a.ld_lat);
+    const int64_t rd = rb - nb;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vbase + (int64_t)kt0 * kDv);
+    // (the empty asm statements keep the compiler from hoisting per-lane
+    // values derived from the offsets out of the tile loop, which would hold
+    // extra registers for the whole kernel)
+    if (kt0 + kTileK - 1 <= klast) {
+#pragma unroll
+      for (int jj = 0; jj < kKj; ++jj) {
+        uint32_t o = koffd[jj];
+        asm volatile("" : "+v"(o));
+        dma16(nb + (o & 0x1ffffffu) + ((o >> 31) ? rd : (int64_t)0), Kd + (jj * NW + wave) * 1024);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kVj; ++jj) dma16s(vb, voffd[jj], Vd + (jj * NW + wave) * 1024);
+    } else {
+      // last tile: rows past the last key move back to it
+#pragma unroll
+      for (int jj = 0; jj < kKj; ++jj) {
+        uint32_t o = koffd[jj];
+        asm volatile("" : "+v"(o));
+        const int over = max(kt0 + (int)((o >> 25) & 63u) - klast, 0);
+        const int64_t back = (int64_t)over * ((o >> 31) ? a.ld_lat * 2 : (int64_t)kDnope * 2);
+        dma16(nb + (o & 0x1ffffffu) + ((o >> 31) ? rd : (int64_t)0) - back, Kd + (jj * NW + wave) * 1024);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kVj; ++jj) {
+        uint32_t o = voffd[jj];
+        asm volatile("" : "+v"(o));
+        const int over = max(kt0 + (int)(o >> 8) - klast, 0);
+        dma16(vb + o - (int64_t)over * kDv * 2, Vd + (jj * NW + wave) * 1024);
+      }
     }
   };
 
@@ -190,6 +222,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[d][i] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;     // reference max (scaled, log2 units), row sum
+  f32x16 S[2];                               // S^T of the current tile
+  bf16x8 P[4];                               // P^T operands of the tile being multiplied by V
+  bool rescale = false;                      // O needs the factor alpha_o before the next PV
+  float alpha_o = 1.f;
 
   // last key (exclusive) any row of this wavefront may see
   const int wave_kend = kCausal ? min(n_k, r0 + wave * 32 + 32 + shift) : n_k;
@@ -197,8 +233,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int row_lim = row + shift;           // causal: keys <= row_lim are visible
   const float c = a.scale_log2;              // scale * log2(e); scores stay raw until exp2
 
-  auto compute = [&](const uint8_t* Ks, const uint8_t* Vs, int kt0) {
-    f32x16 S[2];
+  // S^T = K . Q^T for one tile
+  auto qk = [&](const uint8_t* Ks) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -211,14 +247,18 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
       }
     }
-    // keep the K fragment reads six ahead of the products that use them
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    // keep the K fragment reads kKAhead ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
+    for (int i = 0; i < (24 - kKAhead) / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+  };
+
+  // online softmax of the tile in S (keys kt0..kt0+63) -> P, rescaling O
+  auto softmax = [&](int kt0) {
     // masking only on tiles that cross the key end or the causal diagonal
     const bool edge = (kt0 + kTileK > n_k) || (kCausal && kt0 + kTileK - 1 > wave_first_lim);
     if (edge) {
@@ -257,17 +297,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         ps += p;
       }
     l_run = fmaf(l_run, alpha, ps);
-    if (__any(bump)) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[d][i] *= alpha;
-    }
+    // O is rescaled by alpha right before the next PV products
+    rescale = __any(bump);
+    alpha_o = alpha;
     m_ref = m_new;
     // P^T operand of MFMA mm (keys 16mm..16mm+15 of the tile): lane slots
     // 0-3 hold keys 16mm+4g+0..3, slots 4-7 keys 16mm+8+4g+0..3, which is
-    // where the S^T accumulator layout puts them; the V^T operand is read
-    // for the same keys with two transposing reads.
+    // where the S^T accumulator layout puts them
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       const int kb = mm >> 1, i0 = 8 * (mm & 1);
@@ -276,58 +312,66 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       u.y = cvt_pk_bf16(S[kb][i0 + 2], S[kb][i0 + 3]);
       u.z = cvt_pk_bf16(S[kb][i0 + 4], S[kb][i0 + 5]);
       u.w = cvt_pk_bf16(S[kb][i0 + 6], S[kb][i0 + 7]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, u);
+      P[mm] = __builtin_bit_cast(bf16x8, u);
+    }
+  };
+
+  // O^T += V^T . P^T; the V^T operand is read for the P^T keys with two
+  // transposing reads
+  auto pv = [&](const uint8_t* Vs) {
+    if (rescale) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[d][i] *= alpha_o;
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint8_t* vp = Vs + voff[d] + 16 * mm * kVRow;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * kVRow));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[d], 0, 0, 0);
+        O[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[mm], O[d], 0, 0, 0);
       }
     }
-    // V reads one 16-key step (8 reads) ahead of the products
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+    // V reads kVAhead reads ahead of the products
+    __builtin_amdgcn_sched_group_barrier(0x100, kVAhead, 1);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < (32 - kVAhead) / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, kVAhead / 2, 1);
   };
 
-  // Pipeline over key tiles with NB LDS stages: step t waits for its own DMA
-  // of tile t, meets the others at the barrier (after which tile t is
+  auto stage = [&](int t) -> uint8_t* { return Sm + (t % NB) * kStage; };
+
+  // Pipeline over key tiles with NB LDS stages: step t waits for its own
+  // DMA of tile t, meets the others at the barrier (after which tile t is
   // visible and stage (t-1) % NB is free), issues the DMA of tile t+NB-1
   // into that stage and computes tile t. Tile indices past the end are
   // clamped to the last tile, so every step issues the same number of DMA
   // instructions and the vector-memory counter stays exact.
   const int last_kt0 = (ntiles - 1) * kTileK;
   if (ntiles > 0) {
-    dma(K0, V0, 0);
-    if (NB == 3) dma(K1, V1, min(kTileK, last_kt0));
+    dma(stage(0), 0);
+    if (NB == 3) dma(stage(1), min(kTileK, last_kt0));
   }
-  // the Q fragments (and the first tiles) have landed: without this wait the
-  // compiler, which does not see the DMA, would wait for every outstanding
-  // load before the first product of each tile
+  // the Q fragments (and the first tiles) have landed: without this wait
+  // the compiler, which does not see the DMA, would wait for every
+  // outstanding load before the first product of each tile
   wait_vmcnt<0>();
-  auto step = [&](int kt, uint8_t* Kc, uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
+  for (int kt = 0; kt < ntiles; ++kt) {
     const int kt0 = kt * kTileK;
     wait_vmcnt<kDma * (NB - 2)>();
     __syncthreads();
-    dma(Kn, Vn, min(kt0 + (NB - 1) * kTileK, last_kt0));
-    if (kt0 < wave_kend) compute(Kc, Vc, kt0);
-  };
-  if (NB == 3) {
-    for (int kt = 0; kt < ntiles; kt += 3) {
-      step(kt, K0, V0, K2, V2);
-      if (kt + 1 < ntiles) step(kt + 1, K1, V1, K0, V0);
-      if (kt + 2 < ntiles) step(kt + 2, K2, V2, K1, V1);
-    }
-  } else {
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      step(kt, K0, V0, K1, V1);
-      if (kt + 1 < ntiles) step(kt + 1, K1, V1, K0, V0);
+    dma(stage(kt + NB - 1), min(kt0 + (NB - 1) * kTileK, last_kt0));
+    if (kt0 < wave_kend) {
+      qk(stage(kt));
+      softmax(kt0);
+      pv(stage(kt) + kKTile);
     }
   }
   // no DMA may still be writing this workgroup's LDS when it ends
@@ -429,8 +473,8 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
               MLA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   MLA_REQUIRE(q_row_stride % 8 == 0 && q_row_stride >= (int64_t)H_q * kDqk, MLA_ERR_INVALID_ARG,
               "%s: q_row_stride (%lld) must be a multiple of 8 and >= H_q*192", fn, (long long)q_row_stride);
-  MLA_REQUIRE(ld_latent % 8 == 0 && ld_latent >= kDlat, MLA_ERR_INVALID_ARG,
-              "%s: ld_latent (%lld) must be a multiple of 8 and >= 576", fn, (long long)ld_latent);
+  MLA_REQUIRE(ld_latent % 8 == 0 && ld_latent >= kDlat && ld_latent <= (1 << 17), MLA_ERR_INVALID_ARG,
+              "%s: ld_latent (%lld) must be a multiple of 8 in [576, 2^17]", fn, (long long)ld_latent);
   MLA_REQUIRE(k_head_stride % 8 == 0 && v_head_stride % 8 == 0, MLA_ERR_INVALID_ARG,
               "%s: head strides must be multiples of 8", fn);
   const int Hsel = h_end - h_begin;
