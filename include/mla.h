@@ -182,6 +182,8 @@ int mla_decompress(const void* latent, int64_t ld_latent, int n_tokens,
  * A row with no visible key gets out = 0 and lse = -inf.
  *   q          device bf16; k_nope / v as written by mla_decompress
  *              (row t of head hs at hs * head_stride + t * 128).
+ *   latent     device bf16 rows of ld_latent elements, ld_latent a multiple
+ *              of 8 in [576, 2^17].
  *   out_dtype  MLA_DTYPE_BF16 or MLA_DTYPE_FP32.
  *   max_q      host; >= every n_q (sizes the launch).
  */

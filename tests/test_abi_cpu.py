@@ -166,3 +166,34 @@ def test_artifact_check_rejects_bad_arguments(lib):
     assert lib.mla_artifact_check(None, ctypes.byref(mla.ArtifactMeta()), ctypes.byref(reason)) == \
         _lib.MLA_ERR_INVALID_ARG
     assert reason.value == -7
+
+
+def test_attn_merge_cache_absorbed_validation(lib):
+    base = [FAKE, 8 * 192, 8, 0, 8, FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE, FAKE, None, 1, 10,
+            0.07, 0, FAKE, 8 * 128, FAKE, 8, FAKE, 2, 8 * 128, FAKE, 8]
+    args = list(base); args[18] = None                            # no previous state
+    assert _err(mla.mla_prefill_attn_merge, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[18] = FAKE + 4                        # misaligned previous state
+    assert _err(mla.mla_prefill_attn_merge, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[10] = (1 << 17) + 8                   # latent rows too wide
+    assert _err(mla.mla_prefill_attn_merge, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    # cache append: dtype, row stride, batch limit; empty work is a no-op
+    assert _err(mla.mla_cache_append, FAKE, 7, 4, FAKE, 4, FAKE, FAKE, 1, 8, FAKE, 576, None)[0] == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_cache_append, FAKE, 0, 4, FAKE, 4, FAKE, FAKE, 1, 8, FAKE, 512, None)[0] == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_cache_append, FAKE, 0, 4, FAKE, 4, FAKE, FAKE, 70000, 8, FAKE, 576, None)[0] == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert mla.mla_cache_append(None, 0, 0, None, 0, None, None, 0, 0, None, 576, None, stream=0) == 0
+    # absorbed form: head ranges, dtypes, strides
+    assert _err(mla.mla_absorb_q, FAKE, 8 * 192, 8, 3, 3, FAKE, 4, FAKE, 8, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_absorb_q, FAKE, 8 * 192, 8, 0, 8, FAKE, 4, FAKE, 4, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_absorbed_attn, FAKE, 4, FAKE, 576, FAKE, 1, 0.07, FAKE, 9, FAKE)[0] == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_absorbed_attn, FAKE, 4, FAKE, 500, FAKE, 1, 0.07, FAKE, 0, FAKE)[0] == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_absorbed_attn, FAKE, 4, FAKE, 576, FAKE, 1, -1.0, FAKE, 0, FAKE)[0] == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert mla.mla_absorbed_attn(None, 0, None, 576, None, 0, 0.07, None, 0, None, stream=0) == 0
+    assert _err(mla.mla_absorb_out, FAKE, 4, FAKE, 8, 0, 8, FAKE, 100)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_absorb_out, FAKE, 4, FAKE, 8, 2, 9, FAKE, 1024)[0] == _lib.MLA_ERR_INVALID_ARG
