@@ -227,8 +227,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   bool rescale = false;                      // O needs the factor alpha_o before the next PV
   float alpha_o = 1.f;
 
-  // last key (exclusive) any row of this wavefront may see
-  const int wave_kend = kCausal ? min(n_k, r0 + wave * 32 + 32 + shift) : n_k;
+  // last key (exclusive) any row of this wavefront may see; a wavefront
+  // whose rows all lie past the request's rows (the last row tile of a short
+  // request) sees none and only takes part in the DMA and the barriers
+  const int wave_kend = (r0 + wave * 32 >= n_q) ? 0
+                        : kCausal ? min(n_k, r0 + wave * 32 + 32 + shift) : n_k;
   const int wave_first_lim = r0 + wave * 32 + shift;   // causal: smallest row limit in the wave
   const int row_lim = row + shift;           // causal: keys <= row_lim are visible
   const float c = a.scale_log2;              // scale * log2(e); scores stay raw until exp2
