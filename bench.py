@@ -129,6 +129,45 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFI
     print(json.dumps(d))
 
 
+def timed_steps(torch, run, steps):
+    """Run `steps` steps bracketed by synchronisation, with an event before
+    each step and after the last; returns (mean ms, [ms per step])."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        run()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / max(steps, 1), per
+
+
+def step_stats(step_ms):
+    import statistics
+    return {"median_ms_per_step": round(statistics.median(step_ms), 4), "min_ms_per_step": round(min(step_ms), 4)}
+
+
+def gemm_reference(torch, n=8192, reps=10):
+    """The bf16 rate of the vendor GEMM (torch.matmul, hipBLASLt) on an
+    n x n x n product on this GPU: a measured ceiling for MFMA kernels at the
+    clock the GPU sustains under load, beside the published peak."""
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
+
+
 def cpu_baseline(prob, budget_s=15.0):
     """The fp64 oracle as it stands, on request 0 of the same workload, one
     head at a time, until about budget_s seconds of host work are spent."""
@@ -295,13 +334,7 @@ def bench_artifact(args, torch, mla, mla_inputs):
         b.run()
     torch.cuda.synchronize()
     assert int(b.dev_status.item()) == 0
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        b.run()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / max(args.steps, 1)
+    ms, step_ms = timed_steps(torch, b.run, args.steps)
     timer = KernelTimer()
     for _ in range(args.steps):
         b.run(timer=timer)
@@ -338,6 +371,7 @@ def bench_artifact(args, torch, mla, mla_inputs):
                         "kernel": kname, "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)},
            "kernels": kernels,
            "kernel_timing": "a second pass of the same number of steps with HIP events around every launch"}
+    res.update(step_stats(step_ms))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_artifact(ap)
     print(json.dumps(res))
@@ -421,17 +455,10 @@ def main():
     torch.cuda.synchronize()
     assert int(pre.dev_status.item()) == 0, "gather reported an out-of-range block"
 
-    # Timed steps for the headline value: one event pair around the steps
-    # (events around every launch would add a fence between kernels).
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        pre.run()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / max(args.steps, 1)
+    # Timed steps for the headline value: events only between steps (events
+    # around every launch would add a fence between kernels); the value uses
+    # the mean over the K steps, the median and min per step are reported too.
+    ms, step_ms = timed_steps(torch, pre.run, args.steps)
     # The same number of steps again with events around every launch, on the
     # stream the kernels run on: per-kernel durations for the breakdown and
     # the roofline of the dominant kernel.
@@ -509,6 +536,8 @@ def main():
         "kernels": kernels,
         "kernel_timing": "a second pass of the same number of steps with HIP events around every launch",
     }
+    res.update(step_stats(step_ms))
+    res["gemm_reference"] = gemm_reference(torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_reuse(prob) if reuse else cpu_baseline(prob)
     print(json.dumps(res))
