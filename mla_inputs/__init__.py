@@ -248,8 +248,8 @@ def make_reuse_problem(H=64, n_local=56, L=262144, T=512, delta=4096, P=64,
     q = _normal_bf16(rng, (T, H, D_QK))
     W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
     HL, HG = n_local, H - n_local
-    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / L)))
-    art_lse = (np.log(L) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
+    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / max(L, 1))))
+    art_lse = (np.log(max(L, 1)) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
     prot = np.sort(rng.choice(T, size=P, replace=False)).astype(np.int32)
     WaL = _normal_bf16(rng, (HL * D_V, d_mid), std=1.0 / np.sqrt(HL * D_V))
     WaG = _normal_bf16(rng, (HG * D_V, d_mid), std=1.0 / np.sqrt(HG * D_V))
@@ -281,8 +281,8 @@ def make_multidoc_problem(H=8, n_local=7, doc_lens=(512, 192, 1088), T=100, delt
     q = _normal_bf16(rng, (T, H, D_QK))
     W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
     HL, HG = n_local, H - n_local
-    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / Ltot)))
-    art_lse = (np.log(Ltot) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
+    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / max(Ltot, 1))))
+    art_lse = (np.log(max(Ltot, 1)) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
     prot = np.sort(rng.choice(T, size=P, replace=False)).astype(np.int32)
     WaL = _normal_bf16(rng, (HL * D_V, d_mid), std=1.0 / np.sqrt(HL * D_V))
     WaG = _normal_bf16(rng, (HG * D_V, d_mid), std=1.0 / np.sqrt(HG * D_V))

@@ -315,6 +315,15 @@ class ReusePrefill:
                 cu_qL=_i32(np.arange(kL + 1) * P, device), rid_L=_i32(np.tile(prot, kL), device)))
             n_pieces += k
             n_pieces_L += kL
+        if not self.chunks:
+            # no document keys at all: one empty chunk, whose attention writes
+            # the empty state (out 0, lse -inf) for every row
+            self.chunks.append(dict(
+                doc=0, start=_i32([0], device), len=_i32([0], device), cu=_i32([0, 0], device), n=0,
+                pieces=1, first=0, cu_k=_i32([0, 0], device), pieces_L=1, first_L=0, cu_kL=_i32([0, 0], device),
+                cu_qG=_i32([0, T], device), rid_G=_i32(np.arange(T), device),
+                cu_qL=_i32([0, P], device), rid_L=_i32(prot, device)))
+            n_pieces = n_pieces_L = 1
         self.max_chunk = max([c["n"] for c in self.chunks] + [1])
         self.n_pieces = n_pieces
         self.n_pieces_L = n_pieces_L
@@ -577,6 +586,8 @@ class ArtifactBuilder:
             self.acc = torch.empty((self.R, HL, D_V), dtype=f32, device=device)
             self.acc_lse = torch.empty((self.R, HL), dtype=f32, device=device)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
+        self._cu_rows = _i32([0, self.R], device)
+        self._cu_none = _i32([0, 0], device)
         self.meta = artifact_meta(tokens if tokens is not None else np.zeros(0, np.int32), generation, H,
                                   n_local, rope_base, n_layers, (layer,))
         if tokens is not None and len(tokens) != self.L:
@@ -602,6 +613,13 @@ class ArtifactBuilder:
 
     def run(self, stream=None, timer=None) -> Artifact:
         n_ch = len(self.chunks)
+        if n_ch == 0 and self.R > 0 and self.HL > 0:
+            # an empty document: every row sees no key, so the attention over
+            # an empty key range writes out = 0 and lse = -inf
+            with _span(timer, "attn_full"):
+                L.mla_prefill_attn(self.q, self.H * D_QK, self.H, 0, self.HL, self.k_ws, self.hstride, self.v_ws,
+                                   self.hstride, self.lat_ws, D_LAT, self._cu_rows, self._cu_none, None, 1, self.R,
+                                   self.scale, 0, self.out, L.DTYPE_BF16, self.HL * D_V, self.lse, self.HL, stream)
         for ci, ch in enumerate(self.chunks):
             first, last = ci == 0, ci == n_ch - 1
             with _span(timer, "gather"):
@@ -622,7 +640,7 @@ class ArtifactBuilder:
                 with _span(timer, "attn_causal"):
                     self._attn(ch["s0"], ch["n"], ch["cu"], ch["cu"], True, merge=not first, final=True,
                                stream=stream)
-        return Artifact(self.out[:self.R], self.lse[:self.R], self.meta)
+        return Artifact(self.out[:self.R, :self.HL], self.lse[:self.R, :self.HL], self.meta)
 
     def work(self) -> dict:
         """Algorithmic work of one build: decompression of the Local heads

@@ -53,6 +53,21 @@ def test_artifact_build_parity(doc_rows, chunk, extra):
     assert art.meta.n_tokens == ap.L and art.meta.generation == ap.generation
 
 
+def test_artifact_of_an_empty_document():
+    """No document keys: every row's Local-head state is (0, -inf), the
+    identity of the merge."""
+    require_gpu()
+    ap = mi.make_artifact_problem(H=4, n_local=3, L=64, extra_rows=40, doc_rows=False, chunk=64, seed=48)
+    b = ArtifactBuilder(ap.pool, ap.block_table, 0, ap.q, ap.W, ap.H, ap.n_local, ap.scale, doc_rows=False,
+                        chunk=64, tokens=ap.tokens[:0], generation=1)
+    art = b.run()
+    torch.cuda.synchronize()
+    assert tuple(art.out.shape) == (40, 3, 128) and tuple(art.lse.shape) == (40, 3)
+    assert np.all(f64(art.out) == 0.0)
+    assert np.all(np.isneginf(f64(art.lse)))
+    assert art.meta.n_tokens == 0
+
+
 def _request_meta(prob, tokens, generation, **kw):
     m = artifact_meta(tokens, generation, prob.H, prob.n_local, prob.rope_base)
     for k, v in kw.items():

@@ -140,6 +140,29 @@ def test_multidoc_reuse_all_outputs(split, split_local, chunk, local):
     say(f"  y max-abs {ma:.2e} rel-L2 {r:.2e}")
 
 
+@pytest.mark.parametrize("local", ["absorbed", "decompressed"])
+def test_reuse_with_empty_documents(local):
+    """Degenerate documents: a request whose only document is empty (every
+    recomputed row sees no key: out 0, lse -inf), and empty documents among
+    non-empty ones (they contribute nothing)."""
+    require_gpu()
+    say(f"reuse with empty documents ({local})")
+    for prob in (mi.make_reuse_problem(H=4, n_local=3, L=0, T=20, delta=4096, P=3, d_mid=128, d_model=128,
+                                       chunk=256, seed=49),
+                 mi.make_multidoc_problem(doc_lens=(0, 128, 0, 64), T=30, P=4, seed=50, d_mid=128, d_model=128)):
+        pre = ReusePrefill(prob, split=64, split_local=64, local_path=local)
+        y = pre.run()
+        torch.cuda.synchronize()
+        ref = orc.reuse_reference(prob)
+        # 192 document keys in the second problem: the few-key lse bound
+        tol = LSE_FEW_KEYS if pre.Ldoc < FEW_KEYS else LSE_ABS
+        check_out(f64(pre.glob_out), ref["O_G"], what="O_G")
+        check_lse(f64(pre.lse_G), ref["lse_G"], tol=tol, what="lse_G")
+        check_out(f64(pre.rec_out), ref["rec"], what="rec")
+        check_lse(f64(pre.lse_L), ref["rec_lse"], tol=tol, what="rec_lse")
+        check_out(f64(y), ref["y"], what="y")
+
+
 def test_multidoc_offsets_are_per_document():
     """Relocating every document by the first one's offset must miss the
     oracle: each document's queries are rotated by its own offset."""
