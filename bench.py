@@ -168,6 +168,27 @@ def gemm_reference(torch, n=8192, reps=10):
     return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
 
 
+def mfma_calibration(torch):
+    """Sustained v_mfma_f32_32x32x16_bf16 rate on this GPU (independent
+    chains on every SIMD, libmla_calib.so), or None if that library is not
+    built."""
+    import ctypes
+    path = os.path.join(ROOT, "mla_long_context_amd", "libmla_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mla_calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_double)]
+    lib.mla_calib_mfma_bf16.restype = ctypes.c_int
+    wgs = 4 * 256
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    r = ctypes.c_double(0.0)
+    if lib.mla_calib_mfma_bf16(out.data_ptr(), wgs, 20000, 3, ctypes.byref(r)) != 0:
+        return None
+    return {"op": "independent v_mfma_f32_32x32x16_bf16 chains, 16 wavefronts per CU", "tflops": round(r.value, 1)}
+
+
 def cpu_baseline(prob, budget_s=15.0):
     """The fp64 oracle as it stands, on request 0 of the same workload, one
     head at a time, until about budget_s seconds of host work are spent."""
@@ -538,6 +559,7 @@ def main():
     }
     res.update(step_stats(step_ms))
     res["gemm_reference"] = gemm_reference(torch)
+    res["mfma_sustained"] = mfma_calibration(torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_reuse(prob) if reuse else cpu_baseline(prob)
     print(json.dumps(res))

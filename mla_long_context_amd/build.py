@@ -71,7 +71,25 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
+    build_calib(verbose)
     return LIB
+
+
+CALIB_SRC = os.path.join(PKG, "calib", "mfma_peak.hip")
+CALIB_LIB = os.path.join(PKG, "libmla_calib.so")
+
+
+def build_calib(verbose: bool = False) -> str:
+    """The benchmark's MFMA calibration library (not part of libmla.so)."""
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-shared", CALIB_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the calibration library:\n" + r.stdout + r.stderr)
+    os.replace(tmp, CALIB_LIB)
+    if verbose:
+        print(f"built {CALIB_LIB}")
+    return CALIB_LIB
 
 
 if __name__ == "__main__":
