@@ -90,6 +90,7 @@ int mla_abi_version(void);
  *               byte 32768, per-token fp32 scale [64] at byte 40960.
  *   block_table device int32 [batch][bt_stride].
  *   chunk_start, chunk_len, cu_out  device int32 [batch], [batch], [batch+1].
+ *   batch       host, <= 65535.
  *   max_len     host; >= every chunk_len[b] (sizes the launch).
  *   out_latent  device bf16 [cu_out[batch]][576], row stride 576.
  *   dev_status  device int32 or NULL. A block id outside [0, num_blocks)

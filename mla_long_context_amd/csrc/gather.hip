@@ -2,18 +2,21 @@
 // and Chunked Prefill, section 4.4 step 1; 64-token blocks per "PagedAttention
 // assumed MHA", section "Block size is not a tuning knob here").
 //
-// HBM-bound copy. A token record is 1152 bytes = 72 vectors of 16 bytes;
-// one thread moves one 16-byte vector, so a wavefront reads and writes
-// consecutive bytes of consecutive records (a cache block holds its 64
-// records contiguously). fp8 cache: vectors 0..63 of a record are 8 E4M3FN
-// codes each (8 bytes in, 16 bytes of bf16 out), vectors 64..71 copy the
-// bf16 rope key.
+// HBM-bound copy. A token record is 1152 bytes = 72 vectors of 16 bytes; the
+// chunk's records form one stream of vectors. A workgroup moves kVPT * 256
+// consecutive vectors, thread i the vectors i, i + 256, ... of that range, so
+// every wavefront instruction reads and writes 1 KB of consecutive bytes (a
+// cache block holds its 64 records contiguously), and each thread issues all
+// its loads before its stores (kVPT loads in flight). fp8 cache: vectors
+// 0..63 of a record are 8 E4M3FN codes each (8 bytes in, 16 bytes of bf16
+// out), vectors 64..71 copy the bf16 rope key.
 #include "mla_internal.h"
 
 namespace {
 
 constexpr int kVecPerTok = kDlat * 2 / 16;   // 72
 constexpr int kThreads = 256;
+constexpr int kVPT = 4;                      // vectors per thread
 
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
@@ -25,21 +28,25 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   const int start = cstart[b];
   const int64_t obase = cu_out[b];
   const int64_t nvec = (int64_t)len * kVecPerTok;
-  const int64_t step = (int64_t)gridDim.x * kThreads;
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nvec; g += step) {
+  const int64_t g0 = (int64_t)blockIdx.x * (kThreads * kVPT) + threadIdx.x;
+  if (g0 >= nvec) return;
+  u32x4 val[kVPT];
+#pragma unroll
+  for (int k = 0; k < kVPT; ++k) {
+    val[k] = u32x4{0u, 0u, 0u, 0u};
+    const int64_t g = g0 + k * kThreads;
+    if (g >= nvec) continue;
     const int i = (int)(g / kVecPerTok);
     const int v = (int)(g - (int64_t)i * kVecPerTok);
     const int t = start + i;
     const int lb = t >> 6;
     const int slot = t & 63;
-    int blk = -1;
-    if (t >= 0 && lb < bt_stride) blk = bt[(int64_t)b * bt_stride + lb];
-    u32x4 val = {0u, 0u, 0u, 0u};
+    const int blk = (t >= 0 && lb < bt_stride) ? bt[(int64_t)b * bt_stride + lb] : -1;
     if (blk < 0 || blk >= num_blocks) {
-      if (status) status[0] = MLA_ERR_OUT_OF_RANGE;
+      if (status) status[0] = MLA_ERR_OUT_OF_RANGE;   // the vector is written as zeros
     } else if (!kFp8) {
       const u32x4* src = reinterpret_cast<const u32x4*>(pool + ((int64_t)blk * kBlock + slot) * (kDlat * 2));
-      val = __builtin_nontemporal_load(src + v);
+      val[k] = __builtin_nontemporal_load(src + v);
     } else {
       const uint8_t* base = pool + (int64_t)blk * kFp8BlockBytes;
       if (v < 64) {
@@ -51,15 +58,18 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
           const uint32_t c = ((j < 4 ? codes.x : codes.y) >> (8 * (j & 3))) & 0xffu;
           f[j] = e4m3fn_to_f32(c) * sc;
         }
-        val.x = pack_bf16x2(f[0], f[1]);
-        val.y = pack_bf16x2(f[2], f[3]);
-        val.z = pack_bf16x2(f[4], f[5]);
-        val.w = pack_bf16x2(f[6], f[7]);
+        val[k] = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                       pack_bf16x2(f[6], f[7])};
       } else {
-        val = *reinterpret_cast<const u32x4*>(base + kFp8RopeOff + slot * (kDrope * 2) + (v - 64) * 16);
+        val[k] = *reinterpret_cast<const u32x4*>(base + kFp8RopeOff + slot * (kDrope * 2) + (v - 64) * 16);
       }
     }
-    reinterpret_cast<u32x4*>(out + (obase + i) * kDlat)[v] = val;
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(out + obase * kDlat);
+#pragma unroll
+  for (int k = 0; k < kVPT; ++k) {
+    const int64_t g = g0 + k * kThreads;
+    if (g < nvec) dst[g] = val[k];
   }
 }
 
@@ -83,9 +93,9 @@ extern "C" int mla_gather_context(const void* pool, int cache_dtype, int num_blo
               MLA_ERR_UNSUPPORTED, "mla_gather_context: cache dtype %d not supported", cache_dtype);
   MLA_REQUIRE(mla_aligned16(pool) && mla_aligned16(out_latent), MLA_ERR_INVALID_ARG,
               "mla_gather_context: pool and out_latent must be 16-byte aligned");
-  const int64_t nvec = (int64_t)max_len * kVecPerTok;
-  int64_t gx = (nvec + kThreads * 4 - 1) / (kThreads * 4);   // ~4 vectors per thread
-  if (gx > 65535) gx = 65535;
+  MLA_REQUIRE(batch <= 65535, MLA_ERR_INVALID_ARG, "mla_gather_context: batch (%d) must be <= 65535", batch);
+  const int64_t gx = ((int64_t)max_len * kVecPerTok + kThreads * kVPT - 1) / (kThreads * kVPT);
+  MLA_REQUIRE(gx < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_gather_context: max_len too large");
   dim3 grid((unsigned)gx, (unsigned)batch);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (cache_dtype == MLA_DTYPE_BF16)
