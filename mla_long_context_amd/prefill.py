@@ -235,7 +235,7 @@ class ReusePrefill:
     a log-depth tree of mla_merge_states calls. By the merge identity this
     equals the chunk-by-chunk merge."""
 
-    def __init__(self, prob, device="cuda", chunk=None, split=2048, local_path="absorbed",
+    def __init__(self, prob, device="cuda", chunk=None, split=4096, local_path="absorbed",
                  split_local=8192, artifact=None, request=None):
         assert prob.is_reuse
         assert local_path in ("absorbed", "decompressed")
