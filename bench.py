@@ -12,7 +12,8 @@ Inputs are seeded synthetic data resident in HBM before timing starts.
 
 Prints one JSON line: TFLOP/s of algorithmic work (2*512*256 flop per
 decompressed (token, head), 640 flop per visible (row, key, head)) over the
-timed steps, prefill tokens/s, the roofline of the dominant kernel (per-launch
+timed steps (eager launches; --graph replays one step captured into a HIP
+graph), prefill tokens/s, the roofline of the dominant kernel (per-launch
 duration from HIP events on the launch stream, taken in a second pass of the
 same number of steps, since events between launches add fences to the step),
 and the fp64 CPU oracle timed on a bounded sample on this host.
@@ -355,7 +356,9 @@ def bench_artifact(args, torch, mla, mla_inputs):
         b.run()
     torch.cuda.synchronize()
     assert int(b.dev_status.item()) == 0
-    ms, step_ms = timed_steps(torch, b.run, args.steps)
+    from mla_long_context_amd.prefill import GraphStep
+    step = GraphStep(b).replay if args.graph else b.run
+    ms, step_ms = timed_steps(torch, step, args.steps)
     timer = KernelTimer()
     for _ in range(args.steps):
         b.run(timer=timer)
@@ -391,7 +394,8 @@ def bench_artifact(args, torch, mla, mla_inputs):
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                         "kernel": kname, "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)},
            "kernels": kernels,
-           "kernel_timing": "a second pass of the same number of steps with HIP events around every launch"}
+           "step_launch": "replay of one step captured into a HIP graph" if args.graph else "eager launches",
+           "kernel_timing": "a second pass of the same number of steps, launched eagerly with HIP events around every launch"}
     res.update(step_stats(step_ms))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_artifact(ap)
@@ -416,6 +420,8 @@ def main():
     ap.add_argument("--artifact", action="store_true",
                     help="time the offline Local-head artifact build instead (65536-token document, "
                          "56 Local heads of 64, every document row)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured into a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
@@ -448,7 +454,7 @@ def main():
 
     import mla_inputs
     import mla_long_context_amd as mla
-    from mla_long_context_amd.prefill import ChunkedPrefill, ReusePrefill
+    from mla_long_context_amd.prefill import ChunkedPrefill, GraphStep, ReusePrefill
 
     if args.append:
         bench_append(args, torch, mla, mla_inputs)
@@ -475,11 +481,17 @@ def main():
         pre.run()
     torch.cuda.synchronize()
     assert int(pre.dev_status.item()) == 0, "gather reported an out-of-range block"
+    # Eager launches by default; --graph replays one step captured into a
+    # HIP graph instead (measured equal or slightly slower: the launches are
+    # asynchronous and keep the GPU's queue full).
+    step = GraphStep(pre).replay if args.graph else pre.run
+    for _ in range(args.warmup):
+        step()
 
     # Timed steps for the headline value: events only between steps (events
     # around every launch would add a fence between kernels); the value uses
     # the mean over the K steps, the median and min per step are reported too.
-    ms, step_ms = timed_steps(torch, pre.run, args.steps)
+    ms, step_ms = timed_steps(torch, step, args.steps)
     # The same number of steps again with events around every launch, on the
     # stream the kernels run on: per-kernel durations for the breakdown and
     # the roofline of the dominant kernel.
@@ -555,7 +567,8 @@ def main():
         "mfma_roofline_frac_whole_step": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "kernels": kernels,
-        "kernel_timing": "a second pass of the same number of steps with HIP events around every launch",
+        "step_launch": "replay of one step captured into a HIP graph" if args.graph else "eager launches",
+        "kernel_timing": "a second pass of the same number of steps, launched eagerly with HIP events around every launch",
     }
     res.update(step_stats(step_ms))
     res["gemm_reference"] = gemm_reference(torch)

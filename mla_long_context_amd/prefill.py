@@ -653,3 +653,30 @@ class ArtifactBuilder:
         return dict(dec_flops=2 * 512 * 256 * HL * L_, attn_flops=640 * HL * pairs,
                     causal_attn_flops=640 * HL * causal, full_attn_flops=640 * HL * (pairs - causal),
                     gather_bytes=L_ * 2304, rows=self.R, doc_tokens=L_)
+
+
+class GraphStep:
+    """One step of a driver (ChunkedPrefill, ReusePrefill, ArtifactBuilder)
+    captured once into a HIP graph and replayed: the same kernels on the same
+    buffers, without a host launch per kernel. The driver's buffers must stay
+    alive and in place while the graph is used. Capture runs on a side stream
+    (as torch requires); replay() enqueues on the current stream."""
+
+    def __init__(self, driver, warmup=1):
+        self.driver = driver
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                driver.run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            driver.run()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
+
+    run = replay
