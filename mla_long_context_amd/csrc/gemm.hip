@@ -3,7 +3,7 @@
 //   * kv_b_proj decompression (DeepSeek MLA -- Prefix Cache and Chunked
 //     Prefill, section 4.4 step 2): A = c_kv rows of the gathered latent,
 //     Bt = packed [W_UK | W_UV], output split per head into k_nope and v.
-//     Its own kernel (decompress_kernel) keeps a head's weight slice in LDS.
+//     It has its own persistent, DMA-fed kernel (decompress_kernel).
 //   * the sliced first output projection and the shared second projection of
 //     the Local/Global head partition (RedKnot-MLA, sections 1-3, Equation 4),
 //     with protected-row replacement fused into the A-operand load
@@ -258,11 +258,13 @@ struct DecArgs {
 };
 
 // rank (0 .. n_mt*n_nt-1) -> (token tile, column tile): consecutive ranks
-// walk kGroupM token tiles x all column tiles, so the workgroups of one XCD,
-// which take consecutive ranks together, share 4 latent tiles and 8 weight
-// tiles (3 MB) in that XCD's L2.
+// walk kGroupM token tiles x all column tiles, so the 32 workgroups of one
+// XCD, which take consecutive ranks together, share 6 latent tiles and 5-6
+// weight tiles (3 MB) in that XCD's L2. Groups of 3 to 10 token tiles
+// measured alike; powers of two (2, 4, 8) were 10-13% slower on some shapes
+// (16384 tokens x 128 heads, and 8 heads).
 __device__ __forceinline__ void dec_tile(int rank, int n_mt, int n_nt, int& mt, int& nt) {
-  constexpr int kGroupM = 4;
+  constexpr int kGroupM = 6;
   const int per_group = kGroupM * n_nt;
   const int first_mt = (rank / per_group) * kGroupM;
   const int gm = min(n_mt - first_mt, kGroupM);
