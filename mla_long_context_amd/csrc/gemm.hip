@@ -9,23 +9,26 @@
 //     with protected-row replacement fused into the A-operand load
 //     (gemm_nt_kernel).
 //
-// gemm_nt_kernel tiling: 256 threads (4 wavefronts of 64), a 128 x 128 output tile per
-// workgroup, K in steps of 64 through double-buffered LDS; each wavefront
-// owns a 64 x 64 sub-tile as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks. The MFMA
-// is issued as D^T = Bt_frag x A_frag so that each lane ends up holding four
-// consecutive output columns of one row, which the epilogue packs into 8-byte
-// LDS writes before 16-byte coalesced global stores.
+// gemm_nt_kernel tiling: 256 threads (4 wavefronts of 64), a TB x TB output
+// tile per workgroup (TB = 128, or 64 when 128-wide tiles would leave most
+// compute units idle), K in steps of 64 through double-buffered LDS; each
+// wavefront owns a TB/2 x TB/2 sub-tile as blocks of v_mfma_f32_32x32x16_bf16.
+// The global loads of a k step are issued kPre steps (8 with 64-wide tiles,
+// 4 with 128-wide ones) before the step is computed (a ring of register
+// slots), so that a long K loop is not paced by one load latency per step. The MFMA is issued as D^T = Bt_frag x A_frag so
+// that each lane ends up holding four consecutive output columns of one row,
+// which the epilogue packs into 8-byte LDS writes before 16-byte coalesced
+// global stores.
 #include <algorithm>
 
 #include "mla_internal.h"
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kLdsK = BK + 8;            // padded row (elements): 144 B, conflict-free b128 reads
-constexpr int kLdsC = BN + 8;            // padded epilogue row
-constexpr int kTileElems = BM * kLdsK;   // one operand tile
+constexpr int kTileMin = 128;            // both tile sizes divide multiples of this
 
 // ---------------------------------------------------------------- problem policies
 
@@ -39,9 +42,10 @@ struct SlicedProjP {
 
   __device__ int rows() const { return T; }
   __device__ int K() const { return Kt; }
+  // pointers of row t's two column ranges (k < ksplit: the Local part, else
+  // the Global part indexed with the global k); t < T
   __device__ void a_rows(int t, const uint16_t*& pl, const uint16_t*& pg, int& ksplit) const {
     ksplit = HL * kDv;
-    if (t >= T) { pl = pg = nullptr; return; }
     // binary search of t among the strictly increasing protected rows
     int lo = 0, hi = P;
     while (lo < hi) {
@@ -52,9 +56,9 @@ struct SlicedProjP {
     pl = is_prot ? rec + (int64_t)lo * HL * kDv : art + (int64_t)t * HL * kDv;
     pg = glob + (int64_t)t * HG * kDv - ksplit;   // indexed with the global k
   }
-  __device__ const uint16_t* b_row(int nt, int r) const { return wt + ((int64_t)nt * BN + r) * Kt; }
-  __device__ void store(int t, int nt, int vec, u32x4 val) const {
-    *reinterpret_cast<u32x4*>(z + (int64_t)t * ldz + nt * BN + vec * 8) = val;
+  __device__ const uint16_t* b_row(int n) const { return wt + (int64_t)n * Kt; }
+  __device__ void store(int t, int n, u32x4 val) const {
+    *reinterpret_cast<u32x4*>(z + (int64_t)t * ldz + n) = val;
   }
 };
 
@@ -65,20 +69,26 @@ struct PlainP {
   __device__ int rows() const { return T; }
   __device__ int K() const { return Kt; }
   __device__ void a_rows(int t, const uint16_t*& pl, const uint16_t*& pg, int& ksplit) const {
-    pl = t < T ? a + (int64_t)t * Kt : nullptr;
-    pg = nullptr;
+    pl = a + (int64_t)t * Kt;
+    pg = pl;
     ksplit = Kt;
   }
-  __device__ const uint16_t* b_row(int nt, int r) const { return wt + ((int64_t)nt * BN + r) * Kt; }
-  __device__ void store(int t, int nt, int vec, u32x4 val) const {
-    *reinterpret_cast<u32x4*>(d + (int64_t)t * ldd + nt * BN + vec * 8) = val;
+  __device__ const uint16_t* b_row(int n) const { return wt + (int64_t)n * Kt; }
+  __device__ void store(int t, int n, u32x4 val) const {
+    *reinterpret_cast<u32x4*>(d + (int64_t)t * ldd + n) = val;
   }
 };
 
 // ---------------------------------------------------------------- kernel
 
-template <class P>
+template <class P, int TB>
 __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(P p, int n_mt, int n_nt) {
+  constexpr int kTileElems = TB * kLdsK;   // one operand tile
+  constexpr int kLdsC = TB + 8;            // padded epilogue row
+  constexpr int RPT = TB / 32;             // rows each thread loads per operand
+  constexpr int NBK = TB / 64;             // 32 x 32 blocks per wavefront and dimension
+  constexpr int kPre = TB == 64 ? 8 : 4;   // k steps whose loads are in flight
+  static_assert(TB * kLdsC <= 4 * kTileElems, "epilogue tile fits the operand buffers");
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kTileElems];   // A0 B0 A1 B1
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -89,108 +99,138 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(P p, int n_mt, int n_
   const uint32_t work = xcd_remap(blockIdx.x, (uint32_t)(n_mt * n_nt));
   const int mt = (int)(work % (uint32_t)n_mt);
   const int nt = (int)(work / (uint32_t)n_mt);
-  const int t0 = mt * BM;
+  const int t0 = mt * TB, n0 = nt * TB;
 
-  // each thread loads 4 rows x one 16-byte vector of the A and B tiles per k-step
+  // each thread loads RPT rows x one 16-byte vector of the A and B tiles per k step
   const int lrow = tid >> 3, lvec = tid & 7;
-  const uint16_t* apl[4];
-  const uint16_t* apg[4];
-  const uint16_t* bp[4];
+  // Rows past the last one load row M-1 and are zeroed when written to LDS,
+  // so no load is predicated (the compiler then tracks each slot's loads
+  // exactly and waits only for the slot it moves into LDS).
+  const int M = p.rows();
+  const uint16_t* apl[RPT];
+  const uint16_t* apg[RPT];
+  const uint16_t* bp[RPT];
+  bool aval[RPT];
   int ksplit = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p.a_rows(t0 + lrow + 32 * i, apl[i], apg[i], ksplit);
-    bp[i] = p.b_row(nt, lrow + 32 * i);
+  for (int i = 0; i < RPT; ++i) {
+    const int t = t0 + lrow + 32 * i;
+    aval[i] = t < M;
+    p.a_rows(min(t, M - 1), apl[i], apg[i], ksplit);
+    bp[i] = p.b_row(n0 + lrow + 32 * i);
   }
   const int K = p.K();
   const int nk = K / BK;
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
+  u32x4 ra[kPre][RPT], rb[kPre][RPT];
+  auto gload = [&](int slot, int kt) __attribute__((always_inline)) {
     const int k = kt * BK + lvec * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RPT; ++i) {
       const uint16_t* src = k < ksplit ? apl[i] : apg[i];
-      ra[i] = src ? *reinterpret_cast<const u32x4*>(src + k) : u32x4{0u, 0u, 0u, 0u};
-      rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + k);
+      ra[slot][i] = *reinterpret_cast<const u32x4*>(src + k);
+      rb[slot][i] = *reinterpret_cast<const u32x4*>(bp[i] + k);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int slot, int buf) __attribute__((always_inline)) {
     uint16_t* As = lds + (2 * buf) * kTileElems;
     uint16_t* Bs = lds + (2 * buf + 1) * kTileElems;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(As + (lrow + 32 * i) * kLdsK + lvec * 8) = ra[i];
-      *reinterpret_cast<u32x4*>(Bs + (lrow + 32 * i) * kLdsK + lvec * 8) = rb[i];
+    for (int i = 0; i < RPT; ++i) {
+      *reinterpret_cast<u32x4*>(As + (lrow + 32 * i) * kLdsK + lvec * 8) =
+          aval[i] ? ra[slot][i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(Bs + (lrow + 32 * i) * kLdsK + lvec * 8) = rb[slot][i];
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[NBK][NBK];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NBK; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NBK; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* As = lds + (2 * cur) * kTileElems;
-    const uint16_t* Bs = lds + (2 * cur + 1) * kTileElems;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const uint16_t* As = lds + (2 * buf) * kTileElems;
+    const uint16_t* Bs = lds + (2 * buf + 1) * kTileElems;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[NBK], bfr[NBK];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        af[tb] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + tb * 32 + l32) * kLdsK + ks * 16 + g * 8);
+      for (int tb = 0; tb < NBK; ++tb)
+        af[tb] = *reinterpret_cast<const bf16x8*>(As + (wm * (TB / 2) + tb * 32 + l32) * kLdsK + ks * 16 + g * 8);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + nb * 32 + l32) * kLdsK + ks * 16 + g * 8);
+      for (int nb = 0; nb < NBK; ++nb)
+        bfr[nb] = *reinterpret_cast<const bf16x8*>(Bs + (wn * (TB / 2) + nb * 32 + l32) * kLdsK + ks * 16 + g * 8);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NBK; ++nb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < NBK; ++tb)
           acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[tb], acc[nb][tb], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  };
+
+  // Step kt: refill slot kt % kPre with the loads of step kt + kPre, compute
+  // step kt from LDS buffer kt & 1, move step kt + 1 from its register slot
+  // into the other buffer (last read in step kt - 1, before the previous
+  // barrier), then meet the other wavefronts. Steps past the last are
+  // clamped to it (loaded again, never computed), so every step issues the
+  // same loads.
+#pragma unroll
+  for (int s2 = 0; s2 < kPre; ++s2) gload(s2, min(s2, nk - 1));
+  lstore(0, 0);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < nk; kt0 += kPre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nk) {
+        gload(u, min(kt + kPre, nk - 1));
+        compute(u & 1);
+        lstore((u + 1) % kPre, (u + 1) & 1);
+        __syncthreads();
+      }
+    }
   }
 
   // epilogue: lane holds D^T rows n = 8*(i/4) + 4*g + (i%4), column t = l32
   uint16_t* Cs = lds;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < NBK; ++nb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < NBK; ++tb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int t = wm * 64 + tb * 32 + l32;
-        const int n = wn * 64 + nb * 32 + 8 * q + 4 * g;
+        const int t = wm * (TB / 2) + tb * 32 + l32;
+        const int n = wn * (TB / 2) + nb * 32 + 8 * q + 4 * g;
         u32x2 w;
         w.x = pack_bf16x2(acc[nb][tb][4 * q + 0], acc[nb][tb][4 * q + 1]);
         w.y = pack_bf16x2(acc[nb][tb][4 * q + 2], acc[nb][tb][4 * q + 3]);
         *reinterpret_cast<u32x2*>(Cs + t * kLdsC + n) = w;
       }
   __syncthreads();
-  const int M = p.rows();
 #pragma unroll
-  for (int i = 0; i < (BM * BN / 8) / kThreads; ++i) {
+  for (int i = 0; i < (TB * TB / 8) / kThreads; ++i) {
     const int idx = tid + i * kThreads;
-    const int r = idx >> 4, vec = idx & 15;
-    if (t0 + r < M) p.store(t0 + r, nt, vec, *reinterpret_cast<const u32x4*>(Cs + r * kLdsC + vec * 8));
+    const int r = idx / (TB / 8), vec = idx % (TB / 8);
+    if (t0 + r < M) p.store(t0 + r, n0 + vec * 8, *reinterpret_cast<const u32x4*>(Cs + r * kLdsC + vec * 8));
   }
 }
 
 template <class P>
 int launch_gemm(const P& p, int M, int N, hipStream_t s, const char* what) {
-  const int n_mt = (M + BM - 1) / BM, n_nt = N / BN;
-  const int64_t total = (int64_t)n_mt * n_nt;
-  MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "%s: problem too large", what);
-  hipLaunchKernelGGL(gemm_nt_kernel<P>, dim3((unsigned)total), dim3(kThreads), 0, s, p, n_mt, n_nt);
+  // 128-wide tiles unless they would give fewer workgroups than compute units
+  const int ncu = std::max(mla_num_cus(), 1);
+  const int64_t big = (int64_t)((M + 127) / 128) * (N / 128);
+  if (big >= ncu) {
+    const int n_mt = (M + 127) / 128, n_nt = N / 128;
+    MLA_REQUIRE(big < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "%s: problem too large", what);
+    hipLaunchKernelGGL((gemm_nt_kernel<P, 128>), dim3((unsigned)big), dim3(kThreads), 0, s, p, n_mt, n_nt);
+  } else {
+    const int n_mt = (M + 63) / 64, n_nt = N / 64;
+    hipLaunchKernelGGL((gemm_nt_kernel<P, 64>), dim3((unsigned)(n_mt * n_nt)), dim3(kThreads), 0, s, p, n_mt, n_nt);
+  }
   return mla_check_launch(what);
 }
 
@@ -552,7 +592,7 @@ extern "C" int mla_head_partition_merge(const void* art_out, const void* rec_out
   MLA_REQUIRE(wa_t && wb_t && z && y && (HL == 0 || art_out) && (HG == 0 || glob_out) &&
                   (P == 0 || (rec_out && prot_rows)),
               MLA_ERR_INVALID_ARG, "mla_head_partition_merge: null pointer argument");
-  MLA_REQUIRE(d_mid > 0 && d_model > 0 && d_mid % BN == 0 && d_model % BN == 0, MLA_ERR_UNSUPPORTED,
+  MLA_REQUIRE(d_mid > 0 && d_model > 0 && d_mid % kTileMin == 0 && d_model % kTileMin == 0, MLA_ERR_UNSUPPORTED,
               "mla_head_partition_merge: d_mid (%d) and d_model (%d) must be multiples of 128", d_mid, d_model);
   MLA_REQUIRE((HL * kDv) % BK == 0, MLA_ERR_UNSUPPORTED, "mla_head_partition_merge: HL*128 must be a multiple of 64");
   const void* ptrs[] = {art_out, rec_out, glob_out, wa_t, wb_t, z, y};
