@@ -449,11 +449,15 @@ def test_absorbed_path(n_rows, pieces):
 
 # ---------------------------------------------------------------- head partition merge
 
-def test_head_partition_merge():
+# (T, HL, HG, P, d_mid, d_model): the first gives few 128-wide tiles, so the
+# launcher takes 64-wide ones; the second gives 17 x 16 = 272 128-wide tiles,
+# at least one per compute unit, so it takes those (ragged last row tile)
+@pytest.mark.parametrize("shape", [(300, 7, 1, 13, 256, 384), (2100, 7, 1, 40, 2048, 2048)])
+def test_head_partition_merge(shape):
     require_gpu()
-    say("head partition merge")
+    say(f"head partition merge {shape}")
     rng = np.random.default_rng(62)
-    T, HL, HG, P, d_mid, d_model = 300, 7, 1, 13, 256, 384
+    T, HL, HG, P, d_mid, d_model = shape
     art = mi.f32_to_bf16_bits(rng.standard_normal((T, HL, 128)).astype(np.float32) * 0.05)
     rec = mi.f32_to_bf16_bits(rng.standard_normal((P, HL, 128)).astype(np.float32) * 0.05)
     glob = mi.f32_to_bf16_bits(rng.standard_normal((T, HG, 128)).astype(np.float32) * 0.05)
