@@ -130,18 +130,46 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFI
     print(json.dumps(d))
 
 
-def timed_steps(torch, run, steps):
-    """Run `steps` steps bracketed by synchronisation, with an event before
-    each step and after the last; returns (mean ms, [ms per step])."""
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+def timed_steps(torch, run, steps, flush=None):
+    """Run `steps` steps bracketed by synchronisation; returns (mean ms,
+    [ms per step]). Without `flush`, events sit before each step and after
+    the last. With it, `flush` runs before every step, outside that step's
+    pair of events (same stream, so the step starts after it)."""
     torch.cuda.synchronize()
-    ev[0].record()
+    if flush is None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return ev[0].elapsed_time(ev[steps]) / max(steps, 1), per
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
+        flush()
+        e0[i].record()
         run()
-        ev[i + 1].record()
+        e1[i].record()
     torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return ev[0].elapsed_time(ev[steps]) / max(steps, 1), per
+    per = [e0[i].elapsed_time(e1[i]) for i in range(steps)]
+    return sum(per) / max(steps, 1), per
+
+
+def cache_flusher(torch, mb):
+    """A callable that overwrites an `mb` MB device buffer (one fill kernel),
+    so that a step's inputs are not served from the 256 MB Infinity Cache
+    left warm by the previous step; None for mb = 0."""
+    if mb <= 0:
+        return None
+    buf = torch.empty(mb << 20, dtype=torch.uint8, device="cuda")
+    state = [0]
+
+    def flush():
+        state[0] ^= 1
+        buf.fill_(state[0])
+    return flush
 
 
 def step_stats(step_ms):
@@ -358,7 +386,7 @@ def bench_artifact(args, torch, mla, mla_inputs):
     assert int(b.dev_status.item()) == 0
     from mla_long_context_amd.prefill import GraphStep
     step = GraphStep(b).replay if args.graph else b.run
-    ms, step_ms = timed_steps(torch, step, args.steps)
+    ms, step_ms = timed_steps(torch, step, args.steps, cache_flusher(torch, args.flush_mb))
     timer = KernelTimer()
     for _ in range(args.steps):
         b.run(timer=timer)
@@ -395,6 +423,8 @@ def bench_artifact(args, torch, mla, mla_inputs):
                         "kernel": kname, "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)},
            "kernels": kernels,
            "step_launch": "replay of one step captured into a HIP graph" if args.graph else "eager launches",
+        "cache_flush_mb": args.flush_mb,
+           "cache_flush_mb": args.flush_mb,
            "kernel_timing": "a second pass of the same number of steps, launched eagerly with HIP events around every launch"}
     res.update(step_stats(step_ms))
     if not args.no_cpu_baseline:
@@ -423,6 +453,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="device buffer (MB) overwritten before every timed step, outside its events, "
+                         "so the Infinity Cache holds nothing of the previous step (0: off)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
@@ -491,7 +524,7 @@ def main():
     # Timed steps for the headline value: events only between steps (events
     # around every launch would add a fence between kernels); the value uses
     # the mean over the K steps, the median and min per step are reported too.
-    ms, step_ms = timed_steps(torch, step, args.steps)
+    ms, step_ms = timed_steps(torch, step, args.steps, cache_flusher(torch, args.flush_mb))
     # The same number of steps again with events around every launch, on the
     # stream the kernels run on: per-kernel durations for the breakdown and
     # the roofline of the dominant kernel.
@@ -568,6 +601,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "step_launch": "replay of one step captured into a HIP graph" if args.graph else "eager launches",
+        "cache_flush_mb": args.flush_mb,
         "kernel_timing": "a second pass of the same number of steps, launched eagerly with HIP events around every launch",
     }
     res.update(step_stats(step_ms))
