@@ -55,15 +55,21 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // positions inside a row instead. Measured on gfx950 with rocprofv3
 // (SQ_LDS_BANK_CONFLICT) both read patterns below are conflict-free, while the
 // unswizzled layouts cost 4 (K) and 6 (V) conflict cycles per read.
-//   K tile: 64 keys x 384 B (k_nope 16 chunks | k_rope 8 chunks); chunk c of
-//           key r sits at position c ^ ((r >> 1) & 7) (low three bits only).
+//   K tile: a k_nope region, 64 keys x 256 B (16 chunks), chunk c of key r
+//           at position c ^ (r & 15); then a k_rope region, 64 keys x 128 B
+//           (8 chunks), chunk c of key r at position c ^ ((r >> 1) & 7).
+//           Separate regions let every DMA instruction take one source (the
+//           head's k_nope rows or the latent's k_rope columns) as a
+//           wavefront-uniform base plus a fixed per-lane offset.
 //   V tile: 64 keys x 256 B (16 chunks), row-major; chunk c of key r sits at
 //           position c ^ ((r & 3) << 2). The PV operand (eight keys of one dv
 //           column per lane) is read with ds_read_b64_tr_b16, which hands
 //           each lane four consecutive keys of one column.
-constexpr int kKRow = 384;                 // bytes per K row in LDS
+constexpr int kKNRow = 256;                // bytes per key in the k_nope region
+constexpr int kKRRow = 128;                // bytes per key in the k_rope region
+constexpr int kKNope = 64 * kKNRow;        // k_nope region bytes (16384)
 constexpr int kVRow = 256;                 // bytes per V row in LDS
-constexpr int kKTile = kTileK * kKRow;     // 24576
+constexpr int kKTile = kKNope + 64 * kKRRow;   // 24576
 constexpr int kVTile = kTileK * kVRow;     // 16384
 
 constexpr int kStage = kKTile + kVTile;   // one LDS stage: K tile then V tile
@@ -72,10 +78,13 @@ template <int NW, bool kCausal, bool kRowIds, int kOutDt, bool kMerge>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
   constexpr int NB = (NW == 8) ? 3 : 2;   // LDS stages (tiles in flight)
-  constexpr int kKj = (kTileK * 24) / (64 * NW);   // K DMA instructions per wavefront per tile
+  constexpr int kKnj = (kTileK * 16) / (64 * NW);  // k_nope DMA instructions per wavefront per tile
+  constexpr int kKrj = (kTileK * 8) / (64 * NW);   // k_rope DMA instructions per wavefront per tile
+  constexpr int kKj = kKnj + kKrj;
   constexpr int kVj = (kTileK * 16) / (64 * NW);   // V DMA instructions per wavefront per tile
   constexpr int kDma = kKj + kVj;
-  static_assert(kKj * 64 * NW == kTileK * 24 && kVj * 64 * NW == kTileK * 16, "tile split");
+  static_assert(kKnj * 64 * NW == kTileK * 16 && kKrj * 64 * NW == kTileK * 8 && kVj * 64 * NW == kTileK * 16,
+                "tile split");
   // LDS fragment reads issued ahead of their products (K: of 24 per tile, V:
   // of 32)
   constexpr int kKAhead = 6;
@@ -137,78 +146,66 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint16_t* vbase = a.v + (int64_t)hs * a.vhs + (int64_t)k0 * kDv;
   const uint16_t* rbase = a.lat + (int64_t)k0 * a.ld_lat + kDc;
 
-  // DMA sources of this lane: chunk slot -> (key row r, global chunk). For a
-  // tile inside the keys, a K chunk is read from base + off, where base is
-  // the tile's k_nope or k_rope start (two wavefront-uniform addresses) and
-  // off a per-lane byte offset fixed for the whole kernel; a V chunk from the
-  // tile's v start plus its offset. K offsets carry the chunk's row in bits
-  // 25-30 and a k_rope flag in bit 31 (the host keeps ld_lat <= 2^17, so the
-  // offset fits 25 bits); a V offset is row * 256 + chunk bytes. In the last,
-  // partial tile keys at or past n_k are clamped to the last key (masked
-  // scores, p = 0 values), so no load needs a predicate.
+  // DMA sources of this lane. Instruction i of a region fills its 1 KB
+  // slice: k_nope rows 4i .. 4i+3 (16 chunks each), k_rope rows 8i .. 8i+7 (8
+  // chunks each), v rows 4i .. 4i+3; lane l writes LDS chunk l of the slice
+  // and reads the global chunk the swizzle puts there. A source is the tile's
+  // k_nope, k_rope or v start (wavefront-uniform) plus a per-lane byte
+  // offset fixed for the whole kernel. In the last, partial tile keys at or
+  // past n_k are clamped to the last key (masked scores, p = 0 values), so no
+  // load needs a predicate.
   const int klast = n_k - 1;
-  uint32_t koffd[kKj], voffd[kVj];
+  auto nrow = [&](int jj) { return (jj * NW + wave) * 4 + (lane >> 4); };
+  auto rrow = [&](int jj) { return (jj * NW + wave) * 8 + (lane >> 3); };
+  auto noff = [&](int r, int rsrc) { return (uint32_t)(rsrc * kKNRow + (((lane & 15) ^ (r & 15)) << 4)); };
+  auto roff = [&](int r, int rsrc) {
+    return (uint32_t)(rsrc * (int)a.ld_lat * 2 + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
+  };
+  auto vofs = [&](int r, int rsrc) { return (uint32_t)(rsrc * kVRow + (((lane & 15) ^ ((r & 3) << 2)) << 4)); };
+  uint32_t knoff[kKnj], kroff[kKrj], voffd[kVj];
 #pragma unroll
-  for (int jj = 0; jj < kKj; ++jj) {
-    const int slot = (jj * NW + wave) * 64 + lane;
-    const int r = slot / 24, c = slot % 24;
-    const int gc = (c & ~7) | ((c ^ (r >> 1)) & 7);
-    koffd[jj] = (gc < 16 ? (uint32_t)(r * kDnope + gc * 8) * 2u
-                         : ((uint32_t)(r * a.ld_lat + (gc - 16) * 8) * 2u) | 0x80000000u) |
-                ((uint32_t)r << 25);
-  }
+  for (int jj = 0; jj < kKnj; ++jj) knoff[jj] = noff(nrow(jj), nrow(jj));
 #pragma unroll
-  for (int jj = 0; jj < kVj; ++jj) {
-    const int slot = (jj * NW + wave) * 64 + lane;
-    const int r = slot >> 4, c = slot & 15;
-    voffd[jj] = (uint32_t)(r * kDv + (c ^ ((r & 3) << 2)) * 8) * 2u;
-  }
+  for (int jj = 0; jj < kKrj; ++jj) kroff[jj] = roff(rrow(jj), rrow(jj));
+#pragma unroll
+  for (int jj = 0; jj < kVj; ++jj) voffd[jj] = vofs(nrow(jj), nrow(jj));
   auto dma = [&](uint8_t* St, int kt0) {
     uint8_t* Kd = St;
     uint8_t* Vd = St + kKTile;
     const uint8_t* nb = reinterpret_cast<const uint8_t*>(kbase + (int64_t)kt0 * kDnope);
     const uint8_t* rb = reinterpret_cast<const uint8_t*>(rbase + (int64_t)kt0 * a.ld_lat);
-    const int64_t rd = rb - nb;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(vbase + (int64_t)kt0 * kDv);
-    // (the empty asm statements keep the compiler from hoisting per-lane
-    // values derived from the offsets out of the tile loop, which would hold
-    // extra registers for the whole kernel)
     if (kt0 + kTileK - 1 <= klast) {
 #pragma unroll
-      for (int jj = 0; jj < kKj; ++jj) {
-        uint32_t o = koffd[jj];
-        asm volatile("" : "+v"(o));
-        dma16(nb + (o & 0x1ffffffu) + ((o >> 31) ? rd : (int64_t)0), Kd + (jj * NW + wave) * 1024);
-      }
+      for (int jj = 0; jj < kKnj; ++jj) dma16s(nb, knoff[jj], Kd + (jj * NW + wave) * 1024);
+#pragma unroll
+      for (int jj = 0; jj < kKrj; ++jj) dma16s(rb, kroff[jj], Kd + kKNope + (jj * NW + wave) * 1024);
 #pragma unroll
       for (int jj = 0; jj < kVj; ++jj) dma16s(vb, voffd[jj], Vd + (jj * NW + wave) * 1024);
     } else {
-      // last tile: rows past the last key move back to it
+      // last tile: rows past the last key read the last key
+      const int rl = klast - kt0;
 #pragma unroll
-      for (int jj = 0; jj < kKj; ++jj) {
-        uint32_t o = koffd[jj];
-        asm volatile("" : "+v"(o));
-        const int over = max(kt0 + (int)((o >> 25) & 63u) - klast, 0);
-        const int64_t back = (int64_t)over * ((o >> 31) ? a.ld_lat * 2 : (int64_t)kDnope * 2);
-        dma16(nb + (o & 0x1ffffffu) + ((o >> 31) ? rd : (int64_t)0) - back, Kd + (jj * NW + wave) * 1024);
-      }
+      for (int jj = 0; jj < kKnj; ++jj)
+        dma16s(nb, noff(nrow(jj), min(nrow(jj), rl)), Kd + (jj * NW + wave) * 1024);
 #pragma unroll
-      for (int jj = 0; jj < kVj; ++jj) {
-        uint32_t o = voffd[jj];
-        asm volatile("" : "+v"(o));
-        const int over = max(kt0 + (int)(o >> 8) - klast, 0);
-        dma16(vb + o - (int64_t)over * kDv * 2, Vd + (jj * NW + wave) * 1024);
-      }
+      for (int jj = 0; jj < kKrj; ++jj)
+        dma16s(rb, roff(rrow(jj), min(rrow(jj), rl)), Kd + kKNope + (jj * NW + wave) * 1024);
+#pragma unroll
+      for (int jj = 0; jj < kVj; ++jj)
+        dma16s(vb, vofs(nrow(jj), min(nrow(jj), rl)), Vd + (jj * NW + wave) * 1024);
     }
   };
 
   // per-lane fragment read offsets (bytes)
-  int koff[4];                               // K: row l32, chunk 2s+g -> + (s>>2)*128 + kb*32 rows
-  {
-    const int m = (l32 >> 1) & 7;
+  // K: key l32 (+ 32 for the second block, a constant offset), dims
+  // 16 s + 8 g .. +8: chunk 2 s + g of the k_nope region for s < 8, chunk
+  // 2 (s - 8) + g of the k_rope region for s >= 8
+  int koff[kDqk / 16];
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) koff[qd] = l32 * kKRow + (((2 * qd + g) ^ m) * 16);
-  }
+  for (int s2 = 0; s2 < kDqk / 16; ++s2)
+    koff[s2] = s2 < 8 ? l32 * kKNRow + (((2 * s2 + g) ^ (l32 & 15)) << 4)
+                      : kKNope + l32 * kKRRow + (((2 * (s2 - 8) + g) ^ ((l32 >> 1) & 7)) << 4);
   int voff[4];                               // V^T: dv block d; + (16 mm + 8 half) rows
   {
     const int a4 = (lane & 15) >> 2, b4 = lane & 3, g16 = (lane >> 4) & 1;
@@ -246,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int s = 0; s < kDqk / 16; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + koff[s & 3] + (s >> 2) * 128 + kb * 32 * kKRow);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + koff[s] + kb * 32 * (s < 8 ? kKNRow : kKRRow));
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
       }
     }
