@@ -4,8 +4,9 @@
 Workload (default): DeepSeek-V3 geometry, one layer, 128 heads, 4 requests x
 (8192 cached context tokens + 1024 new tokens), 64-token blocks in a shuffled
 pool, context chunk 4096, bf16 cache. A step is one pass of the whole path:
-per context chunk gather -> kv_b_proj decompression -> attention -> LSE merge,
-then decompression of the new tokens -> causal attention -> final merge.
+per context chunk gather -> kv_b_proj decompression -> attention -> LSE merge
+into the running state; the last chunk's attention also covers the new
+tokens' keys (decompressed beside the chunk's, causal) and writes the result.
 Inputs are seeded synthetic data resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
@@ -97,7 +98,8 @@ def _counter_rows(csv_path, counter):
 
 def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFIC_FILE):
     """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE per-dispatch counters (KiB) of the
-    context-attention launches into HBM bytes per launch, each scaled by what
+    two-segment attention launches (the dominant kernel of the dsv3 workload)
+    into HBM bytes per launch, each scaled by what
     the same counter reads for the 1 GiB copy of --calibrate-copy."""
     gib_kib = float(1 << 20)
     # the copy dispatches (the fill before them reads almost nothing)
@@ -105,12 +107,14 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFI
     cal_w = [v for n, v in _counter_rows(cal_write_csv, "WRITE_SIZE") if v > gib_kib / 8]
     kf = gib_kib / (sum(cal_f) / len(cal_f))
     kw = gib_kib / (sum(cal_w) / len(cal_w))
-    ctx = lambda n: "attn_kernel<8, false, false" in n
+    # the two-segment pass (last chunk + new tokens; bf16 out, merged)
+    ctx = lambda n: "attn_kernel<8, false, false, 0, true, true>" in n
     f = [v for n, v in _counter_rows(fetch_csv, "FETCH_SIZE") if ctx(n)]
     w = [v for n, v in _counter_rows(write_csv, "WRITE_SIZE") if ctx(n)]
     fetch_b = sum(f) / len(f) * 1024 * kf
     write_b = sum(w) / len(w) * 1024 * kw
-    d = {"kernel": "mla_prefill_attn (context pass), 4 x (8192 ctx + 1024 new), H=128, chunk 4096",
+    d = {"kernel": "mla_prefill_attn_2seg (second context chunk + causal pass), 4 x (8192 ctx + 1024 new), "
+                   "H=128, chunk 4096",
          "source_sha256_16": source_hash(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip")),
          "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
          "bytes_per_launch": round(fetch_b + write_b),
@@ -123,7 +127,7 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFI
              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/cw -o cw -- python3 bench.py --calibrate-copy",
              "python3 bench.py --write-traffic <out>/f/f_counter_collection.csv <out>/w/w_counter_collection.csv "
              "<out>/cf/cf_counter_collection.csv <out>/cw/cw_counter_collection.csv"],
-         "note": "per-dispatch counters in KiB, averaged over the context-attention launches; the 1 GiB "
+         "note": "per-dispatch counters in KiB, averaged over the two-segment attention launches; the 1 GiB "
                  "copy reads FETCH_SIZE x 1/2 and WRITE_SIZE x 1, hence the scales"}
     with open(out, "w") as fh:
         json.dump(d, fh, indent=1)
@@ -540,6 +544,7 @@ def main():
     # algorithmic work per step of each timed kernel: flops for the MFMA
     # kernels, bytes for the HBM-bound ones
     mfma_work = {"attn_ctx": work.get("ctx_attn_flops"), "attn_ext": work.get("ext_attn_flops"),
+                 "attn_last": work.get("last_attn_flops"),
                  "decompress": work["dec_flops"], "attn_global": work.get("global_attn_flops"),
                  "attn_local": work.get("local_attn_flops"), "projection": work.get("proj_flops"),
                  "absorb": work.get("absorb_flops")}
@@ -564,9 +569,10 @@ def main():
     c_unit = mfma_work[dom] / per_step_launch[dom]
     achieved = c_unit / (c_ms * 1e-3) / 1e12
     traffic = None
-    if dom == "attn_ctx" and args.workload == 2:   # the workload the counter record was taken on
+    if dom == "attn_last" and args.workload == 2:   # the workload the counter record was taken on
         traffic = traffic_for(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip"))
     kname = {"attn_ctx": "mla_prefill_attn (context pass)", "attn_ext": "mla_prefill_attn (causal pass)",
+             "attn_last": "mla_prefill_attn_2seg (last context chunk + causal pass)",
              "decompress": "mla_decompress", "attn_global": "mla_prefill_attn (Global heads)",
              "attn_local": ("mla_absorbed_attn (protected Local rows)" if getattr(pre, "absorbed", False)
                             else "mla_prefill_attn (protected Local rows)"),

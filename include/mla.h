@@ -226,6 +226,40 @@ int mla_prefill_attn_merge(const void* q, int64_t q_row_stride, int H_q, int h_b
                            float* lse, int64_t lse_row_stride, void* stream);
 
 /*
+ * mla_prefill_attn_2seg -- the last pass of the [DSMLA] 4.4 chunk loop and
+ * the causal pass over the new tokens ([DSMLA] 4.2) in one launch: each row
+ * attends to the keys of two segments with one online softmax, then (when a
+ * previous state is given) is merged into it as in mla_prefill_attn_merge.
+ * The result is the plain softmax over the union of both key sets, the
+ * same value the two passes and their merge compute, up to rounding order.
+ *
+ *   segment 1: keys t in [cu_k[b], cu_k[b+1]) of (k_nope, v, latent), all
+ *              visible (the chunk's context tokens);
+ *   segment 2: keys t in [cu_k2[b], cu_k2[b+1]) of (k_nope2, v2, latent2),
+ *              causal: row i sees key t iff (t - cu_k2[b]) <= i + n_k2 - n_q
+ *              (the request's own new tokens).
+ * Scores, k_rope (columns 512..575 of each segment's latent rows), out and
+ * lse as mla_prefill_attn. Either segment may be empty for a request; with
+ * prev_out = prev_lse = NULL no merge happens, otherwise both must be given
+ * (fp32, as in mla_prefill_attn_merge, with the same aliasing rule).
+ * Constraints: ld_latent2 == ld_latent (MLA_ERR_UNSUPPORTED otherwise); no
+ * row ids; pointers 16-byte aligned and head strides multiples of 8 as in
+ * mla_prefill_attn.
+ */
+int mla_prefill_attn_2seg(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                          const void* k_nope, int64_t k_head_stride,
+                          const void* v, int64_t v_head_stride,
+                          const void* latent, int64_t ld_latent, const int32_t* cu_k,
+                          const void* k_nope2, int64_t k_head_stride2,
+                          const void* v2, int64_t v_head_stride2,
+                          const void* latent2, int64_t ld_latent2, const int32_t* cu_k2,
+                          const int32_t* cu_q, int batch, int max_q, float scale,
+                          const float* prev_out, int64_t prev_row_stride,
+                          const float* prev_lse, int64_t prev_lse_row_stride,
+                          void* out, int out_dtype, int64_t out_row_stride,
+                          float* lse, int64_t lse_row_stride, void* stream);
+
+/*
  * Absorbed-form attention ([DSMLA] section 3: W_UK folded into the query,
  * W_UV applied after the attention, every head attends to the shared
  * 576-wide latent), for query sets small next to the key count: the

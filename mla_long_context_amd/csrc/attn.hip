@@ -44,6 +44,10 @@ struct AttnArgs {
   int batch; int n_qt; float scale_log2;
   void* out; int64_t out_rs; float* lse; int64_t lse_rs;
   const float* prev; int64_t prev_rs; const float* prev_lse; int64_t prev_lse_rs;   // merge mode only
+  // second key segment (two-segment kernel only): the request's new tokens,
+  // causal, with the same latent row stride
+  const uint16_t* k2; int64_t khs2; const uint16_t* v2; int64_t vhs2; const uint16_t* lat2;
+  const int32_t* cu_k2;
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -74,8 +78,12 @@ constexpr int kVTile = kTileK * kVRow;     // 16384
 
 constexpr int kStage = kKTile + kVTile;   // one LDS stage: K tile then V tile
 
-template <int NW, bool kCausal, bool kRowIds, int kOutDt, bool kMerge>
+// kSeg2: after the keys of cu_k (all visible), the keys of cu_k2 from the
+// second segment, causal (row i sees key j iff j <= i + n_k2 - n_q), in the
+// same online softmax: the last context chunk and the new tokens in one pass.
+template <int NW, bool kCausal, bool kRowIds, int kOutDt, bool kMerge, bool kSeg2 = false>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
+  static_assert(!(kSeg2 && (kCausal || kRowIds)), "two segments: plain first segment, no row ids");
   constexpr int ROWS = 32 * NW;
   constexpr int NB = (NW == 8) ? 3 : 2;   // LDS stages (tiles in flight)
   constexpr int kKnj = (kTileK * 16) / (64 * NW);  // k_nope DMA instructions per wavefront per tile
@@ -121,7 +129,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int shift = n_k - n_q;               // causal: row i sees key j iff j <= i + shift
   int kend = n_k;
   if (kCausal) kend = min(n_k, r0 + ROWS + shift);
-  const int ntiles = kend > 0 ? (kend + kTileK - 1) / kTileK : 0;
+  const int ntiles1 = kend > 0 ? (kend + kTileK - 1) / kTileK : 0;   // tiles of the first segment
+  int ntiles = ntiles1;
+  int k02 = 0, n_k2 = 0, shift2 = 0;
+  if constexpr (kSeg2) {
+    k02 = a.cu_k2[b];
+    n_k2 = a.cu_k2[b + 1] - k02;
+    shift2 = n_k2 - n_q;
+    const int kend2 = min(n_k2, r0 + ROWS + shift2);
+    ntiles += kend2 > 0 ? (kend2 + kTileK - 1) / kTileK : 0;
+  }
 
   const int row = r0 + wave * 32 + l32;      // this lane's query row (request-local)
   const bool row_ok = row < n_q;
@@ -145,6 +162,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const uint16_t* kbase = a.k + (int64_t)hs * a.khs + (int64_t)k0 * kDnope;
   const uint16_t* vbase = a.v + (int64_t)hs * a.vhs + (int64_t)k0 * kDv;
   const uint16_t* rbase = a.lat + (int64_t)k0 * a.ld_lat + kDc;
+  const uint16_t* kbase2 = nullptr;
+  const uint16_t* vbase2 = nullptr;
+  const uint16_t* rbase2 = nullptr;
+  if constexpr (kSeg2) {
+    kbase2 = a.k2 + (int64_t)hs * a.khs2 + (int64_t)k02 * kDnope;
+    vbase2 = a.v2 + (int64_t)hs * a.vhs2 + (int64_t)k02 * kDv;
+    rbase2 = a.lat2 + (int64_t)k02 * a.ld_lat + kDc;
+  }
 
   // DMA sources of this lane. Instruction i of a region fills its 1 KB
   // slice: k_nope rows 4i .. 4i+3 (16 chunks each), k_rope rows 8i .. 8i+7 (8
@@ -154,7 +179,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // offset fixed for the whole kernel. In the last, partial tile keys at or
   // past n_k are clamped to the last key (masked scores, p = 0 values), so no
   // load needs a predicate.
-  const int klast = n_k - 1;
   auto nrow = [&](int jj) { return (jj * NW + wave) * 4 + (lane >> 4); };
   auto rrow = [&](int jj) { return (jj * NW + wave) * 8 + (lane >> 3); };
   auto noff = [&](int r, int rsrc) { return (uint32_t)(rsrc * kKNRow + (((lane & 15) ^ (r & 15)) << 4)); };
@@ -169,12 +193,17 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int jj = 0; jj < kKrj; ++jj) kroff[jj] = roff(rrow(jj), rrow(jj));
 #pragma unroll
   for (int jj = 0; jj < kVj; ++jj) voffd[jj] = vofs(nrow(jj), nrow(jj));
-  auto dma = [&](uint8_t* St, int kt0) {
+  // DMA of tile t of the key sequence (the first segment's tiles, then the
+  // second's)
+  auto dma = [&](uint8_t* St, int t) {
+    const bool s2 = kSeg2 && t >= ntiles1;
+    const int kt0 = (s2 ? t - ntiles1 : t) * kTileK;
+    const int klast = (s2 ? n_k2 : n_k) - 1;
     uint8_t* Kd = St;
     uint8_t* Vd = St + kKTile;
-    const uint8_t* nb = reinterpret_cast<const uint8_t*>(kbase + (int64_t)kt0 * kDnope);
-    const uint8_t* rb = reinterpret_cast<const uint8_t*>(rbase + (int64_t)kt0 * a.ld_lat);
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vbase + (int64_t)kt0 * kDv);
+    const uint8_t* nb = reinterpret_cast<const uint8_t*>((s2 ? kbase2 : kbase) + (int64_t)kt0 * kDnope);
+    const uint8_t* rb = reinterpret_cast<const uint8_t*>((s2 ? rbase2 : rbase) + (int64_t)kt0 * a.ld_lat);
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>((s2 ? vbase2 : vbase) + (int64_t)kt0 * kDv);
     if (kt0 + kTileK - 1 <= klast) {
 #pragma unroll
       for (int jj = 0; jj < kKnj; ++jj) dma16s(nb, knoff[jj], Kd + (jj * NW + wave) * 1024);
@@ -231,6 +260,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
                         : kCausal ? min(n_k, r0 + wave * 32 + 32 + shift) : n_k;
   const int wave_first_lim = r0 + wave * 32 + shift;   // causal: smallest row limit in the wave
   const int row_lim = row + shift;           // causal: keys <= row_lim are visible
+  // the same for the second segment
+  const int wave_kend2 = (r0 + wave * 32 >= n_q) ? 0 : min(n_k2, r0 + wave * 32 + 32 + shift2);
+  const int wave_first_lim2 = r0 + wave * 32 + shift2;
+  const int row_lim2 = row + shift2;
   const float c = a.scale_log2;              // scale * log2(e); scores stay raw until exp2
 
   // S^T = K . Q^T for one tile
@@ -257,17 +290,22 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
   };
 
-  // online softmax of the tile in S (keys kt0..kt0+63) -> P, rescaling O
-  auto softmax = [&](int kt0) {
+  // online softmax of the tile in S (keys kt0..kt0+63 of the first
+  // segment, or of the second when s2) -> P, rescaling O
+  auto softmax = [&](int kt0, bool s2) {
     // masking only on tiles that cross the key end or the causal diagonal
-    const bool edge = (kt0 + kTileK > n_k) || (kCausal && kt0 + kTileK - 1 > wave_first_lim);
+    const bool causal = kCausal || s2;
+    const int nk = s2 ? n_k2 : n_k;
+    const int first_lim = s2 ? wave_first_lim2 : wave_first_lim;
+    const int rlim = s2 ? row_lim2 : row_lim;
+    const bool edge = (kt0 + kTileK > nk) || (causal && kt0 + kTileK - 1 > first_lim);
     if (edge) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool vis = key < n_k && (!kCausal || key <= row_lim);
+          const bool vis = key < nk && (!causal || key <= rlim);
           S[kb][i] = vis ? S[kb][i] : -INFINITY;
         }
     }
@@ -354,23 +392,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // into that stage and computes tile t. Tile indices past the end are
   // clamped to the last tile, so every step issues the same number of DMA
   // instructions and the vector-memory counter stays exact.
-  const int last_kt0 = (ntiles - 1) * kTileK;
   if (ntiles > 0) {
     dma(stage(0), 0);
-    if (NB == 3) dma(stage(1), min(kTileK, last_kt0));
+    if (NB == 3) dma(stage(1), min(1, ntiles - 1));
   }
   // the Q fragments (and the first tiles) have landed: without this wait
   // the compiler, which does not see the DMA, would wait for every
   // outstanding load before the first product of each tile
   wait_vmcnt<0>();
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int kt0 = kt * kTileK;
+    const bool s2 = kSeg2 && kt >= ntiles1;
+    const int kt0 = (s2 ? kt - ntiles1 : kt) * kTileK;
     wait_vmcnt<kDma * (NB - 2)>();
     __syncthreads();
-    dma(stage(kt + NB - 1), min(kt0 + (NB - 1) * kTileK, last_kt0));
-    if (kt0 < wave_kend) {
+    dma(stage(kt + NB - 1), min(kt + NB - 1, ntiles - 1));
+    if (kt0 < (s2 ? wave_kend2 : wave_kend)) {
       qk(stage(kt));
-      softmax(kt0);
+      softmax(kt0, s2);
       pv(stage(kt) + kKTile);
     }
   }
@@ -428,6 +466,25 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if (g == 0) a.lse[orow * a.lse_rs + hs] = lse2 * kLn2;
 }
 
+template <int NW, bool kMerge>
+void launch_seg2(int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
+  if (out_dt == MLA_DTYPE_FP32)
+    hipLaunchKernelGGL((attn_kernel<NW, false, false, MLA_DTYPE_FP32, kMerge, true>), g, dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<NW, false, false, MLA_DTYPE_BF16, kMerge, true>), g, dim3(NW * 64), 0, s, a);
+}
+template <int NW>
+void launch_seg2m(bool merge, int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
+  if (merge) launch_seg2<NW, true>(out_dt, g, s, a);
+  else launch_seg2<NW, false>(out_dt, g, s, a);
+}
+
+// second key segment of mla_prefill_attn_2seg
+struct Seg2 {
+  const void* k_nope; int64_t k_head_stride; const void* v; int64_t v_head_stride;
+  const void* latent; int64_t ld_latent; const int32_t* cu_k;
+};
+
 template <int NW, bool kCausal, bool kRowIds, bool kMerge>
 void launch4(int out_dt, dim3 g, hipStream_t s, const AttnArgs& a) {
   if (out_dt == MLA_DTYPE_FP32)
@@ -458,7 +515,7 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
                  const int32_t* q_row_ids, int batch, int max_q, float scale, int causal, void* out,
                  int out_dtype, int64_t out_row_stride, float* lse, int64_t lse_row_stride,
                  const float* prev, int64_t prev_row_stride, const float* prev_lse, int64_t prev_lse_row_stride,
-                 bool merge, void* stream) {
+                 bool merge, void* stream, const Seg2* seg2 = nullptr) {
   mla_clear_error();
   MLA_REQUIRE(batch >= 0 && max_q >= 0, MLA_ERR_INVALID_ARG, "%s: batch and max_q must be >= 0", fn);
   MLA_REQUIRE(H_q > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_q, MLA_ERR_INVALID_ARG,
@@ -481,6 +538,18 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
   MLA_REQUIRE(out_row_stride % 4 == 0 && out_row_stride >= (int64_t)Hsel * kDv && lse_row_stride >= Hsel,
               MLA_ERR_INVALID_ARG, "%s: out_row_stride must be >= Hsel*128 (multiple of 4), lse_row_stride >= Hsel", fn);
   MLA_REQUIRE(scale > 0.f && scale < 1e30f, MLA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  if (seg2) {
+    MLA_REQUIRE(!causal && !q_row_ids, MLA_ERR_UNSUPPORTED, "%s: the first segment is plain (no causal, no row ids)", fn);
+    MLA_REQUIRE(seg2->k_nope && seg2->v && seg2->latent && seg2->cu_k, MLA_ERR_INVALID_ARG,
+                "%s: null second-segment argument", fn);
+    MLA_REQUIRE(mla_aligned16(seg2->k_nope) && mla_aligned16(seg2->v) && mla_aligned16(seg2->latent),
+                MLA_ERR_INVALID_ARG, "%s: second-segment pointers must be 16-byte aligned", fn);
+    MLA_REQUIRE(seg2->k_head_stride % 8 == 0 && seg2->v_head_stride % 8 == 0, MLA_ERR_INVALID_ARG,
+                "%s: second-segment head strides must be multiples of 8", fn);
+    MLA_REQUIRE(seg2->ld_latent == ld_latent, MLA_ERR_UNSUPPORTED,
+                "%s: both segments' latents need the same row stride (%lld != %lld)", fn,
+                (long long)seg2->ld_latent, (long long)ld_latent);
+  }
   if (merge) {
     MLA_REQUIRE(prev && prev_lse, MLA_ERR_INVALID_ARG, "%s: null previous state", fn);
     MLA_REQUIRE(mla_aligned16(prev) && prev_row_stride % 4 == 0 && prev_row_stride >= (int64_t)Hsel * kDv &&
@@ -509,10 +578,25 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
              static_cast<const uint16_t*>(latent), ld_latent,
              cu_q, cu_k, q_row_ids, batch, n_qt, scale * kLog2e,
              out, out_row_stride, lse, lse_row_stride,
-             prev, prev_row_stride, prev_lse, prev_lse_row_stride};
+             prev, prev_row_stride, prev_lse, prev_lse_row_stride,
+             nullptr, 0, nullptr, 0, nullptr, nullptr};
+  if (seg2) {
+    a.k2 = static_cast<const uint16_t*>(seg2->k_nope);
+    a.khs2 = seg2->k_head_stride;
+    a.v2 = static_cast<const uint16_t*>(seg2->v);
+    a.vhs2 = seg2->v_head_stride;
+    a.lat2 = static_cast<const uint16_t*>(seg2->latent);
+    a.cu_k2 = seg2->cu_k;
+  }
   dim3 g((unsigned)total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool rid = q_row_ids != nullptr, c = causal != 0;
+  if (seg2) {
+    if (NW == 8) launch_seg2m<8>(merge, out_dtype, g, s, a);
+    else if (NW == 4) launch_seg2m<4>(merge, out_dtype, g, s, a);
+    else launch_seg2m<2>(merge, out_dtype, g, s, a);
+    return mla_check_launch(fn);
+  }
   if (NW == 8) launch1<8>(c, rid, merge, out_dtype, g, s, a);
   else if (NW == 4) launch1<4>(c, rid, merge, out_dtype, g, s, a);
   else launch1<2>(c, rid, merge, out_dtype, g, s, a);
@@ -548,4 +632,22 @@ extern "C" int mla_prefill_attn_merge(const void* q, int64_t q_row_stride, int H
                       v, v_head_stride, latent, ld_latent, cu_q, cu_k, q_row_ids, batch, max_q, scale, causal,
                       out, out_dtype, out_row_stride, lse, lse_row_stride, prev_out, prev_row_stride, prev_lse,
                       prev_lse_row_stride, true, stream);
+}
+
+extern "C" int mla_prefill_attn_2seg(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                                     const void* k_nope, int64_t k_head_stride, const void* v,
+                                     int64_t v_head_stride, const void* latent, int64_t ld_latent,
+                                     const int32_t* cu_k, const void* k_nope2, int64_t k_head_stride2,
+                                     const void* v2, int64_t v_head_stride2, const void* latent2,
+                                     int64_t ld_latent2, const int32_t* cu_k2, const int32_t* cu_q, int batch,
+                                     int max_q, float scale, const float* prev_out, int64_t prev_row_stride,
+                                     const float* prev_lse, int64_t prev_lse_row_stride, void* out,
+                                     int out_dtype, int64_t out_row_stride, float* lse, int64_t lse_row_stride,
+                                     void* stream) {
+  const Seg2 seg2{k_nope2, k_head_stride2, v2, v_head_stride2, latent2, ld_latent2, cu_k2};
+  const bool merge = prev_out != nullptr || prev_lse != nullptr;
+  return prefill_attn("mla_prefill_attn_2seg", q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,
+                      v_head_stride, latent, ld_latent, cu_q, cu_k, nullptr, batch, max_q, scale, 0, out,
+                      out_dtype, out_row_stride, lse, lse_row_stride, prev_out, prev_row_stride, prev_lse,
+                      prev_lse_row_stride, merge, stream, &seg2);
 }

@@ -76,7 +76,7 @@ def upload_pool(prob, device) -> torch.Tensor:
 class ChunkedPrefill:
     """Configs with a paged context and new (extend) tokens per request."""
 
-    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all"):
+    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True):
         self.prob = prob
         self.device = device
         assert fuse_merge in ("none", "final", "all")
@@ -102,8 +102,13 @@ class ChunkedPrefill:
             ln = np.clip(C - c * self.S, 0, self.S)
             self.chunks.append(dict(start=_i32(start, device), len=_i32(ln, device),
                                     cu=_i32(_cu(ln), device), n=int(ln.sum()), max_len=int(ln.max())))
-        self.max_tok = max([ch["n"] for ch in self.chunks] + [self.T, 1])
         max_ctx_tok = max([ch["n"] for ch in self.chunks] + [1])
+        # With every merge fused, the last chunk's pass also covers the new
+        # tokens (mla_prefill_attn_2seg): their keys are decompressed behind
+        # the chunk's, at token offset ext_off of the same workspaces.
+        self.two_seg = two_segment and fuse_merge == "all" and bool(self.chunks)
+        self.ext_off = max_ctx_tok if self.two_seg else 0
+        self.max_tok = max([ch["n"] for ch in self.chunks] + [self.ext_off + self.T, 1])
         self.lat_ws = torch.empty((max_ctx_tok, D_LAT), dtype=torch.bfloat16, device=device)
         self.k_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
         self.v_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
@@ -124,9 +129,28 @@ class ChunkedPrefill:
                              self.bt.shape[1], ch["start"], ch["len"], ch["cu"], self.B,
                              ch["max_len"], self.lat_ws, self.dev_status, stream)
 
-    def decompress(self, latent, n, stream=None):
-        L.mla_decompress(latent, D_LAT, n, self.w_t, self.H, 0, self.H, self.k_ws, self.hstride,
-                         self.v_ws, self.hstride, stream)
+    def decompress(self, latent, n, stream=None, off=0):
+        """k_nope / v of n tokens into the workspaces from token `off` on."""
+        L.mla_decompress(latent, D_LAT, n, self.w_t, self.H, 0, self.H, self._at(self.k_ws, off),
+                         self.hstride, self._at(self.v_ws, off), self.hstride, stream)
+
+    @staticmethod
+    def _at(ws, off):
+        # device address of token `off` of head 0 in a [H, tokens, 128] bf16 workspace
+        return ws.data_ptr() + off * D_V * 2
+
+    def attend_2seg(self, ch, merge, stream=None):
+        """The last chunk's keys (all visible) and the new tokens' keys
+        (causal) in one pass, merged into the running state when `merge`;
+        writes the bf16 result."""
+        L.mla_prefill_attn_2seg(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
+                                self.v_ws, self.hstride, self.lat_ws, D_LAT, ch["cu"],
+                                self._at(self.k_ws, self.ext_off), self.hstride,
+                                self._at(self.v_ws, self.ext_off), self.hstride, self.ext, D_LAT,
+                                self.cu_ext, self.cu_ext, self.B, self.maxE, self.prob.scale,
+                                self.acc_o if merge else None, self.H * D_V,
+                                self.acc_l if merge else None, self.H, self.out, L.DTYPE_BF16,
+                                self.H * D_V, self.lse, self.H, stream)
 
     def attend(self, latent, cu_k, causal, out, out_dtype, lse, stream=None):
         L.mla_prefill_attn(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
@@ -151,7 +175,8 @@ class ChunkedPrefill:
         attention wrote a bf16 chunk state, or inside the attention kernel
         (mla_prefill_attn_merge): fuse_merge selects which merges are fused
         ("none", "final" = only the last, "all"). The last merge writes the
-        bf16 result."""
+        bf16 result. With "all", the last chunk and the causal pass share
+        one launch (mla_prefill_attn_2seg)."""
         if self.T == 0:
             return self.out, self.lse
         fuse_mid = self.fuse_merge == "all"
@@ -161,6 +186,12 @@ class ChunkedPrefill:
                 self.gather(ch, stream)
             with _span(timer, "decompress"):
                 self.decompress(self.lat_ws, ch["n"], stream)
+            if self.two_seg and ci == len(self.chunks) - 1:
+                with _span(timer, "decompress"):
+                    self.decompress(self.ext, self.T, stream, off=self.ext_off)
+                with _span(timer, "attn_last"):
+                    self.attend_2seg(ch, ci > 0, stream)
+                return self.out, self.lse
             if ci == 0:
                 with _span(timer, "attn_ctx"):
                     self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
@@ -202,12 +233,19 @@ class ChunkedPrefill:
         dec_tok = int(C.sum() + E.sum())
         ctx_pairs = int((C * E).sum())
         ext_pairs = int((E * (E + 1) // 2).sum())
+        # context pairs of the last chunk (its pass also takes the new
+        # tokens when the chunk loop ends in one two-segment launch)
+        last_pairs = 0
+        if self.chunks:
+            c = len(self.chunks) - 1
+            last_pairs = int((np.clip(C - c * self.S, 0, self.S) * E).sum())
         n_merge = max(len(self.chunks) - 1, 0) + (1 if self.chunks else 0)
         return dict(
             dec_flops=2 * 512 * 256 * H * dec_tok,
             attn_flops=640 * H * (ctx_pairs + ext_pairs),
-            ctx_attn_flops=640 * H * ctx_pairs,
-            ext_attn_flops=640 * H * ext_pairs,
+            ctx_attn_flops=640 * H * (ctx_pairs - last_pairs if self.two_seg else ctx_pairs),
+            ext_attn_flops=0 if self.two_seg else 640 * H * ext_pairs,
+            last_attn_flops=640 * H * (last_pairs + ext_pairs) if self.two_seg else 0,
             gather_tokens=int(C.sum()),
             gather_bytes=int(C.sum()) * (2304 if p.cache_dtype == "bf16" else 644 + 1152),
             new_tokens=int(E.sum()), ctx_tokens=int(C.sum()), merges=n_merge,

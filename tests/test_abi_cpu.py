@@ -86,6 +86,28 @@ def test_attn_validation(lib):
     assert _err(mla.mla_prefill_attn, *args)[0] == _lib.MLA_ERR_INVALID_ARG
 
 
+def test_two_segment_attn_validation(lib):
+    # q, q_rs, H_q, h0, h1, k, khs, v, vhs, lat, ld, cu_k, k2, khs2, v2, vhs2, lat2, ld2, cu_k2, cu_q,
+    # batch, max_q, scale, prev_out, prev_rs, prev_lse, prev_lse_rs, out, out_dt, out_rs, lse, lse_rs
+    base = [FAKE, 8 * 192, 8, 0, 8, FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE,
+            FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE, FAKE, 1, 10, 0.07,
+            None, 0, None, 0, FAKE, 0, 8 * 128, FAKE, 8]
+    args = list(base); args[17] = 584                     # latents with different row strides
+    assert _err(mla.mla_prefill_attn_2seg, *args)[0] == _lib.MLA_ERR_UNSUPPORTED
+    args = list(base); args[12] = None                    # no second-segment keys
+    code, msg = _err(mla.mla_prefill_attn_2seg, *args)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "second-segment" in msg
+    args = list(base); args[16] = FAKE + 4                # misaligned second latent
+    assert _err(mla.mla_prefill_attn_2seg, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[13] = 1284                    # head stride not a multiple of 8
+    assert _err(mla.mla_prefill_attn_2seg, *args)[0] == _lib.MLA_ERR_INVALID_ARG
+    args = list(base); args[23] = FAKE                    # previous out without its lse
+    code, msg = _err(mla.mla_prefill_attn_2seg, *args)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "previous state" in msg
+    args = list(base); args[20] = 0                       # nothing to do
+    assert mla.mla_prefill_attn_2seg(*args, stream=0) == 0
+
+
 def test_merge_rope_partition_pack_validation(lib):
     assert _err(mla.mla_merge_states, FAKE, 9, FAKE, FAKE, 0, FAKE, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_UNSUPPORTED
     assert _err(mla.mla_merge_states, FAKE, 0, FAKE, FAKE + 4, 0, FAKE, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG

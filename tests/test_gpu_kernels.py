@@ -367,6 +367,83 @@ def test_attention_merge_into_previous_state(causal, in_place):
             check_lse(gl[rows, hs], rl, tol=tol, what=f"b{b} h{hs} lse")
 
 
+# ---------------------------------------------------------------- two key segments in one pass
+
+# (seed, nq, nA, nB, merge): nA plain keys (the last context chunk), nB causal
+# keys (the request's new tokens: row i sees key j <= i + nB - nq), merged
+# into a previous state from nC further plain keys when `merge`. max_q picks
+# 256-, 128- and 64-row tiles; empty segments on either side; one request
+# with nB != nq.
+TWO_SEG_CASES = [
+    (80, [300, 5, 0, 77, 40, 260], [700, 0, 5, 130, 0, 64], [300, 5, 0, 77, 43, 260], True),
+    (81, [300, 5, 0, 77, 40, 260], [700, 0, 5, 130, 0, 64], [300, 5, 0, 77, 43, 260], False),
+    (82, [100, 64, 7], [256, 0, 65], [100, 64, 7], True),
+    (83, [33, 64, 1], [0, 129, 3], [33, 64, 1], True),
+]
+
+
+@pytest.mark.parametrize("case", TWO_SEG_CASES, ids=[f"seed{c[0]}" for c in TWO_SEG_CASES])
+def test_attention_two_segments(case):
+    """mla_prefill_attn_2seg: the last chunk's keys and the new tokens' keys
+    (causal) in one pass, merged into a state holding further keys; the
+    result must be the plain softmax over all three key sets."""
+    require_gpu()
+    seed, nq, nA, nB, merge = case
+    say(f"attn two segments seed={seed} nq={nq} merge={merge}")
+    rng = np.random.default_rng(seed)
+    H, h0, h1 = 3, 0, 3
+    Hs = h1 - h0
+    nC = [int(x) for x in rng.integers(0, 200, len(nq))] if merge else [0] * len(nq)
+    B = len(nq)
+    cu_q = np.concatenate([[0], np.cumsum(nq)])
+    T = int(cu_q[-1])
+    q = mi.f32_to_bf16_bits(rng.standard_normal((T, H, 192)).astype(np.float32))
+    scale = 1 / math.sqrt(192)
+
+    def segment(n):
+        cu = np.concatenate([[0], np.cumsum(n)]); NK = max(int(cu[-1]), 1)
+        kn = mi.f32_to_bf16_bits(rng.standard_normal((Hs, NK, 128)).astype(np.float32))
+        v = mi.f32_to_bf16_bits(rng.standard_normal((Hs, NK, 128)).astype(np.float32))
+        lat = mi.f32_to_bf16_bits(rng.standard_normal((NK, 576)).astype(np.float32))
+        return cu, NK, kn, v, lat
+
+    cuA, NKA, knA, vA, latA = segment(nA)
+    cuB, NKB, knB, vB, latB = segment(nB)
+    cuC, NKC, knC, vC, latC = segment(nC)
+    acc = accl = None
+    if merge:
+        acc = torch.full((T, Hs, 128), float("nan"), dtype=torch.float32, device="cuda")
+        accl = torch.full((T, Hs), float("nan"), dtype=torch.float32, device="cuda")
+        mla.mla_prefill_attn(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knC), NKC * 128, bf16_dev(vC),
+                             NKC * 128, bf16_dev(latC), 576, _i32(cu_q), _i32(cuC), None, B, max(nq), scale, 0,
+                             acc, mla.DTYPE_FP32, Hs * 128, accl, Hs)
+    out = torch.full((T, Hs, 128), 9.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, Hs), 9.0, dtype=torch.float32, device="cuda")
+    mla.mla_prefill_attn_2seg(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knA), NKA * 128, bf16_dev(vA),
+                              NKA * 128, bf16_dev(latA), 576, _i32(cuA), bf16_dev(knB), NKB * 128,
+                              bf16_dev(vB), NKB * 128, bf16_dev(latB), 576, _i32(cuB), _i32(cu_q), B,
+                              max(nq), scale, acc, Hs * 128, accl, Hs, out, mla.DTYPE_BF16, Hs * 128, lse, Hs)
+    torch.cuda.synchronize()
+    go, gl = f64(out), f64(lse)
+    for b in range(B):
+        rows = np.arange(cu_q[b], cu_q[b + 1])
+        kc = np.arange(cuC[b], cuC[b + 1]); ka = np.arange(cuA[b], cuA[b + 1]); kb = np.arange(cuB[b], cuB[b + 1])
+        # keys C and A all visible; key j of B visible to row i iff j <= i + nB - nq
+        i = np.arange(nq[b])[:, None]
+        vis = np.concatenate([np.ones((nq[b], len(kc) + len(ka)), dtype=bool),
+                              np.arange(nB[b])[None, :] <= i + nB[b] - nq[b]], axis=1)
+        for hs in range(Hs):
+            kn = np.concatenate([knC[hs, kc], knA[hs, ka], knB[hs, kb]])
+            vv = np.concatenate([vC[hs, kc], vA[hs, ka], vB[hs, kb]])
+            kr = np.concatenate([latC[kc, 512:], latA[ka, 512:], latB[kb, 512:]])
+            ro, rl = orc.attend(orc.bf16_to_f64(q[rows, h0 + hs]), orc.bf16_to_f64(kn), orc.bf16_to_f64(kr),
+                                orc.bf16_to_f64(vv), scale, vis)
+            check_out(go[rows, hs], ro, what=f"b{b} h{hs} out")
+            n_keys = len(kc) + len(ka) + len(kb)
+            tol = LSE_FEW_KEYS if n_keys < FEW_KEYS else 1e-3
+            check_lse(gl[rows, hs], rl, tol=tol, what=f"b{b} h{hs} lse")
+
+
 # ---------------------------------------------------------------- absorbed-form attention
 
 @pytest.mark.parametrize("n_rows,pieces", [(37, [0, 300, 364, 1000, 1000]), (64, [0, 2048]), (130, [0, 31, 97])])
