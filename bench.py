@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MLA chunked-prefill TFLOP/s + prefill tokens/s; % of MFMA/HBM roofline"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_ctx_dsv3_hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_2seg_dsv3_hbm_traffic.json")
 
 
 class KernelTimer:
