@@ -67,15 +67,19 @@ def test_config1_tiny_all_outputs():
 
 
 # every merge arrangement of the chunk loop: separate mla_merge_states, only
-# the last merge fused into the causal pass, or every merge fused
-@pytest.mark.parametrize("chunk,fuse", [(64, "all"), (100, "all"), (4096, "all"), (64, "none"),
-                                        (100, "final")])
-def test_ragged_multichunk_bf16(chunk, fuse):
+# the last merge fused into the causal pass, every merge fused with the last
+# chunk and the causal pass in one launch (the default), or every merge fused
+# with separate last-chunk and causal launches
+@pytest.mark.parametrize("chunk,fuse,two_seg", [(64, "all", True), (100, "all", True), (4096, "all", True),
+                                                (64, "all", False), (100, "all", False), (64, "none", True),
+                                                (100, "final", True)])
+def test_ragged_multichunk_bf16(chunk, fuse, two_seg):
     require_gpu()
-    say(f"ragged bf16 chunk={chunk} fuse_merge={fuse}")
+    say(f"ragged bf16 chunk={chunk} fuse_merge={fuse} two_segment={two_seg}")
     prob = mi.make_problem(4, [320, 0, 64 * 9, 64], [70, 5, 300, 1], chunk, "bf16", seed=71,
                            extra_blocks=3, poison=True)
-    pre = ChunkedPrefill(prob, fuse_merge=fuse)
+    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg)
+    assert pre.two_seg == (two_seg and fuse == "all")
     _run(pre)
     _compare_chunked(prob, pre)
 
