@@ -443,6 +443,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       lse2 = m2 + __builtin_amdgcn_logf(wp + wt);
     }
   }
+  // The previous state is read in full before anything is written: out may
+  // be that state (in place), so a read after a store of this lane would
+  // have to wait for the store, and 16 read/write round trips in a row
+  // measured 8% of a merging pass.
+  f32x4 prv[16];
+  if (kMerge && c_prev != 0.f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      prv[i] = *reinterpret_cast<const f32x4*>(pp + (i >> 2) * 32 + 8 * (i & 3) + 4 * g);
+  }
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       float o0 = O[d][4 * qq + 0] * c_this, o1 = O[d][4 * qq + 1] * c_this;
       float o2 = O[d][4 * qq + 2] * c_this, o3 = O[d][4 * qq + 3] * c_this;
       if (kMerge && c_prev != 0.f) {
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(pp + dv);
+        const f32x4 pv = prv[4 * d + qq];
         o0 = fmaf(c_prev, pv.x, o0); o1 = fmaf(c_prev, pv.y, o1);
         o2 = fmaf(c_prev, pv.z, o2); o3 = fmaf(c_prev, pv.w, o3);
       }
