@@ -212,7 +212,9 @@ int mla_prefill_attn(const void* q, int64_t q_row_stride, int H_q, int h_begin, 
  * side with lse = -inf contributes nothing (its out is not read), both -inf
  * give out = 0 and lse = -inf. out and lse may be the previous state itself
  * (same pointers and strides, out_dtype = MLA_DTYPE_FP32): each element is
- * read before it is written. Any other overlap is undefined.
+ * read before it is written, and rows of a request with no keys in this pass
+ * are left untouched (the merge with an empty set is the identity). Any
+ * other overlap is undefined.
  */
 int mla_prefill_attn_merge(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
                            const void* k_nope, int64_t k_head_stride,

@@ -140,6 +140,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     ntiles += kend2 > 0 ? (kend2 + kTileK - 1) / kTileK : 0;
   }
 
+  // Merging an empty key set into a state in place leaves the state as it
+  // is (the identity of the merge): such a workgroup has nothing to read or
+  // write. In a chunk loop over ragged requests this skips every request
+  // whose context ended in an earlier chunk.
+  if constexpr (kMerge && kOutDt == MLA_DTYPE_FP32) {
+    if (ntiles == 0 && a.out == static_cast<const void*>(a.prev) && a.out_rs == a.prev_rs &&
+        a.lse == a.prev_lse && a.lse_rs == a.prev_lse_rs)
+      return;
+  }
+
   const int row = r0 + wave * 32 + l32;      // this lane's query row (request-local)
   const bool row_ok = row < n_q;
   const int h = a.h_begin + hs;
