@@ -325,6 +325,22 @@ int mla_merge_states(const void* out_a, int dtype_a, const float* lse_a,
                      void* stream);
 
 /*
+ * mla_merge_states_n -- the [DSMLA] 4.3 merge of `pieces` states per row in
+ * one pass, for the partial states of key ranges attended separately. By the
+ * merge identity this equals any order of pairwise mla_merge_states calls.
+ *
+ * Piece p's states: outs[(p * rows + r) * 128 + d] (dtype_in), lses[p * rows + r].
+ *   m = max_p lse_p; w_p = e^{lse_p - m} (0 for lse_p = -inf);
+ *   out[r * 128 + d] = sum_p w_p outs_p[r][d] / sum_p w_p; lse_out[r] = m + ln sum_p w_p.
+ * Pieces at -inf contribute nothing (their out is not read); all at -inf
+ * gives out = 0, lse = -inf. pieces >= 1. out and lse_out may be piece 0's
+ * states (same layout); any other overlap is undefined. dtype_in, dtype_out:
+ * MLA_DTYPE_BF16 or MLA_DTYPE_FP32; state pointers 16-byte aligned.
+ */
+int mla_merge_states_n(const void* outs, int dtype_in, const float* lses, int pieces, int64_t rows,
+                       void* out, int dtype_out, float* lse_out, void* stream);
+
+/*
  * mla_rope_relocate_q -- [REDKNOT] Abstract and section 2 (query-side RoPE
  * relocation): for every row r < T and head h < H, the rope part
  * q[r * q_row_stride + h * 192 + 128 + (0..63)] is rotated by the angle

@@ -28,7 +28,7 @@ ROPE_HALF = 1
 EXPORTS = (
     "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_cache_append", "mla_pack_weight_t",
     "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_prefill_attn_2seg", "mla_absorb_q",
-    "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states",
+    "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states", "mla_merge_states_n",
     "mla_rope_relocate_q",
     "mla_head_partition_merge", "mla_token_hash", "mla_artifact_check",
 )
@@ -83,6 +83,7 @@ _SIGS = {
     "mla_absorbed_attn": [P, I32, P, I64, P, I32, F32, P, I32, P, P],
     "mla_absorb_out": [P, I32, P, I32, I32, I32, P, I64, P],
     "mla_merge_states": [P, I32, P, P, I32, P, I64, P, I32, P, P],
+    "mla_merge_states_n": [P, I32, P, I32, I64, P, I32, P, P],
     "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
     "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
     "mla_artifact_check": [ctypes.POINTER(ArtifactMeta), ctypes.POINTER(ArtifactMeta), ctypes.POINTER(I32)],
@@ -213,6 +214,11 @@ def mla_merge_states(out_a, dtype_a, lse_a, out_b, dtype_b, lse_b, rows, out, dt
                      stream=None):
     return _call("mla_merge_states", _ptr(out_a), dtype_a, _ptr(lse_a), _ptr(out_b), dtype_b,
                  _ptr(lse_b), rows, _ptr(out), dtype_out, _ptr(lse_out), _stream(stream))
+
+
+def mla_merge_states_n(outs, dtype_in, lses, pieces, rows, out, dtype_out, lse_out, stream=None):
+    return _call("mla_merge_states_n", _ptr(outs), dtype_in, _ptr(lses), pieces, rows, _ptr(out), dtype_out,
+                 _ptr(lse_out), _stream(stream))
 
 
 def mla_rope_relocate_q(q_in, q_out, q_row_stride, T, H, delta, rope_base=10000.0,

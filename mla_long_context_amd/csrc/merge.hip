@@ -101,6 +101,67 @@ int launch_b(int dtb, int dto, dim3 g, hipStream_t s, const void* oa, const floa
   return launch_o<kDa, MLA_DTYPE_FP32>(dto, g, s, oa, la, ob, lb, rows, out, lo);
 }
 
+// The merge of `pieces` states per row in one pass (the merge of the same
+// section applied to all of them at once, which by its identity equals any
+// order of pairwise merges): m = max_p l_p, w_p = e^{l_p - m} (0 for a piece
+// at -inf), out = sum_p w_p o_p / sum_p w_p, lse = m + ln sum_p w_p. Each
+// state is read once; the pieces' lse are read twice (max, then weights).
+template <int kDi, int kDo>
+__global__ __launch_bounds__(kThreads) void merge_n_kernel(const void* outs, const float* lses, int pieces,
+                                                            int64_t rows, void* out, float* lo) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = gid >> 4;
+  const int part = (int)(gid & 15);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int p = 0; p < pieces; ++p) m = fmaxf(m, lses[(int64_t)p * rows + row]);
+  const int64_t off = row * kDv + part * 8;
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = 0.f;
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
+    float s = 0.f;
+    int p = 0;
+    // four pieces per round, their loads issued together
+    for (; p + 4 <= pieces; p += 4) {
+      float w[4], f[4][8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float l = lses[(int64_t)(p + k) * rows + row];
+        w[k] = (l == -INFINITY) ? 0.f : expf(l - m);
+        if (w[k] != 0.f) Vec8<kDi>::load(outs, (int64_t)(p + k) * rows * kDv + off, f[k]);
+        else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[k][j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s += w[k];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = fmaf(w[k], f[k][j], r[j]);
+      }
+    }
+    for (; p < pieces; ++p) {
+      const float l = lses[(int64_t)p * rows + row];
+      if (l == -INFINITY) continue;
+      const float w = expf(l - m);
+      float f[8];
+      Vec8<kDi>::load(outs, (int64_t)p * rows * kDv + off, f);
+      s += w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = fmaf(w, f[j], r[j]);
+    }
+    const float inv = 1.f / s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] *= inv;
+    lse = m + logf(s);
+  }
+  Vec8<kDo>::store(out, off, r);
+  if (part == 0) lo[row] = lse;
+}
+
 bool ok_dt(int d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP32; }
 
 }  // namespace
@@ -125,4 +186,38 @@ extern "C" int mla_merge_states(const void* out_a, int dtype_a, const float* lse
   if (dtype_a == MLA_DTYPE_BF16)
     return launch_b<MLA_DTYPE_BF16>(dtype_b, dtype_out, g, s, out_a, lse_a, out_b, lse_b, rows, out, lse_out);
   return launch_b<MLA_DTYPE_FP32>(dtype_b, dtype_out, g, s, out_a, lse_a, out_b, lse_b, rows, out, lse_out);
+}
+
+extern "C" int mla_merge_states_n(const void* outs, int dtype_in, const float* lses, int pieces, int64_t rows,
+                                  void* out, int dtype_out, float* lse_out, void* stream) {
+  mla_clear_error();
+  MLA_REQUIRE(rows >= 0 && pieces >= 1, MLA_ERR_INVALID_ARG,
+              "mla_merge_states_n: need rows (%lld) >= 0 and pieces (%d) >= 1", (long long)rows, pieces);
+  if (rows == 0) return MLA_OK;
+  MLA_REQUIRE(outs && lses && out && lse_out, MLA_ERR_INVALID_ARG, "mla_merge_states_n: null pointer argument");
+  MLA_REQUIRE(ok_dt(dtype_in) && ok_dt(dtype_out), MLA_ERR_UNSUPPORTED,
+              "mla_merge_states_n: dtypes must be bf16 or fp32 (got %d, %d)", dtype_in, dtype_out);
+  MLA_REQUIRE(mla_aligned16(outs) && mla_aligned16(out), MLA_ERR_INVALID_ARG,
+              "mla_merge_states_n: state pointers must be 16-byte aligned");
+  MLA_REQUIRE(rows <= (int64_t)1 << 40 && (int64_t)pieces * rows <= (int64_t)1 << 40, MLA_ERR_INVALID_ARG,
+              "mla_merge_states_n: rows too large");
+  const int64_t threads = rows * 16;
+  dim3 g((unsigned)((threads + kThreads - 1) / kThreads));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype_in == MLA_DTYPE_BF16) {
+    if (dtype_out == MLA_DTYPE_BF16)
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_BF16>), g, dim3(kThreads), 0, s, outs, lses,
+                         pieces, rows, out, lse_out);
+    else
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_FP32>), g, dim3(kThreads), 0, s, outs, lses,
+                         pieces, rows, out, lse_out);
+  } else {
+    if (dtype_out == MLA_DTYPE_BF16)
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_BF16>), g, dim3(kThreads), 0, s, outs, lses,
+                         pieces, rows, out, lse_out);
+    else
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_FP32>), g, dim3(kThreads), 0, s, outs, lses,
+                         pieces, rows, out, lse_out);
+  }
+  return mla_check_launch("mla_merge_states_n");
 }

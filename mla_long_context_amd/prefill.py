@@ -274,9 +274,11 @@ class ReusePrefill:
     equals the chunk-by-chunk merge."""
 
     def __init__(self, prob, device="cuda", chunk=None, split=4096, local_path="absorbed",
-                 split_local=8192, artifact=None, request=None):
+                 split_local=8192, artifact=None, request=None, merge="one_pass"):
         assert prob.is_reuse
         assert local_path in ("absorbed", "decompressed")
+        assert merge in ("one_pass", "tree")
+        self.merge_mode = merge
         self.prob = prob
         prot_rows = np.asarray(prob.prot_rows, dtype=np.int64)
         # An artifact built offline (ArtifactBuilder) replaces the problem's
@@ -439,12 +441,19 @@ class ReusePrefill:
                             out, odt, lse, stream)
 
     def _merge_tree(self, part, partl, n_rows, fin, finl, stream, n_pieces=None):
-        """Merge the partial states of all pieces into (fin, finl). Each level
-        merges the first half of the remaining pieces with the last half in
-        place (fp32; an odd middle piece waits for the next level); the last
-        level writes the bf16 result."""
+        """Merge the partial states of all pieces into (fin, finl): in one
+        pass over all of them (mla_merge_states_n, the default), or as a
+        tree of pairwise merges (merge="tree"), where each level merges the
+        first half of the remaining pieces with the last half in place (fp32;
+        an odd middle piece waits for the next level) and the last level
+        writes the bf16 result."""
         n = self.n_pieces if n_pieces is None else n_pieces
         heads = part.shape[1]
+        if n <= 1:
+            return          # a single piece was written to (fin, finl) directly
+        if self.merge_mode == "one_pass":
+            L.mla_merge_states_n(part, L.DTYPE_FP32, partl, n, n_rows * heads, fin, L.DTYPE_BF16, finl, stream)
+            return
         while n > 1:
             h = n // 2
             m = n - h
@@ -516,9 +525,11 @@ class ReusePrefill:
 
     def work(self) -> dict:
         """Algorithmic work of one run, in the same units as ChunkedPrefill.work.
-        The merge tree makes n_pieces - 1 merges per (row, head); each reads
-        two fp32 states (2 * 516 B) and writes one (516 B), the last one in
-        bf16 (260 B)."""
+        Merges: the one-pass merge reads every piece's fp32 state once
+        (516 B per piece and (row, head)) and writes one bf16 state (260 B);
+        the pairwise tree makes n_pieces - 1 merges per (row, head), each
+        reading two fp32 states (2 * 516 B) and writing one (516 B), the last
+        one in bf16 (260 B)."""
         H, HL, HG, T, P, Ld = self.H, self.HL, self.HG, self.T, self.P, self.Ldoc
         n = self.n_pieces
         if self.absorbed:
@@ -536,7 +547,11 @@ class ReusePrefill:
             local = 640 * Ld * P * HL
             absorb = 0
         def tree(rows, k):
-            return rows * ((k - 2) * 3 * 516 + (2 * 516 + 260)) if k > 1 else 0
+            if k <= 1:
+                return 0
+            if self.merge_mode == "one_pass":
+                return rows * (k * 516 + 260)
+            return rows * ((k - 2) * 3 * 516 + (2 * 516 + 260))
         merge_bytes = tree(T * HG, n) + tree(merge_rows - T * HG, self.n_pieces_L)
         glob = 640 * Ld * T * HG
         return dict(

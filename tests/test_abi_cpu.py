@@ -112,6 +112,10 @@ def test_merge_rope_partition_pack_validation(lib):
     assert _err(mla.mla_merge_states, FAKE, 9, FAKE, FAKE, 0, FAKE, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_UNSUPPORTED
     assert _err(mla.mla_merge_states, FAKE, 0, FAKE, FAKE + 4, 0, FAKE, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
     assert mla.mla_merge_states(None, 0, None, None, 0, None, 0, None, 0, None, stream=0) == 0
+    assert _err(mla.mla_merge_states_n, FAKE, 0, FAKE, 0, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG  # no piece
+    assert _err(mla.mla_merge_states_n, FAKE, 7, FAKE, 3, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_merge_states_n, FAKE + 8, 0, FAKE, 3, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert mla.mla_merge_states_n(None, 0, None, 3, 0, None, 0, None, stream=0) == 0
     assert _err(mla.mla_rope_relocate_q, FAKE, FAKE, 8 * 192, 4, 8, 4096, 10000.0, 3)[0] == _lib.MLA_ERR_UNSUPPORTED
     assert _err(mla.mla_rope_relocate_q, FAKE, FAKE, 100, 4, 8, 4096, 10000.0, 0)[0] == _lib.MLA_ERR_INVALID_ARG
     assert _err(mla.mla_rope_relocate_q, FAKE, FAKE, 8 * 192, 4, 8, 4096, 0.5, 0)[0] == _lib.MLA_ERR_INVALID_ARG
@@ -127,6 +131,10 @@ def test_last_error_is_thread_local_and_cleared(lib):
     _err(mla.mla_pack_weight_t, FAKE, 10, 16, FAKE)
     assert b"multiples of 8" in lib.mla_last_error()
     assert mla.mla_merge_states(None, 0, None, None, 0, None, 0, None, 0, None, stream=0) == 0
+    assert _err(mla.mla_merge_states_n, FAKE, 0, FAKE, 0, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG  # no piece
+    assert _err(mla.mla_merge_states_n, FAKE, 7, FAKE, 3, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert _err(mla.mla_merge_states_n, FAKE + 8, 0, FAKE, 3, 4, FAKE, 0, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert mla.mla_merge_states_n(None, 0, None, 3, 0, None, 0, None, stream=0) == 0
     assert lib.mla_last_error() == b""
 
 

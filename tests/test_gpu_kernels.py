@@ -181,6 +181,46 @@ def test_merge_states(da, db, do):
         assert torch.equal(ta2, out) and torch.equal(tla2, lout)
 
 
+@pytest.mark.parametrize("pieces,di,do", [(1, 2, 0), (2, 2, 2), (5, 2, 0), (9, 0, 2), (64, 2, 0)])
+def test_merge_states_n(pieces, di, do):
+    """mla_merge_states_n against the oracle's pairwise merge folded over the
+    pieces: empty pieces, rows with every piece empty, extreme weights, a
+    ragged piece count; in place into piece 0 as well."""
+    require_gpu()
+    rng = np.random.default_rng(45 + pieces)
+    rows = 1031
+    o = rng.standard_normal((pieces, rows, 128)).astype(np.float32)
+    lse = (rng.standard_normal((pieces, rows)) * 3 + 8).astype(np.float32)
+    lse[:, :5] = -np.inf                             # every piece empty
+    lse[0, 5:40] = -np.inf                           # some pieces empty
+    if pieces > 2:
+        lse[1:3, 40:60] = -np.inf
+    lse[0, 60] = 80.0; lse[-1, 60] = -80.0           # extreme weights
+    tdt = {0: torch.bfloat16, 2: torch.float32}
+    to = torch.tensor(o).to(tdt[di]).cuda()
+    tl = torch.tensor(lse).cuda()
+    out = torch.empty((rows, 128), dtype=tdt[do], device="cuda")
+    lout = torch.empty(rows, dtype=torch.float32, device="cuda")
+    mla.mla_merge_states_n(to, di, tl, pieces, rows, out, do, lout)
+    to2 = to.clone(); tl2 = tl.clone()
+    mla.mla_merge_states_n(to2, di, tl2, pieces, rows, to2[0], di, tl2[0])
+    torch.cuda.synchronize()
+    go = f64(to)
+    # fold from the merge identity (0, -inf), so that a single empty piece
+    # also gives (0, -inf)
+    ref_o, ref_l = np.zeros((rows, 128)), np.full(rows, -np.inf)
+    for p in range(pieces):
+        ref_o, ref_l = orc.merge_states(ref_o, ref_l, go[p], lse[p].astype(np.float64))
+    tol = 1e-5 if do == 2 else 2 ** -8
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - ref_o) / np.maximum(np.abs(ref_o), 1.0)) <= tol
+    check_lse(f64(lout), ref_l, tol=1e-5)
+    assert np.all(got[:5] == 0.0)
+    if di == do:
+        assert torch.equal(to2[0], out) and torch.equal(tl2[0], lout)
+
+
 # ---------------------------------------------------------------- rope relocation
 
 @pytest.mark.parametrize("delta", [0, 1, 4096, 2 ** 18])

@@ -98,16 +98,20 @@ def test_ragged_multichunk_fp8():
 # chunk with a ragged last one, and the whole document as a single piece
 # split / split_local: keys per Global / Local piece (one piece per chunk,
 # four per chunk with a ragged last one, the whole document as one piece)
-@pytest.mark.parametrize("split,split_local,chunk,local", [
-    (2048, 8192, 256, "absorbed"), (64, 64, 256, "absorbed"), (64, 128, 256, "absorbed"),
-    (4096, 8192, 2048, "absorbed"), (2048, 2048, 256, "decompressed"), (64, 64, 256, "decompressed"),
-    (4096, 4096, 2048, "decompressed")])
-def test_reuse_small_all_outputs(split, split_local, chunk, local):
+# the pieces' states merge in one pass by default; two cases keep the
+# pairwise tree
+@pytest.mark.parametrize("split,split_local,chunk,local,merge", [
+    (2048, 8192, 256, "absorbed", "one_pass"), (64, 64, 256, "absorbed", "one_pass"),
+    (64, 128, 256, "absorbed", "one_pass"), (4096, 8192, 2048, "absorbed", "one_pass"),
+    (2048, 2048, 256, "decompressed", "one_pass"), (64, 64, 256, "decompressed", "one_pass"),
+    (4096, 4096, 2048, "decompressed", "one_pass"), (64, 128, 256, "absorbed", "tree"),
+    (64, 64, 256, "decompressed", "tree")])
+def test_reuse_small_all_outputs(split, split_local, chunk, local, merge):
     require_gpu()
-    say(f"reuse small split={split}/{split_local} chunk={chunk} local={local}")
+    say(f"reuse small split={split}/{split_local} chunk={chunk} local={local} merge={merge}")
     prob = mi.make_reuse_problem(H=8, n_local=7, L=1024 + 64, T=300, delta=4096, P=9,
                                  d_mid=256, d_model=384, chunk=chunk, seed=73)
-    pre = ReusePrefill(prob, split=split, local_path=local, split_local=split_local)
+    pre = ReusePrefill(prob, split=split, local_path=local, split_local=split_local, merge=merge)
     say(f"  {pre.n_pieces} / {pre.n_pieces_L} pieces")
     y = pre.run()
     torch.cuda.synchronize()
