@@ -104,62 +104,91 @@ int launch_b(int dtb, int dto, dim3 g, hipStream_t s, const void* oa, const floa
 // The merge of `pieces` states per row in one pass (the merge of the same
 // section applied to all of them at once, which by its identity equals any
 // order of pairwise merges): m = max_p l_p, w_p = e^{l_p - m} (0 for a piece
-// at -inf), out = sum_p w_p o_p / sum_p w_p, lse = m + ln sum_p w_p. Each
-// state is read once; the pieces' lse are read twice (max, then weights).
+// at -inf), out = sum_p w_p o_p / sum_p w_p, lse = m + ln sum_p w_p.
+//
+// A workgroup owns 4 rows (16 lanes per row, 8 values per lane) and W <= 8
+// wavefronts; wavefront w folds pieces w, w + W, w + 2W, ... into a running
+// state (m, s, r) with the usual rescaling by e^{m_old - m_new}, four pieces'
+// loads in flight per round. Wavefront 0 then folds the W states from LDS in
+// wavefront order, so the result does not depend on timing. Splitting the
+// pieces over wavefronts keeps many loads in flight when there are few rows
+// and many pieces (thousands of rows, tens of pieces). Every state is read
+// once, before anything is written, so the output may alias piece 0.
+constexpr int kMaxW = 8;
+
 template <int kDi, int kDo>
-__global__ __launch_bounds__(kThreads) void merge_n_kernel(const void* outs, const float* lses, int pieces,
-                                                            int64_t rows, void* out, float* lo) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gid >> 4;
-  const int part = (int)(gid & 15);
-  if (row >= rows) return;
-  float m = -INFINITY;
-  for (int p = 0; p < pieces; ++p) m = fmaxf(m, lses[(int64_t)p * rows + row]);
-  const int64_t off = row * kDv + part * 8;
-  float r[8];
+__global__ __launch_bounds__(kMaxW * 64) void merge_n_kernel(const void* outs, const float* lses, int pieces,
+                                                              int64_t rows, void* out, float* lo) {
+  __shared__ float sh[kMaxW - 1][10][64];      // [wavefront 1..W-1][m, s, r0..r7][lane]
+  const int W = (int)(blockDim.x >> 6);
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t row = (int64_t)blockIdx.x * 4 + (lane >> 4);
+  const bool live = row < rows;
+  const int64_t off = row * kDv + (lane & 15) * 8;
+  float m = -INFINITY, s = 0.f, r[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = 0.f;
-  float lse = -INFINITY;
-  if (m != -INFINITY) {
-    float s = 0.f;
-    int p = 0;
-    // four pieces per round, their loads issued together
-    for (; p + 4 <= pieces; p += 4) {
-      float w[4], f[4][8];
+  if (live) {
+    for (int p0 = wave; p0 < pieces; p0 += 4 * W) {
+      float l[4], f[4][8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float l = lses[(int64_t)(p + k) * rows + row];
-        w[k] = (l == -INFINITY) ? 0.f : expf(l - m);
-        if (w[k] != 0.f) Vec8<kDi>::load(outs, (int64_t)(p + k) * rows * kDv + off, f[k]);
-        else {
+        const int p = p0 + k * W;
+        l[k] = -INFINITY;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) f[k][j] = 0.f;
+        for (int j = 0; j < 8; ++j) f[k][j] = 0.f;
+        if (p < pieces) {
+          l[k] = lses[(int64_t)p * rows + row];
+          Vec8<kDi>::load(outs, (int64_t)p * rows * kDv + off, f[k]);
         }
       }
+      const float mn = fmaxf(fmaxf(m, fmaxf(l[0], l[1])), fmaxf(l[2], l[3]));
+      if (mn == -INFINITY) continue;
+      const float c = expf(m - mn);              // 0 while the state is empty
+      s *= c;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] *= c;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        s += w[k];
+        const float w = (l[k] == -INFINITY) ? 0.f : expf(l[k] - mn);
+        s += w;
+        // a piece of weight 0 contributes nothing, whatever its values hold
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = fmaf(w[k], f[k][j], r[j]);
+        for (int j = 0; j < 8; ++j) r[j] = fmaf(w, w != 0.f ? f[k][j] : 0.f, r[j]);
       }
+      m = mn;
     }
-    for (; p < pieces; ++p) {
-      const float l = lses[(int64_t)p * rows + row];
-      if (l == -INFINITY) continue;
-      const float w = expf(l - m);
-      float f[8];
-      Vec8<kDi>::load(outs, (int64_t)p * rows * kDv + off, f);
-      s += w;
+  }
+  if (W > 1) {
+    if (wave > 0) {
+      sh[wave - 1][0][lane] = m;
+      sh[wave - 1][1][lane] = s;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = fmaf(w, f[j], r[j]);
+      for (int j = 0; j < 8; ++j) sh[wave - 1][2 + j][lane] = r[j];
     }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int v = 0; v < W - 1; ++v) {
+      const float m2 = sh[v][0][lane];
+      const float mn = fmaxf(m, m2);
+      if (mn == -INFINITY) continue;
+      const float ca = expf(m - mn), cb = expf(m2 - mn);
+      s = s * ca + sh[v][1][lane] * cb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = r[j] * ca + sh[v][2 + j][lane] * cb;
+      m = mn;
+    }
+  }
+  if (!live) return;
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
     const float inv = 1.f / s;
 #pragma unroll
     for (int j = 0; j < 8; ++j) r[j] *= inv;
     lse = m + logf(s);
   }
   Vec8<kDo>::store(out, off, r);
-  if (part == 0) lo[row] = lse;
+  if ((lane & 15) == 0) lo[row] = lse;
 }
 
 bool ok_dt(int d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP32; }
@@ -201,22 +230,24 @@ extern "C" int mla_merge_states_n(const void* outs, int dtype_in, const float* l
               "mla_merge_states_n: state pointers must be 16-byte aligned");
   MLA_REQUIRE(rows <= (int64_t)1 << 40 && (int64_t)pieces * rows <= (int64_t)1 << 40, MLA_ERR_INVALID_ARG,
               "mla_merge_states_n: rows too large");
-  const int64_t threads = rows * 16;
-  dim3 g((unsigned)((threads + kThreads - 1) / kThreads));
+  MLA_REQUIRE((rows + 3) / 4 <= 0x7fffffff, MLA_ERR_INVALID_ARG, "mla_merge_states_n: rows too large");
+  // as many wavefronts per 4-row group as pieces, up to 8
+  const int W = pieces < kMaxW ? pieces : kMaxW;
+  dim3 g((unsigned)((rows + 3) / 4)), blk((unsigned)(W * 64));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype_in == MLA_DTYPE_BF16) {
     if (dtype_out == MLA_DTYPE_BF16)
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_BF16>), g, dim3(kThreads), 0, s, outs, lses,
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_BF16>), g, blk, 0, s, outs, lses,
                          pieces, rows, out, lse_out);
     else
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_FP32>), g, dim3(kThreads), 0, s, outs, lses,
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_FP32>), g, blk, 0, s, outs, lses,
                          pieces, rows, out, lse_out);
   } else {
     if (dtype_out == MLA_DTYPE_BF16)
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_BF16>), g, dim3(kThreads), 0, s, outs, lses,
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_BF16>), g, blk, 0, s, outs, lses,
                          pieces, rows, out, lse_out);
     else
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_FP32>), g, dim3(kThreads), 0, s, outs, lses,
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_FP32>), g, blk, 0, s, outs, lses,
                          pieces, rows, out, lse_out);
   }
   return mla_check_launch("mla_merge_states_n");
