@@ -332,8 +332,9 @@ int mla_merge_states(const void* out_a, int dtype_a, const float* lse_a,
  * Piece p's states: outs[(p * rows + r) * 128 + d] (dtype_in), lses[p * rows + r].
  *   m = max_p lse_p; w_p = e^{lse_p - m} (0 for lse_p = -inf);
  *   out[r * 128 + d] = sum_p w_p outs_p[r][d] / sum_p w_p; lse_out[r] = m + ln sum_p w_p.
- * Pieces at -inf contribute nothing (their out is not read); all at -inf
- * gives out = 0, lse = -inf. pieces >= 1. out and lse_out may be piece 0's
+ * Pieces at -inf contribute nothing (their out values are loaded but ignored,
+ * whatever they hold, so all pieces * rows states must be readable memory);
+ * all at -inf gives out = 0, lse = -inf. pieces >= 1. out and lse_out may be piece 0's
  * states (same layout); any other overlap is undefined. dtype_in, dtype_out:
  * MLA_DTYPE_BF16 or MLA_DTYPE_FP32; state pointers 16-byte aligned.
  */
