@@ -114,7 +114,8 @@ int launch_b(int dtb, int dto, dim3 g, hipStream_t s, const void* oa, const floa
 // pieces over wavefronts keeps many loads in flight when there are few rows
 // and many pieces (thousands of rows, tens of pieces). Every state is read
 // once, before anything is written, so the output may alias piece 0.
-constexpr int kMaxW = 8;
+constexpr int kMaxW = 8;    // wavefronts per workgroup, at most
+constexpr int kPer = 4;     // pieces whose loads one wavefront issues together
 
 template <int kDi, int kDo>
 __global__ __launch_bounds__(kMaxW * 64) void merge_n_kernel(const void* outs, const float* lses, int pieces,
@@ -129,10 +130,10 @@ __global__ __launch_bounds__(kMaxW * 64) void merge_n_kernel(const void* outs, c
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = 0.f;
   if (live) {
-    for (int p0 = wave; p0 < pieces; p0 += 4 * W) {
-      float l[4], f[4][8];
+    for (int p0 = wave; p0 < pieces; p0 += kPer * W) {
+      float l[kPer], f[kPer][8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kPer; ++k) {
         const int p = p0 + k * W;
         l[k] = -INFINITY;
 #pragma unroll
@@ -142,14 +143,16 @@ __global__ __launch_bounds__(kMaxW * 64) void merge_n_kernel(const void* outs, c
           Vec8<kDi>::load(outs, (int64_t)p * rows * kDv + off, f[k]);
         }
       }
-      const float mn = fmaxf(fmaxf(m, fmaxf(l[0], l[1])), fmaxf(l[2], l[3]));
+      float mn = m;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) mn = fmaxf(mn, l[k]);
       if (mn == -INFINITY) continue;
       const float c = expf(m - mn);              // 0 while the state is empty
       s *= c;
 #pragma unroll
       for (int j = 0; j < 8; ++j) r[j] *= c;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kPer; ++k) {
         const float w = (l[k] == -INFINITY) ? 0.f : expf(l[k] - mn);
         s += w;
         // a piece of weight 0 contributes nothing, whatever its values hold
