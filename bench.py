@@ -108,7 +108,7 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFI
     kf = gib_kib / (sum(cal_f) / len(cal_f))
     kw = gib_kib / (sum(cal_w) / len(cal_w))
     # the two-segment pass (last chunk + new tokens; bf16 out, merged)
-    ctx = lambda n: "attn_kernel<8, false, false, 0, true, true>" in n
+    ctx = lambda n: "attn_kernel<4, false, false, 0, true, true>" in n
     f = [v for n, v in _counter_rows(fetch_csv, "FETCH_SIZE") if ctx(n)]
     w = [v for n, v in _counter_rows(write_csv, "WRITE_SIZE") if ctx(n)]
     fetch_b = sum(f) / len(f) * 1024 * kf

@@ -578,14 +578,16 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
                 "%s: previous state must be 16-byte aligned with row stride >= Hsel*128 (multiple of 4)", fn);
   }
 
-  // rows per workgroup: 256 (8 wavefronts) for long query sets, fewer when
-  // that would leave most wavefronts without rows or the grid too small.
-  // Causal passes use at most 4 wavefronts: in a 256-row tile the wavefronts
-  // above the diagonal idle through up to 3.5 key tiles each, and the 80 KB
-  // two-stage LDS of the 4-wavefront kernel lets two workgroups share a CU.
-  int NW = 8;
+  // rows per workgroup: 128 (4 wavefronts; two workgroups share a CU, 80 KB
+  // of two-stage LDS each) by default. Ragged query sets fill 128-row tiles
+  // better than 256-row ones, and in a causal segment fewer wavefronts idle
+  // above the diagonal. Launches with row ids repeat one full query set for
+  // every key piece, so their tiles are never ragged: above 128 rows they use
+  // 8 wavefronts (256 rows), which halves the K/V tile loads per row. 64 rows
+  // (2 wavefronts) when no request has more.
+  int NW = 4;
   if (max_q <= 64) NW = 2;
-  else if (max_q <= 128 || causal) NW = 4;
+  else if (q_row_ids != nullptr && max_q > 128 && !causal) NW = 8;
   const int rows = 32 * NW;
   const int n_qt = (max_q + rows - 1) / rows;
   // (request, head) pairs rounded up to a multiple of the 8 XCDs (the
@@ -612,8 +614,7 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool rid = q_row_ids != nullptr, c = causal != 0;
   if (seg2) {
-    if (NW == 8) launch_seg2m<8>(merge, out_dtype, g, s, a);
-    else if (NW == 4) launch_seg2m<4>(merge, out_dtype, g, s, a);
+    if (NW == 4) launch_seg2m<4>(merge, out_dtype, g, s, a);   // no row ids: never 8 wavefronts
     else launch_seg2m<2>(merge, out_dtype, g, s, a);
     return mla_check_launch(fn);
   }

@@ -321,13 +321,13 @@ def _attn_case(seed, H, h0, h1, nq, nk, causal, out_dtype, row_ids=False):
 def test_attention_varlen(causal, out_dtype):
     require_gpu()
     say(f"attn varlen causal={causal} out={out_dtype}")
-    # several query tiles (NW=8 -> 256 rows), ragged tails, an empty request
+    # several query tiles (128 rows each), ragged tails, an empty request
     nq = [300, 1, 0, 77]
     nk = [300 + 130, 1, 5, 77] if causal else [700, 64, 5, 0]
     _attn_case(50 + causal, 3, 0, 3, nq, nk, causal, out_dtype)
 
 
-@pytest.mark.parametrize("nq", [[64], [100], [40, 64]])
+@pytest.mark.parametrize("nq", [[64], [100], [40, 64], [300, 77]])
 def test_attention_row_ids_and_head_range(nq):
     require_gpu()
     say(f"attn row ids nq={nq}")
