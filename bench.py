@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of MLA chunked prefill on one MI355X.
 
-Workload (default): DeepSeek-V3 geometry, one layer, 128 heads, 4 requests x
-(8192 cached context tokens + 1024 new tokens), 64-token blocks in a shuffled
-pool, context chunk 4096, bf16 cache. A step is one pass of the whole path:
-per context chunk gather -> kv_b_proj decompression -> attention -> LSE merge
-into the running state; the last chunk's attention also covers the new
-tokens' keys (decompressed beside the chunk's, causal) and writes the result.
-Inputs are seeded synthetic data resident in HBM before timing starts.
+Headline workload (default): the fp8 ragged batch, the largest single-GPU
+configuration: one layer, 128 heads, 16 requests with context lengths uniform
+in [1024, 32768] (multiples of 64) and 256..2048 new tokens each, c_kv stored
+as fp8-e4m3 with one fp32 scale per token beside bf16 k_rope, 64-token blocks
+in a shuffled pool, context chunk 4096. A step is one pass of the whole path:
+per context chunk gather (fp8 dequantisation) -> kv_b_proj decompression ->
+attention -> LSE merge into the running state; the last chunk's attention
+also covers the new tokens' keys (decompressed beside the chunk's, causal)
+and writes the result. Inputs are seeded synthetic data resident in HBM
+before timing starts.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 
@@ -17,9 +20,12 @@ timed steps (eager launches; --graph replays one step captured into a HIP
 graph), prefill tokens/s, the roofline of the dominant kernel (per-launch
 duration from HIP events on the launch stream, taken in a second pass of the
 same number of steps, since events between launches add fences to the step),
-and the fp64 CPU oracle timed on a bounded sample on this host.
+the fp64 CPU oracle timed on a bounded sample on this host's cores, and one
+sub-record per other standard workload (bf16 DeepSeek-V3 geometry, long
+context, head-partitioned reuse), each with its own dominant kernel's
+roofline (--no-sub skips them).
 
-    python bench.py --workload {1..5}   # the other standard workloads
+    python bench.py --workload {1..5}   # one standard workload alone
     python bench.py --append            # the cache write path
     python bench.py --artifact          # the offline Local-head artifact build
 """
@@ -39,7 +45,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MLA chunked-prefill TFLOP/s + prefill tokens/s; % of MFMA/HBM roofline"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_2seg_dsv3_hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+HEADLINE = 4                   # the fp8 ragged batch: the largest single-GPU workload
+SUB_WORKLOADS = (2, 3, 5)
+CSRC = os.path.join(ROOT, "mla_long_context_amd", "csrc")
+# timer span -> (kernel name in rocprofv3 traces, source file) for the HBM
+# counter records
+SPAN_KERNEL = {
+    "attn_ctx": ("attn_kernel<4, false, false, 2, false, false>", "attn.hip"),
+    "attn_ctx_merge": ("attn_kernel<4, false, false, 2, true, false>", "attn.hip"),
+    "attn_last": ("attn_kernel<4, false, false, 0, true, true>", "attn.hip"),
+    "attn_global": ("attn_kernel<8, false, true, 2, false, false>", "attn.hip"),
+    "attn_local": ("absorbed_attn_kernel", "absorbed.hip"),
+    "decompress": ("decompress_kernel", "gemm.hip"),
+    "gather": ("gather_kernel", "gather.hip"),
+}
 
 
 class KernelTimer:
@@ -73,15 +93,17 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(kernel_src):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    counters, scaled by a plain copy's counter reading; None when absent or
-    when the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_for(workload, span):
+    """HBM bytes per launch of a kernel from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters (each scaled by what the same counter reads for a
+    plain copy of known size); None when there is no record for this
+    workload and kernel, or the kernel's source changed since the counters
+    were taken."""
+    if span not in SPAN_KERNEL or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
-        d = json.load(f)
-    if d.get("source_sha256_16") != source_hash(kernel_src):
+        d = json.load(f).get(f"w{workload}:{span}")
+    if not d or d.get("source_sha256_16") != source_hash(os.path.join(CSRC, SPAN_KERNEL[span][1])):
         return None
     return d.get("bytes_per_launch")
 
@@ -96,42 +118,48 @@ def _counter_rows(csv_path, counter):
     return rows
 
 
-def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out=TRAFFIC_FILE):
-    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE per-dispatch counters (KiB) of the
-    two-segment attention launches (the dominant kernel of the dsv3 workload)
-    into HBM bytes per launch, each scaled by what
-    the same counter reads for the 1 GiB copy of --calibrate-copy."""
+def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload, span, out=TRAFFIC_FILE):
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE per-dispatch counters (KiB) of one
+    kernel of one workload into HBM bytes per launch, each scaled by what the
+    same counter reads for the 1 GiB copy of --calibrate-copy, and store the
+    record under "w<workload>:<span>" in the traffic file."""
     gib_kib = float(1 << 20)
     # the copy dispatches (the fill before them reads almost nothing)
     cal_f = [v for n, v in _counter_rows(cal_fetch_csv, "FETCH_SIZE") if v > gib_kib / 8]
     cal_w = [v for n, v in _counter_rows(cal_write_csv, "WRITE_SIZE") if v > gib_kib / 8]
     kf = gib_kib / (sum(cal_f) / len(cal_f))
     kw = gib_kib / (sum(cal_w) / len(cal_w))
-    # the two-segment pass (last chunk + new tokens; bf16 out, merged)
-    ctx = lambda n: "attn_kernel<4, false, false, 0, true, true>" in n
-    f = [v for n, v in _counter_rows(fetch_csv, "FETCH_SIZE") if ctx(n)]
-    w = [v for n, v in _counter_rows(write_csv, "WRITE_SIZE") if ctx(n)]
+    kname, src = SPAN_KERNEL[span]
+    f = [v for n, v in _counter_rows(fetch_csv, "FETCH_SIZE") if kname in n]
+    w = [v for n, v in _counter_rows(write_csv, "WRITE_SIZE") if kname in n]
     fetch_b = sum(f) / len(f) * 1024 * kf
     write_b = sum(w) / len(w) * 1024 * kw
-    d = {"kernel": "mla_prefill_attn_2seg (second context chunk + causal pass), 4 x (8192 ctx + 1024 new), "
-                   "H=128, chunk 4096",
-         "source_sha256_16": source_hash(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip")),
-         "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
-         "bytes_per_launch": round(fetch_b + write_b),
-         "copy_scale": {"fetch": round(kf, 4), "write": round(kw, 4)},
-         "launches": {"fetch": len(f), "write": len(w)},
-         "commands": [
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/w -o w -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/cf -o cf -- python3 bench.py --calibrate-copy",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/cw -o cw -- python3 bench.py --calibrate-copy",
-             "python3 bench.py --write-traffic <out>/f/f_counter_collection.csv <out>/w/w_counter_collection.csv "
-             "<out>/cf/cf_counter_collection.csv <out>/cw/cw_counter_collection.csv"],
-         "note": "per-dispatch counters in KiB, averaged over the two-segment attention launches; the 1 GiB "
-                 "copy reads FETCH_SIZE x 1/2 and WRITE_SIZE x 1, hence the scales"}
+    cmd = f"python3 bench.py --workload {workload} --no-sub --steps 2 --warmup 1 --no-cpu-baseline"
+    rec = {"kernel": kname, "span": span, "workload": workload,
+           "source_sha256_16": source_hash(os.path.join(CSRC, src)),
+           "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+           "bytes_per_launch": round(fetch_b + write_b),
+           "copy_scale": {"fetch": round(kf, 4), "write": round(kw, 4)},
+           "launches": {"fetch": len(f), "write": len(w)},
+           "commands": [
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f -- {cmd}",
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/w -o w -- {cmd}",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/cf -o cf -- python3 bench.py --calibrate-copy",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/cw -o cw -- python3 bench.py --calibrate-copy",
+               f"python3 bench.py --workload {workload} --traffic-span {span} --write-traffic "
+               "<out>/f/f_counter_collection.csv <out>/w/w_counter_collection.csv "
+               "<out>/cf/cf_counter_collection.csv <out>/cw/cw_counter_collection.csv"],
+           "note": "per-dispatch counters in KiB averaged over the kernel's launches; each counter is "
+                   "scaled so that the 1 GiB copy reads exactly its 1 GiB (copy_scale: the copy's FETCH_SIZE "
+                   "reads half its bytes, WRITE_SIZE all of them)"}
+    d = {}
+    if os.path.exists(out):
+        with open(out) as fh:
+            d = json.load(fh)
+    d[f"w{workload}:{span}"] = rec
     with open(out, "w") as fh:
-        json.dump(d, fh, indent=1)
-    print(json.dumps(d))
+        json.dump(d, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec))
 
 
 def timed_steps(torch, run, steps, flush=None):
@@ -222,67 +250,110 @@ def mfma_calibration(torch):
     return {"op": "independent v_mfma_f32_32x32x16_bf16 chains, 16 wavefronts per CU", "tflops": round(r.value, 1)}
 
 
-def cpu_baseline(prob, budget_s=15.0):
-    """The fp64 oracle as it stands, on request 0 of the same workload, one
-    head at a time, until about budget_s seconds of host work are spent."""
-    import numpy as np
-    from oracle import mla_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
-    C, E = int(prob.ctx_len[0]), int(prob.ext_len[0])
-    per_head = 2 * 512 * 256 * (C + E) + 640 * (C * E + E * (E + 1) // 2)
-    heads = 0
-    t0 = time.time()
-    while heads < prob.H and time.time() - t0 < budget_s:
-        orc.prefill_reference(prob, heads=[heads], rows={0: np.arange(E)})
-        heads += 1
-    dt = time.time() - t0
-    flops = per_head * heads
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"request 0 (C={C}, E={E}), heads 0..{heads - 1} of {prob.H}, all {E} new rows: "
-                      f"{flops / 1e9:.1f} GFLOP fp64 in {dt:.1f} s; NumPy/OpenBLAS with "
-                      f"{blas_threads} BLAS threads (exp single-threaded)"}
+# ---------------------------------------------------------------- the oracle on the host's cores
+#
+# The fp64 oracle as it stands, on a bounded sample of the workload: units of
+# (request, head) for the chunked workloads (all of a request's new rows over
+# all its keys, by the plain unchunked definition) and heads for the reuse
+# workload (the whole document for that head, every Global row or every
+# protected Local row), split over worker processes that each use one BLAS
+# thread (NumPy's exp is single-threaded). The workers are forked before this
+# process makes any HIP call, so they hold no GPU state, and start work only
+# after the GPU timing.
+
+_ORACLE_PROB = None
+_ORACLE_DOC = None
 
 
-def cpu_baseline_reuse(prob, budget_s=15.0):
-    """The fp64 oracle as it stands on the reuse workload: Global heads one
-    at a time (decompression of the whole document for that head, then all
-    query rows against it), until about budget_s seconds are spent."""
+def oracle_units(prob):
+    """[(unit, algorithmic flops)] of the whole workload in a seeded order."""
+    import numpy as np
+    if getattr(prob, "is_reuse", False):
+        Ld, T, P = int(prob.ctx_len[0]), prob.T, len(prob.prot_rows)
+        units = [(("G", h), 2 * 512 * 256 * Ld + 640 * Ld * T) for h in range(prob.n_local, prob.H)]
+        units += [(("L", h), 2 * 512 * 256 * Ld + 640 * Ld * P) for h in range(prob.n_local)]
+    else:
+        units = []
+        for r in range(prob.B):
+            C, E = int(prob.ctx_len[r]), int(prob.ext_len[r])
+            f = 2 * 512 * 256 * (C + E) + 640 * (C * E + E * (E + 1) // 2)
+            units += [((r, h), f) for h in range(prob.H)]
+    order = np.random.default_rng(12345).permutation(len(units))
+    return [units[i] for i in order]
+
+
+def _oracle_unit(unit):
     import numpy as np
     from oracle import mla_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                            if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
-    H, HL, T = prob.H, prob.n_local, prob.T
-    Ld = int(prob.ctx_len[0])
-    t_dec = time.time()
-    W = orc.bf16_to_f64(prob.W)
-    lat = orc.context_latent_f64(prob, 0, 0, Ld)
-    k_rope = orc.rope_rotate(lat[:, 512:], float(prob.delta), prob.rope_base)
-    q = orc.bf16_to_f64(prob.q)
+    global _ORACLE_DOC
+    prob = _ORACLE_PROB
+    if getattr(prob, "is_reuse", False):
+        if _ORACLE_DOC is None:
+            lat = orc.context_latent_f64(prob, 0, 0, int(prob.ctx_len[0]))
+            _ORACLE_DOC = (lat, orc.rope_rotate(lat[:, 512:], float(prob.delta), prob.rope_base),
+                           orc.bf16_to_f64(prob.W), orc.bf16_to_f64(prob.q))
+        lat, k_rope, W, q = _ORACLE_DOC
+        kind, h = unit
+        rows = np.arange(prob.T) if kind == "G" else np.asarray(prob.prot_rows)
+        kn, v = orc.decompress_head(lat[:, :512], W, prob.H, h)
+        orc.attend(q[rows, h], kn, k_rope, v, prob.scale)
+    else:
+        r, h = unit
+        orc.prefill_reference(prob, heads=[h], rows={r: np.arange(int(prob.ext_len[r]))})
+
+
+def _oracle_worker(job):
+    """Run units in order until the deadline; returns (flops, units, start, end)."""
+    units, deadline = job
+    from threadpoolctl import threadpool_limits
+    flops = n = 0
     t0 = time.time()
-    t_dec = t0 - t_dec
-    heads = 0
-    while HL + heads < H and (heads == 0 or time.time() - t0 < budget_s):
-        h = HL + heads
-        kn, v = orc.decompress_head(lat[:, :512], W, H, h)
-        orc.attend(q[:, h], kn, k_rope, v, prob.scale)
-        heads += 1
-    dt = time.time() - t0
-    flops = heads * (2 * 512 * 256 * Ld + 640 * Ld * T)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"Global heads {HL}..{HL + heads - 1}: decompression of the {Ld}-token document "
-                      f"and all {T} query rows, {flops / 1e9:.1f} GFLOP fp64 in {dt:.1f} s (plus {t_dec:.1f} s "
-                      f"decoding the document once, not counted); NumPy/OpenBLAS with {blas_threads} BLAS threads"}
+    with threadpool_limits(1):
+        for unit, f in units:
+            if time.time() >= deadline:
+                break
+            _oracle_unit(unit)
+            flops += f
+            n += 1
+    return flops, n, t0, time.time()
+
+
+class OraclePool:
+    """Worker processes for the oracle, forked now (before any HIP call)."""
+
+    def __init__(self, prob):
+        import multiprocessing as mp
+        global _ORACLE_PROB
+        _ORACLE_PROB = prob
+        self.prob = prob
+        self.affinity = len(os.sched_getaffinity(0))
+        # one GPU's share of a shared host is 16 cores at most
+        self.procs = max(1, min(self.affinity, 16))
+        self.pool = mp.get_context("fork").Pool(self.procs)
+
+    def run(self, budget_s=15.0):
+        units = oracle_units(self.prob)
+        deadline = time.time() + budget_s
+        jobs = [(units[i::self.procs], deadline) for i in range(self.procs)]
+        res = self.pool.map(_oracle_worker, jobs)
+        self.pool.close()
+        self.pool.join()
+        flops = sum(r[0] for r in res)
+        n = sum(r[1] for r in res)
+        dt = max(r[3] for r in res) - min(r[2] for r in res)
+        try:
+            import numpy as np
+            cfg = np.show_config(mode="dicts")
+            blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name", "unknown")
+        except Exception:  # pragma: no cover
+            blas = "unknown"
+        what = ("heads (the whole document for one head: every Global row or every protected Local row)"
+                if getattr(self.prob, "is_reuse", False) else
+                "(request, head) units (all of a request's new rows over all its keys for one head)")
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": self.procs, "kind": "oracle",
+                "sample": f"{n} of {len(units)} {what} of the same workload, in a seeded order, "
+                          f"{flops / 1e9:.1f} GFLOP fp64 in {dt:.1f} s; {self.procs} worker processes with one "
+                          f"{blas} BLAS thread each ({self.affinity} cores in this process's affinity set)"}
 
 
 def bench_append(args, torch, mla, mla_inputs):
@@ -367,7 +438,8 @@ def cpu_baseline_artifact(ap, budget_s=15.0):
     flops = heads * (2 * 512 * 256 * ap.L + 640 * pairs)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"Local heads 0..{heads - 1}: decompression of the {ap.L}-token document and 1024 "
+            "sample": f"Local heads 0..{heads - 1} (one process, {len(os.sched_getaffinity(0))} cores in its "
+                      f"affinity set): decompression of the {ap.L}-token document and 1024 "
                       f"document rows spread over it (causal prefixes), {flops / 1e9:.1f} GFLOP fp64 in "
                       f"{dt:.1f} s (plus {t_dec:.1f} s decoding once, not counted); NumPy/OpenBLAS with "
                       f"{blas_threads} BLAS threads"}
@@ -385,16 +457,16 @@ def bench_artifact(args, torch, mla, mla_inputs):
     print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.ARTIFACT_CONFIG_NAME}",
           file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        b.run()
-    torch.cuda.synchronize()
-    assert int(b.dev_status.item()) == 0
+        b.run(check=False)
+    b.check()
     from mla_long_context_amd.prefill import GraphStep
-    step = GraphStep(b).replay if args.graph else b.run
+    step = GraphStep(b).replay if args.graph else (lambda: b.run(check=False))
     ms, step_ms = timed_steps(torch, step, args.steps, cache_flusher(torch, args.flush_mb))
     timer = KernelTimer()
     for _ in range(args.steps):
-        b.run(timer=timer)
+        b.run(timer=timer, check=False)
     kern = timer.summary()
+    b.check()
     flops = work["dec_flops"] + work["attn_flops"]
     tflops = flops / (ms * 1e-3) / 1e12
     per_kind = {"decompress": work["dec_flops"], "attn_causal": work["causal_attn_flops"],
@@ -427,7 +499,6 @@ def bench_artifact(args, torch, mla, mla_inputs):
                         "kernel": kname, "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)},
            "kernels": kernels,
            "step_launch": "replay of one step captured into a HIP graph" if args.graph else "eager launches",
-        "cache_flush_mb": args.flush_mb,
            "cache_flush_mb": args.flush_mb,
            "kernel_timing": "a second pass of the same number of steps, launched eagerly with HIP events around every launch"}
     res.update(step_stats(step_ms))
@@ -436,13 +507,141 @@ def bench_artifact(args, torch, mla, mla_inputs):
     print(json.dumps(res))
 
 
+KERNEL_NAMES = {
+    "attn_ctx": "mla_prefill_attn (first context chunk)",
+    "attn_ctx_merge": "mla_prefill_attn_merge (context chunks after the first)",
+    "attn_ext": "mla_prefill_attn (causal pass)",
+    "attn_last": "mla_prefill_attn_2seg (last context chunk + causal pass)",
+    "decompress": "mla_decompress", "attn_global": "mla_prefill_attn (Global heads)",
+    "attn_local_absorbed": "mla_absorbed_attn (protected Local rows)",
+    "attn_local": "mla_prefill_attn (protected Local rows)",
+    "projection": "mla_head_partition_merge", "absorb": "mla_absorb_q / mla_absorb_out",
+}
+
+
+def run_workload(k, prob, args, torch, steps, warmup, graph=False):
+    """Time one standard workload: `steps` timed steps (mean, median, min),
+    then the same number again with events around every launch for the
+    per-kernel breakdown and the dominant kernel's roofline."""
+    from mla_long_context_amd.prefill import ChunkedPrefill, GraphStep, ReusePrefill
+    import mla_inputs
+    reuse = bool(getattr(prob, "is_reuse", False))
+    if reuse:
+        kw = {} if args.split is None else {"split": args.split}
+        pre = ReusePrefill(prob, chunk=args.chunk, local_path=args.local_path, **kw)
+    else:
+        pre = ChunkedPrefill(prob, chunk=args.chunk)
+    work = pre.work()
+
+    for _ in range(warmup):
+        pre.run(check=False)
+    pre.check()                      # raises if the gather saw a block id outside the pool
+    # Eager launches by default; --graph replays one step captured into a
+    # HIP graph instead (measured equal or slightly slower: the launches are
+    # asynchronous and keep the GPU's queue full).
+    step = GraphStep(pre).replay if graph else (lambda: pre.run(check=False))
+    for _ in range(warmup):
+        step()
+
+    # Timed steps for the value: events only between steps (events around
+    # every launch would add a fence between kernels); the value uses the
+    # mean over the K steps, the median and min per step are reported too.
+    ms, step_ms = timed_steps(torch, step, steps, cache_flusher(torch, args.flush_mb))
+    # The same number of steps again with events around every launch, on the
+    # stream the kernels run on: per-kernel durations for the breakdown and
+    # the roofline of the dominant kernel.
+    timer = KernelTimer()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        pre.run(timer=timer, check=False)
+    torch.cuda.synchronize()
+    kern = timer.summary()
+    pre.check()
+
+    flops = work["dec_flops"] + work["attn_flops"] + work.get("proj_flops", 0) + work.get("absorb_flops", 0)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # algorithmic work per step of each timed kernel: flops for the MFMA
+    # kernels, bytes for the HBM-bound ones
+    mfma_work = {"attn_ctx": work.get("ctx_attn_flops"), "attn_ctx_merge": work.get("ctx_merge_attn_flops"),
+                 "attn_ext": work.get("ext_attn_flops"), "attn_last": work.get("last_attn_flops"),
+                 "decompress": work["dec_flops"], "attn_global": work.get("global_attn_flops"),
+                 "attn_local": work.get("local_attn_flops"), "projection": work.get("proj_flops"),
+                 "absorb": work.get("absorb_flops")}
+    hbm_work = {"gather": work["gather_bytes"], "merge": work.get("merge_bytes"),
+                "relocate": work.get("relocate_bytes")}
+    per_step_launch = {name: c / steps for name, (c, _) in kern.items()}
+    kernels = {}
+    for name, (c, tot) in kern.items():
+        entry = {"launches_per_step": per_step_launch[name], "avg_ms": round(tot / c, 4),
+                 "ms_per_step": round(tot / steps, 4)}
+        step_s = tot / steps * 1e-3           # this kernel's time per step
+        if name in mfma_work:
+            entry["tflops"] = round(mfma_work[name] / step_s / 1e12, 2)
+            entry["mfma_frac"] = round(entry["tflops"] / PEAK_BF16_TFLOPS, 4)
+        else:
+            entry["gbs"] = round(hbm_work[name] / step_s / 1e9, 1)
+            entry["hbm_frac"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = entry
+
+    # the dominant kernel: the MFMA kernel with the most time per step; its
+    # algorithmic flops per launch (the mean over its launches of a step,
+    # which differ in a ragged batch) over its mean launch duration
+    dom = max((name for name in kern if name in mfma_work), key=lambda name: kern[name][1])
+    c_ms = kern[dom][1] / kern[dom][0]
+    c_unit = mfma_work[dom] / per_step_launch[dom]
+    achieved = c_unit / (c_ms * 1e-3) / 1e12
+    span = dom
+    if dom == "attn_local" and getattr(pre, "absorbed", False):
+        span = "attn_local"
+        kname = KERNEL_NAMES["attn_local_absorbed"]
+    else:
+        kname = KERNEL_NAMES[dom]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(k, span), "kernel": kname,
+                "rocprof_kernel": SPAN_KERNEL.get(span, (None,))[0],
+                "flop_per_launch": c_unit, "launches_per_step": per_step_launch[dom],
+                "avg_launch_ms": round(c_ms, 4),
+                "timing": "HIP events around each launch on the launch stream, second pass of the timed steps"}
+
+    if reuse:
+        cfg = {"workload": mla_inputs.CONFIG_NAMES[k], "heads": prob.H,
+               "local_heads": pre.HL, "global_heads": pre.HG, "local_path": pre.local_path,
+               "document_tokens": pre.Ldoc,
+               "query_rows": pre.T, "protected_rows": pre.P, "chunk": pre.S, "split": pre.split,
+               "cache": "bf16"}
+    else:
+        cfg = {"workload": mla_inputs.CONFIG_NAMES[k], "heads": prob.H,
+               "requests": prob.B, "ctx_tokens_per_request": int(prob.ctx_len.max()),
+               "ctx_tokens_total": work["ctx_tokens"],
+               "new_tokens_total": work["new_tokens"], "chunk": pre.S,
+               "cache": prob.cache_dtype}
+    rec = {
+        "value": round(tflops, 2), "unit": "TFLOP/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "config": cfg,
+        "prefill_tokens_per_s": round(work["new_tokens"] / (ms * 1e-3), 1),
+        "context_tokens_per_s": round(work["ctx_tokens"] / (ms * 1e-3), 1),
+        "algorithmic_flop_per_step": flops,
+        "mfma_roofline_frac_whole_step": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    rec.update(step_stats(step_ms))
+    del pre
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="standard workload number; 2 (the default) is the headline line")
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help=f"time one standard workload alone (default: workload {HEADLINE}, the headline, "
+                         f"with sub-records for workloads {', '.join(map(str, SUB_WORKLOADS))})")
+    ap.add_argument("--no-sub", action="store_true", help="headline only, no sub-records")
+    ap.add_argument("--sub-steps", type=int, default=10, help="timed steps per sub-record workload")
     ap.add_argument("--chunk", type=int, default=None, help="context chunk override (tokens)")
     ap.add_argument("--split", type=int, default=None,
                     help="reuse workload: keys per attention piece (default: the driver's)")
@@ -457,6 +656,7 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work on the host")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="device buffer (MB) overwritten before every timed step, outside its events, "
                          "so the Infinity Cache holds nothing of the previous step (0: off)")
@@ -464,22 +664,21 @@ def main():
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="FETCH_SIZE and WRITE_SIZE counter CSVs of a bench run, then of a "
-                         "--calibrate-copy run: write the HBM-traffic record and exit")
+                         "--calibrate-copy run: store the HBM-traffic record of --traffic-span for "
+                         "--workload and exit")
+    ap.add_argument("--traffic-span", default=None, choices=sorted(SPAN_KERNEL))
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, args.workload or HEADLINE, args.traffic_span)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only; the prefill path has no multi-GPU mode. "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: this build runs on one GPU and has no multi-GPU mode "
+              "(how the path would shard is described in the design notes). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-
     if args.calibrate_copy:
+        import torch
         n = 1 << 29   # 512 Mi bf16 elements = 1 GiB
         a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
         b = torch.empty_like(a)
@@ -490,131 +689,62 @@ def main():
         return
 
     import mla_inputs
-    import mla_long_context_amd as mla
-    from mla_long_context_amd.prefill import ChunkedPrefill, GraphStep, ReusePrefill
-
-    if args.append:
-        bench_append(args, torch, mla, mla_inputs)
-        return
-    if args.artifact:
+    if args.append or args.artifact:
+        import torch
+        import mla_long_context_amd as mla
         mla.load()
-        bench_artifact(args, torch, mla, mla_inputs)
+        (bench_append if args.append else bench_artifact)(args, torch, mla, mla_inputs)
         return
 
-    mla.load()                       # fails loudly if libmla.so is missing
+    k = args.workload or HEADLINE
+    subs = [] if (args.workload is not None or args.no_sub) else [j for j in SUB_WORKLOADS if j != k]
+    # The headline's inputs, and the oracle's worker processes forked from a
+    # process that has not touched the GPU yet.
     t_gen = time.time()
-    prob = mla_inputs.make_config(args.workload)
-    reuse = bool(getattr(prob, "is_reuse", False))
-    if reuse:
-        kw = {} if args.split is None else {"split": args.split}
-        pre = ReusePrefill(prob, chunk=args.chunk, local_path=args.local_path, **kw)
-    else:
-        pre = ChunkedPrefill(prob, chunk=args.chunk)
-    work = pre.work()
-    print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.CONFIG_NAMES[args.workload]}",
+    prob = mla_inputs.make_config(k)
+    print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.CONFIG_NAMES[k]}",
           file=sys.stderr, flush=True)
+    oracle_pool = None if args.no_cpu_baseline else OraclePool(prob)
 
-    for _ in range(args.warmup):
-        pre.run()
-    torch.cuda.synchronize()
-    assert int(pre.dev_status.item()) == 0, "gather reported an out-of-range block"
-    # Eager launches by default; --graph replays one step captured into a
-    # HIP graph instead (measured equal or slightly slower: the launches are
-    # asynchronous and keep the GPU's queue full).
-    step = GraphStep(pre).replay if args.graph else pre.run
-    for _ in range(args.warmup):
-        step()
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import mla_long_context_amd as mla
+    mla.load()                       # fails loudly if libmla.so is missing
 
-    # Timed steps for the headline value: events only between steps (events
-    # around every launch would add a fence between kernels); the value uses
-    # the mean over the K steps, the median and min per step are reported too.
-    ms, step_ms = timed_steps(torch, step, args.steps, cache_flusher(torch, args.flush_mb))
-    # The same number of steps again with events around every launch, on the
-    # stream the kernels run on: per-kernel durations for the breakdown and
-    # the roofline of the dominant kernel.
-    timer = KernelTimer()
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        pre.run(timer=timer)
-    torch.cuda.synchronize()
-    kern = timer.summary()
-
-    flops = work["dec_flops"] + work["attn_flops"] + work.get("proj_flops", 0) + work.get("absorb_flops", 0)
-    tflops = flops / (ms * 1e-3) / 1e12
-    # algorithmic work per step of each timed kernel: flops for the MFMA
-    # kernels, bytes for the HBM-bound ones
-    mfma_work = {"attn_ctx": work.get("ctx_attn_flops"), "attn_ext": work.get("ext_attn_flops"),
-                 "attn_last": work.get("last_attn_flops"),
-                 "decompress": work["dec_flops"], "attn_global": work.get("global_attn_flops"),
-                 "attn_local": work.get("local_attn_flops"), "projection": work.get("proj_flops"),
-                 "absorb": work.get("absorb_flops")}
-    hbm_work = {"gather": work["gather_bytes"], "merge": work.get("merge_bytes"),
-                "relocate": work.get("relocate_bytes")}
-    per_step_launch = {k: c / args.steps for k, (c, _) in kern.items()}
-    kernels = {}
-    for name, (c, tot) in kern.items():
-        avg = tot / c
-        entry = {"launches_per_step": per_step_launch[name], "avg_ms": round(avg, 4),
-                 "ms_per_step": round(tot / args.steps, 4)}
-        step_s = tot / args.steps * 1e-3           # this kernel's time per step
-        if name in mfma_work:
-            entry["tflops"] = round(mfma_work[name] / step_s / 1e12, 2)
-        else:
-            entry["gbs"] = round(hbm_work[name] / step_s / 1e9, 1)
-        kernels[name] = entry
-
-    # the dominant kernel: the MFMA kernel with the most time per step
-    dom = max((k for k in kern if k in mfma_work), key=lambda k: kern[k][1])
-    c_ms = kern[dom][1] / kern[dom][0]
-    c_unit = mfma_work[dom] / per_step_launch[dom]
-    achieved = c_unit / (c_ms * 1e-3) / 1e12
-    traffic = None
-    if dom == "attn_last" and args.workload == 2:   # the workload the counter record was taken on
-        traffic = traffic_for(os.path.join(ROOT, "mla_long_context_amd", "csrc", "attn.hip"))
-    kname = {"attn_ctx": "mla_prefill_attn (context pass)", "attn_ext": "mla_prefill_attn (causal pass)",
-             "attn_last": "mla_prefill_attn_2seg (last context chunk + causal pass)",
-             "decompress": "mla_decompress", "attn_global": "mla_prefill_attn (Global heads)",
-             "attn_local": ("mla_absorbed_attn (protected Local rows)" if getattr(pre, "absorbed", False)
-                            else "mla_prefill_attn (protected Local rows)"),
-             "projection": "mla_head_partition_merge",
-             "absorb": "mla_absorb_q / mla_absorb_out"}[dom]
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": kname,
-                "flop_per_launch": c_unit, "avg_launch_ms": round(c_ms, 4)}
-
-    if reuse:
-        cfg = {"workload": mla_inputs.CONFIG_NAMES[args.workload], "heads": prob.H,
-               "local_heads": pre.HL, "global_heads": pre.HG, "local_path": pre.local_path,
-               "document_tokens": pre.Ldoc,
-               "query_rows": pre.T, "protected_rows": pre.P, "chunk": pre.S, "split": pre.split,
-               "cache": "bf16"}
-    else:
-        cfg = {"workload": mla_inputs.CONFIG_NAMES[args.workload], "heads": prob.H,
-               "requests": prob.B, "ctx_tokens_per_request": int(prob.ctx_len.max()),
-               "new_tokens_total": work["new_tokens"], "chunk": pre.S,
-               "cache": prob.cache_dtype}
-    res = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": cfg,
-        "prefill_tokens_per_s": round(work["new_tokens"] / (ms * 1e-3), 1),
-        "context_tokens_per_s": round(work["ctx_tokens"] / (ms * 1e-3), 1),
-        "algorithmic_flop_per_step": flops,
-        "mfma_roofline_frac_whole_step": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline,
-        "kernels": kernels,
-        "step_launch": "replay of one step captured into a HIP graph" if args.graph else "eager launches",
-        "cache_flush_mb": args.flush_mb,
-        "kernel_timing": "a second pass of the same number of steps, launched eagerly with HIP events around every launch",
-    }
-    res.update(step_stats(step_ms))
+    rec = run_workload(k, prob, args, torch, args.steps, args.warmup, args.graph)
+    print(f"# workload {k}: {rec['ms_per_step']} ms/step, {rec['value']} TFLOP/s", file=sys.stderr, flush=True)
+    res = {"metric": METRIC, "value": rec["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": rec["config"]}
+    for key in ("prefill_tokens_per_s", "context_tokens_per_s", "algorithmic_flop_per_step",
+                "mfma_roofline_frac_whole_step", "roofline", "kernels", "median_ms_per_step", "min_ms_per_step"):
+        res[key] = rec[key]
+    res["dtype_note"] = ("MFMA products in bf16 with fp32 accumulation; the fp8 cache is dequantised exactly "
+                         "(fp8 codes times fp32 scales, rounded once to bf16) before the products"
+                         if prob.cache_dtype == "fp8" else "MFMA products in bf16 with fp32 accumulation")
+    res["step_launch"] = "replay of one step captured into a HIP graph" if args.graph else "eager launches"
+    res["cache_flush_mb"] = args.flush_mb
+    res["kernel_timing"] = ("a second pass of the same number of steps, launched eagerly with HIP events "
+                            "around every launch")
+    del prob
+    if subs:
+        res["workloads"] = {}
+        for j in subs:
+            t_gen = time.time()
+            pj = mla_inputs.make_config(j)
+            print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.CONFIG_NAMES[j]}",
+                  file=sys.stderr, flush=True)
+            r = run_workload(j, pj, args, torch, args.sub_steps, args.warmup, args.graph)
+            print(f"# workload {j}: {r['ms_per_step']} ms/step, {r['value']} TFLOP/s", file=sys.stderr, flush=True)
+            res["workloads"][str(j)] = r
+            del pj
     res["gemm_reference"] = gemm_reference(torch)
     res["mfma_sustained"] = mfma_calibration(torch)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_reuse(prob) if reuse else cpu_baseline(prob)
+    if oracle_pool is not None:
+        res["cpu_baseline"] = oracle_pool.run(args.cpu_budget)
     print(json.dumps(res))
 
 

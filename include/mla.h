@@ -366,7 +366,10 @@ int mla_rope_relocate_q(const void* q_in, void* q_out, int64_t q_row_stride, int
  *   z = O_L . W_aL + O_G . W_aG      (bf16 [T][d_mid], fp32 accumulate)
  *   y = z . W_b                      (bf16 [T][d_model])
  *   art_out   device bf16 [T][HL][128];  rec_out bf16 [P][HL][128];
- *   prot_rows device int32 [P], strictly increasing, each < T;
+ *   prot_rows device int32 [P], strictly increasing, each in [0, T) (not
+ *             checked: the device cannot be read here; out of order, a
+ *             protected row may take its artifact row instead, and no access
+ *             leaves the given arrays either way);
  *   glob_out  device bf16 [T][HG][128];
  *   wa_t      device bf16 [d_mid][(HL+HG)*128]: [W_aL ; W_aG] stacked along
  *             K (Local rows first) and packed by mla_pack_weight_t;

@@ -51,14 +51,46 @@ BF16_NAN = np.uint16(0x7FC0)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bf16 (nearest even) and return the bit patterns."""
+    """Round fp32 values to bf16 (nearest even) and return the bit patterns.
+
+    Large arrays are converted in cache-sized pieces on several threads (the
+    result does not depend on the split)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
-    return r.astype(np.uint16)
+    u = x.view(np.uint32).reshape(-1)
+    out = np.empty(u.shape, dtype=np.uint16)
+    piece = 1 << 20
+
+    def conv(s):
+        t = u[s:s + piece]
+        r = t >> np.uint32(16)
+        r &= np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += t
+        r >>= np.uint32(16)
+        out[s:s + piece] = r
+
+    starts = range(0, u.size, piece)
+    if u.size > 4 * piece:
+        import concurrent.futures as cf
+        import os
+        with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+            list(ex.map(conv, starts))
+    else:
+        for s in starts:
+            conv(s)
+    return out.reshape(x.shape)
+
+
+_BIG = 1 << 24      # arrays above this many elements are drawn in parallel blocks
 
 
 def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) draws rounded to bf16. Arrays of more than 2^24 elements
+    take one 64-bit seed from rng and are drawn in parallel blocks from it
+    (_normal_bf16_blocks), so that the largest workloads' inputs are ready
+    in seconds; smaller ones are drawn from rng directly."""
+    if int(np.prod(shape)) > _BIG:
+        return _normal_bf16_blocks(int(rng.integers(0, 2 ** 63, dtype=np.int64)), shape, std)
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
         x *= np.float32(std)
@@ -97,19 +129,48 @@ def quantize_rows_e4m3(x_bf16_bits: np.ndarray):
     scale = fp32(max|x|) / 448 (fp32 division), code = e4m3(clamp(x / scale)),
     rounding by torch's float8_e4m3fn cast (round to nearest even). An
     all-zero row gets scale 0 and zero codes. This produces the fp8 cache
-    input; dequantisation is not done here.
+    input; dequantisation is not done here. (torch's CPU ops, which divide
+    with IEEE fp32 rounding, do the elementwise work on several threads.)
     """
     import torch
 
-    x = _bf16_bits_to_f32(x_bf16_bits)
-    amax = np.max(np.abs(x), axis=-1).astype(np.float32)
-    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    y = (x / safe[..., None]).astype(np.float32)
-    y = np.clip(y, -FP8_MAX, FP8_MAX)
+    xb = torch.from_numpy(np.ascontiguousarray(x_bf16_bits).view(np.int16)).view(torch.bfloat16)
+    x = xb.to(torch.float32)
+    amax = x.abs().amax(dim=-1)
+    scale = amax / torch.tensor(FP8_MAX, dtype=torch.float32)
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    y = (x / safe.unsqueeze(-1)).clamp_(-FP8_MAX, FP8_MAX)
     y[scale == 0] = 0.0
-    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    return codes, scale
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale.numpy()
+
+
+def selection_kv_b_proj(rng: np.random.Generator, H: int) -> np.ndarray:
+    """A kv_b_proj [512, H*256] (bf16 bits) whose every column picks one
+    latent dimension with weight +-1/4 or +-1/8: the 128 key columns of a
+    head pick distinct dimensions, and so do its 128 value columns. Every
+    k_nope and v entry it produces is then a latent entry times a power of
+    two, so it is exactly representable in bf16 whatever the arithmetic
+    order, and the absorbed query W_UK q_nope has at most one term per latent
+    dimension. Edge-case problems use it so that rounding of decompressed
+    keys cannot mask a wrong key set (a dropped or duplicated key moves the
+    lse of an n-key row by about 1/n). The small weights keep values and
+    outputs of a softmax over a few keys near the size they have over many
+    (a fraction of one), where the absolute output bar is a few bf16 ulps."""
+    W = np.zeros((D_C, H * (D_NOPE + D_V)), dtype=np.float32)
+    vals = np.array([-0.25, -0.125, 0.125, 0.25], dtype=np.float32)
+    for blk in range(2 * H):      # blocks 0..H-1: W_UK of head blk; H..2H-1: W_UV of head blk-H
+        rows = rng.choice(D_C, size=D_NOPE, replace=False)
+        W[rows, blk * D_NOPE + np.arange(D_NOPE)] = vals[rng.integers(0, 4, size=D_NOPE)]
+    return f32_to_bf16_bits(W)
+
+
+def _kv_b_proj(rng, H, weights="normal", w_std=None):
+    if weights == "selection":
+        return selection_kv_b_proj(rng, H)
+    if weights != "normal":
+        raise ValueError(weights)
+    return _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=(w_std if w_std else 1.0 / np.sqrt(D_C)))
 
 
 @dataclasses.dataclass
@@ -170,8 +231,13 @@ class Problem:
         return self.delta is not None
 
 
-def _build_pool(rng, ctx_len, cache_dtype, extra_blocks=0, poison=False):
-    """Draw context latents in logical order and scatter them into a shuffled pool."""
+def _build_pool(rng, ctx_len, cache_dtype, extra_blocks=0, poison=False, exact_dequant=False):
+    """Draw context latents in logical order and scatter them into a shuffled pool.
+
+    exact_dequant (fp8 only): every record's c_kv gets its largest magnitude
+    at exactly 7 = 448 / 64 (values clipped to [-6.5, 6.5], one seeded
+    position per record set to +-7), so its scale is 2^-6 and every
+    dequantised value (code times 2^-6) is exactly representable in bf16."""
     B = len(ctx_len)
     nblk = [(int(c) + BLOCK - 1) // BLOCK for c in ctx_len]
     used = int(sum(nblk))
@@ -184,6 +250,15 @@ def _build_pool(rng, ctx_len, cache_dtype, extra_blocks=0, poison=False):
         bt[r, :nblk[r]] = perm[off:off + nblk[r]]
         off += nblk[r]
     lat = _normal_bf16(rng, (used * BLOCK, D_LAT))          # logical order, whole blocks
+    if exact_dequant:
+        if cache_dtype != "fp8":
+            raise ValueError("exact_dequant applies to the fp8 cache")
+        x = np.clip(_bf16_bits_to_f32(lat[:, :D_C]), -6.5, 6.5)
+        pos = rng.integers(0, D_C, size=x.shape[0])
+        sgn = np.where(rng.integers(0, 2, size=x.shape[0]) == 1, 7.0, -7.0).astype(np.float32)
+        x[np.arange(x.shape[0]), pos] = sgn
+        lat = lat.copy()
+        lat[:, :D_C] = f32_to_bf16_bits(x)
     if cache_dtype == "bf16":
         pool = np.empty((NB, BLOCK, D_LAT), dtype=np.uint16)
         if extra_blocks:
@@ -207,49 +282,65 @@ def _build_pool(rng, ctx_len, cache_dtype, extra_blocks=0, poison=False):
 
 def make_problem(H, ctx_len, ext_len, chunk, cache_dtype="bf16", seed=0,
                  extra_blocks=0, poison=False, name="custom", w_std=None,
-                 scale=None) -> Problem:
+                 scale=None, weights="normal", exact_dequant=False) -> Problem:
     """A prefill problem with the given per-request lengths.
 
     Lengths are taken as given (the caller draws them first when they are
-    random). Latents and q are N(0,1), kv_b_proj is N(0, 1/512).
+    random). Latents and q are N(0,1), kv_b_proj is N(0, 1/512)
+    (weights="normal") or a selection matrix (weights="selection",
+    selection_kv_b_proj); exact_dequant as in _build_pool.
     """
     rng = np.random.default_rng(seed)
     ctx_len = np.asarray(ctx_len, dtype=np.int64)
     ext_len = np.asarray(ext_len, dtype=np.int64)
     return _finish(rng, name, H, ctx_len, ext_len, chunk, cache_dtype, seed,
-                   extra_blocks, poison, w_std, scale)
+                   extra_blocks, poison, w_std, scale, weights, exact_dequant)
 
 
 def _finish(rng, name, H, ctx_len, ext_len, chunk, cache_dtype, seed,
-            extra_blocks=0, poison=False, w_std=None, scale=None):
-    pool, bt = _build_pool(rng, ctx_len, cache_dtype, extra_blocks, poison)
+            extra_blocks=0, poison=False, w_std=None, scale=None, weights="normal",
+            exact_dequant=False):
+    pool, bt = _build_pool(rng, ctx_len, cache_dtype, extra_blocks, poison, exact_dequant)
     T = int(ext_len.sum())
     ext = _normal_bf16(rng, (T, D_LAT))
     q = _normal_bf16(rng, (T, H, D_QK))
-    W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=(w_std if w_std else 1.0 / np.sqrt(D_C)))
+    W = _kv_b_proj(rng, H, weights, w_std)
     return Problem(name=name, H=H, ctx_len=ctx_len, ext_len=ext_len, chunk=int(chunk),
                    cache_dtype=cache_dtype, pool=pool, block_table=bt, ext_latent=ext,
                    q=q, W=W, scale=float(scale if scale else 1.0 / np.sqrt(D_QK)), seed=seed)
 
 
+def _synthetic_artifact(rng, T, HL, L):
+    """Seeded Local-head artifact rows for a document of L keys: out ~
+    N(0, e/L), lse = ln L + 0.5 + 0.1 N(0,1); for L = 0 the draws are made
+    (so later draws do not move) and replaced by the empty state (0, -inf)."""
+    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / max(L, 1))))
+    art_lse = (np.log(max(L, 1)) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
+    if L == 0:
+        art_out[:] = 0
+        art_lse[:] = -np.inf
+    return art_out, art_lse
+
+
 def make_reuse_problem(H=64, n_local=56, L=262144, T=512, delta=4096, P=64,
                        d_mid=2048, d_model=4096, chunk=8192, seed=5,
-                       name="reuse") -> Problem:
+                       name="reuse", weights="normal") -> Problem:
     """Head-partitioned reuse: one document at canonical positions 0..L-1,
     T query rows at request positions delta+L+i, Local heads [0, n_local)
     served from a seeded artifact with P protected rows recomputed.
 
     The artifact is synthetic: out ~ N(0, e/L) (the spread a softmax over L
-    N(0,1)-scored keys gives), lse = ln L + 0.5 + 0.1 N(0,1).
+    N(0,1)-scored keys gives), lse = ln L + 0.5 + 0.1 N(0,1). An empty
+    document's artifact is the empty state, out = 0 and lse = -inf (what the
+    offline build writes for it).
     """
     rng = np.random.default_rng(seed)
     ctx_len = np.array([L], dtype=np.int64)
     pool, bt = _build_pool(rng, ctx_len, "bf16")
     q = _normal_bf16(rng, (T, H, D_QK))
-    W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
+    W = _kv_b_proj(rng, H, weights)
     HL, HG = n_local, H - n_local
-    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / max(L, 1))))
-    art_lse = (np.log(max(L, 1)) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
+    art_out, art_lse = _synthetic_artifact(rng, T, HL, L)
     prot = np.sort(rng.choice(T, size=P, replace=False)).astype(np.int32)
     WaL = _normal_bf16(rng, (HL * D_V, d_mid), std=1.0 / np.sqrt(HL * D_V))
     WaG = _normal_bf16(rng, (HG * D_V, d_mid), std=1.0 / np.sqrt(HG * D_V))
@@ -263,7 +354,8 @@ def make_reuse_problem(H=64, n_local=56, L=262144, T=512, delta=4096, P=64,
 
 
 def make_multidoc_problem(H=8, n_local=7, doc_lens=(512, 192, 1088), T=100, delta=4096, P=7,
-                          d_mid=256, d_model=256, chunk=256, seed=6, name="multidoc") -> Problem:
+                          d_mid=256, d_model=256, chunk=256, seed=6, name="multidoc",
+                          weights="normal") -> Problem:
     """Segmented reuse: documents d = 0..n-1, each built at canonical
     positions 0..L_d-1 in a pool of its own, placed one after another in the
     request (document d at offset delta_d = delta + L_0 + ... + L_{d-1});
@@ -279,10 +371,9 @@ def make_multidoc_problem(H=8, n_local=7, doc_lens=(512, 192, 1088), T=100, delt
         off += int(L)
     Ltot = int(sum(doc_lens))
     q = _normal_bf16(rng, (T, H, D_QK))
-    W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
+    W = _kv_b_proj(rng, H, weights)
     HL, HG = n_local, H - n_local
-    art_out = _normal_bf16(rng, (T, HL, D_V), std=float(np.sqrt(np.e / max(Ltot, 1))))
-    art_lse = (np.log(max(Ltot, 1)) + 0.5 + 0.1 * rng.standard_normal((T, HL))).astype(np.float32)
+    art_out, art_lse = _synthetic_artifact(rng, T, HL, Ltot)
     prot = np.sort(rng.choice(T, size=P, replace=False)).astype(np.int32)
     WaL = _normal_bf16(rng, (HL * D_V, d_mid), std=1.0 / np.sqrt(HL * D_V))
     WaG = _normal_bf16(rng, (HG * D_V, d_mid), std=1.0 / np.sqrt(HG * D_V))
@@ -329,7 +420,7 @@ class ArtifactProblem:
 
 
 def make_artifact_problem(H=8, n_local=7, L=1088, extra_rows=50, doc_rows=True, chunk=256, seed=7,
-                          generation=3, vocab=129280, name="artifact") -> ArtifactProblem:
+                          generation=3, vocab=129280, name="artifact", weights="normal") -> ArtifactProblem:
     """A document to build an artifact for: L tokens in a shuffled pool,
     R = (L if doc_rows else 0) + extra_rows query rows (N(0,1), rope part at
     the rows' canonical positions; drawn from SeedSequence([seed, 1]) in
@@ -339,7 +430,7 @@ def make_artifact_problem(H=8, n_local=7, L=1088, extra_rows=50, doc_rows=True, 
     R = (L if doc_rows else 0) + int(extra_rows)
     # the query rows of a long document are large: drawn in parallel blocks
     q = _normal_bf16_blocks([seed, 1], (R, H, D_QK))
-    W = _normal_bf16(rng, (D_C, H * (D_NOPE + D_V)), std=1.0 / np.sqrt(D_C))
+    W = _kv_b_proj(rng, H, weights)
     tokens = rng.integers(0, vocab, size=L).astype(np.int32)
     return ArtifactProblem(name=name, H=H, n_local=n_local, L=int(L), doc_rows=bool(doc_rows), pool=pool,
                            block_table=bt, q=q, W=W, scale=float(1.0 / np.sqrt(D_QK)), tokens=tokens,

@@ -59,6 +59,20 @@ class MlaError(RuntimeError):
         self.code = code
 
 
+DEVICE_STATUS_TEXT = {
+    MLA_ERR_OUT_OF_RANGE: "a block id outside the pool (or a position outside the block table) reached "
+                          "the device; the records it named were not read (zeros were written in their place)",
+}
+
+
+def raise_on_device_status(code: int, what: str) -> None:
+    """Raise MlaError for a device status word read back after a step
+    (MLA_OK = 0 passes)."""
+    code = int(code)
+    if code != MLA_OK:
+        raise MlaError(what, code, DEVICE_STATUS_TEXT.get(code, "device-side error"))
+
+
 _lib = None
 
 P = ctypes.c_void_p

@@ -245,7 +245,10 @@ __global__ __launch_bounds__(kAW * 64, 1) void absorbed_attn_kernel(AbsAttnArgs 
     return vb[hi][d & 3] + 16384 * mm + 256 * (d >> 2);
   };
 
-  for (int t = 0; t < kANB - 1; ++t) dma(min(t, max(ntiles - 1, 0)), t);
+  // An empty piece issues no DMA at all: with no key there is no address to
+  // clamp to, and the epilogue writes the identity state (0, -inf).
+  if (ntiles > 0)
+    for (int t = 0; t < kANB - 1; ++t) dma(min(t, ntiles - 1), t);
   wait_vmcnt<0>();
   for (int t = 0; t < ntiles; ++t) {
     // own DMA of tile t done (tiles t+1, t+2 may be in flight); then the
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kAW * 64, 1) void absorbed_attn_kernel(AbsAttnArgs 
 extern "C" int mla_absorb_q(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
                             const int32_t* row_ids, int n_rows, const void* kv_b_proj, int H_total,
                             void* q_abs, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(n_rows >= 0, MLA_ERR_INVALID_ARG, "mla_absorb_q: n_rows must be >= 0");
   MLA_REQUIRE(H_q > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_q && h_end <= H_total, MLA_ERR_INVALID_ARG,
               "mla_absorb_q: need 0 <= h_begin (%d) < h_end (%d) <= min(H_q (%d), H_total (%d))", h_begin, h_end,
@@ -408,7 +411,7 @@ extern "C" int mla_absorb_q(const void* q, int64_t q_row_stride, int H_q, int h_
 extern "C" int mla_absorbed_attn(const void* q_abs, int R, const void* latent, int64_t ld_latent,
                                  const int32_t* cu_k, int pieces, float scale, void* out_lat, int out_dtype,
                                  float* lse4, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(R >= 0 && pieces >= 0, MLA_ERR_INVALID_ARG, "mla_absorbed_attn: R and pieces must be >= 0");
   if (R == 0 || pieces == 0) return MLA_OK;
   MLA_REQUIRE(q_abs && latent && cu_k && out_lat && lse4, MLA_ERR_INVALID_ARG,
@@ -435,7 +438,7 @@ extern "C" int mla_absorbed_attn(const void* q_abs, int R, const void* latent, i
 
 extern "C" int mla_absorb_out(const void* o_lat, int n_rows, const void* w_t, int H_total, int h_begin, int h_end,
                               void* out, int64_t out_row_stride, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(n_rows >= 0, MLA_ERR_INVALID_ARG, "mla_absorb_out: n_rows must be >= 0");
   MLA_REQUIRE(H_total > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_total, MLA_ERR_INVALID_ARG,
               "mla_absorb_out: need 0 <= h_begin (%d) < h_end (%d) <= H_total (%d)", h_begin, h_end, H_total);

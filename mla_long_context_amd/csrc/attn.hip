@@ -536,7 +536,7 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
                  int out_dtype, int64_t out_row_stride, float* lse, int64_t lse_row_stride,
                  const float* prev, int64_t prev_row_stride, const float* prev_lse, int64_t prev_lse_row_stride,
                  bool merge, void* stream, const Seg2* seg2 = nullptr) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(batch >= 0 && max_q >= 0, MLA_ERR_INVALID_ARG, "%s: batch and max_q must be >= 0", fn);
   MLA_REQUIRE(H_q > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_q, MLA_ERR_INVALID_ARG,
               "%s: need 0 <= h_begin (%d) < h_end (%d) <= H_q (%d)", fn, h_begin, h_end, H_q);

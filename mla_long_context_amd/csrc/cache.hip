@@ -126,7 +126,7 @@ extern "C" int mla_cache_append(void* pool, int cache_dtype, int num_blocks, con
                                 int64_t bt_stride, const int32_t* pos0, const int32_t* cu_new, int batch,
                                 int max_new, const void* latent_new, int64_t ld_latent, int32_t* dev_status,
                                 void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(batch >= 0 && max_new >= 0 && num_blocks >= 0, MLA_ERR_INVALID_ARG,
               "mla_cache_append: batch, max_new and num_blocks must be >= 0");
   if (batch == 0 || max_new == 0) return MLA_OK;

@@ -80,7 +80,7 @@ extern "C" int mla_gather_context(const void* pool, int cache_dtype, int num_blo
                                   const int32_t* chunk_start, const int32_t* chunk_len,
                                   const int32_t* cu_out, int batch, int max_len,
                                   void* out_latent, int32_t* dev_status, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(batch >= 0 && max_len >= 0, MLA_ERR_INVALID_ARG,
               "mla_gather_context: batch (%d) and max_len (%d) must be >= 0", batch, max_len);
   if (batch == 0 || max_len == 0) return MLA_OK;

@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 }  // namespace
 
 extern "C" int mla_pack_weight_t(const void* w, int K, int N, void* out, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(w && out, MLA_ERR_INVALID_ARG, "mla_pack_weight_t: null pointer argument");
   MLA_REQUIRE(K > 0 && N > 0 && K % 8 == 0 && N % 8 == 0, MLA_ERR_INVALID_ARG,
               "mla_pack_weight_t: K (%d) and N (%d) must be positive multiples of 8", K, N);
@@ -540,7 +540,7 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
                               const void* w_t, int H_total, int h_begin, int h_end,
                               void* k_nope, int64_t k_head_stride,
                               void* v, int64_t v_head_stride, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(n_tokens >= 0, MLA_ERR_INVALID_ARG, "mla_decompress: n_tokens must be >= 0");
   MLA_REQUIRE(H_total > 0 && 0 <= h_begin && h_begin < h_end && h_end <= H_total, MLA_ERR_INVALID_ARG,
               "mla_decompress: need 0 <= h_begin (%d) < h_end (%d) <= H_total (%d)", h_begin, h_end, H_total);
@@ -585,7 +585,7 @@ extern "C" int mla_head_partition_merge(const void* art_out, const void* rec_out
                                         const int32_t* prot_rows, int P, const void* glob_out,
                                         const void* wa_t, const void* wb_t, int T, int HL, int HG,
                                         int d_mid, int d_model, void* z, void* y, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(T >= 0 && P >= 0 && P <= T && HL >= 0 && HG >= 0 && HL + HG > 0, MLA_ERR_INVALID_ARG,
               "mla_head_partition_merge: need T >= 0, 0 <= P <= T, HL, HG >= 0, HL + HG > 0");
   if (T == 0) return MLA_OK;

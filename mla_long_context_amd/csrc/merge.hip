@@ -202,7 +202,7 @@ extern "C" int mla_merge_states(const void* out_a, int dtype_a, const float* lse
                                 const void* out_b, int dtype_b, const float* lse_b,
                                 int64_t rows, void* out, int dtype_out, float* lse_out,
                                 void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(rows >= 0, MLA_ERR_INVALID_ARG, "mla_merge_states: rows (%lld) must be >= 0", (long long)rows);
   if (rows == 0) return MLA_OK;
   MLA_REQUIRE(out_a && lse_a && out_b && lse_b && out && lse_out, MLA_ERR_INVALID_ARG,
@@ -222,7 +222,7 @@ extern "C" int mla_merge_states(const void* out_a, int dtype_a, const float* lse
 
 extern "C" int mla_merge_states_n(const void* outs, int dtype_in, const float* lses, int pieces, int64_t rows,
                                   void* out, int dtype_out, float* lse_out, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(rows >= 0 && pieces >= 1, MLA_ERR_INVALID_ARG,
               "mla_merge_states_n: need rows (%lld) >= 0 and pieces (%d) >= 1", (long long)rows, pieces);
   if (rows == 0) return MLA_OK;

@@ -59,6 +59,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ---------------------------------------------------------------- host error state
 void mla_set_error(const char* fmt, ...);
 void mla_clear_error();
+// start of every entry point that launches: clears the message and any
+// stale runtime error left by earlier, unrelated calls
+void mla_begin_call();
 int mla_check_launch(const char* what);
 // compute units of the current device (0 if the runtime cannot tell)
 int mla_num_cus();

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const uint16_t* qin, uin
 
 extern "C" int mla_rope_relocate_q(const void* q_in, void* q_out, int64_t q_row_stride, int T, int H,
                                    int64_t delta, double rope_base, int pairing, void* stream) {
-  mla_clear_error();
+  mla_begin_call();
   MLA_REQUIRE(T >= 0 && H >= 0, MLA_ERR_INVALID_ARG, "mla_rope_relocate_q: T and H must be >= 0");
   if (T == 0 || H == 0) return MLA_OK;
   MLA_REQUIRE(q_in && q_out, MLA_ERR_INVALID_ARG, "mla_rope_relocate_q: q is null");

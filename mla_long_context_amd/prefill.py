@@ -73,7 +73,34 @@ def upload_pool(prob, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(prob.pool)).to(device)
 
 
-class ChunkedPrefill:
+def _capturing() -> bool:
+    return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+
+
+class _DeviceStatus:
+    """The device status word every gather of a driver reports into (a block
+    id outside the pool makes the gather write zeros for those tokens and
+    store MLA_ERR_OUT_OF_RANGE there)."""
+
+    def check(self, stream=None):
+        """Wait for the work enqueued so far, then raise MlaError if a kernel
+        stored an error in the status word; the word is cleared for the next
+        step either way. Not allowed while a graph is being captured."""
+        if stream is None:
+            torch.cuda.synchronize(self.dev_status.device)
+        else:
+            stream.synchronize()
+        code = int(self.dev_status.item())
+        if code != 0:
+            self.dev_status.zero_()
+            L.raise_on_device_status(code, type(self).__name__)
+
+    def _finish(self, check, stream):
+        if check and not _capturing():
+            self.check(stream)
+
+
+class ChunkedPrefill(_DeviceStatus):
     """Configs with a paged context and new (extend) tokens per request."""
 
     def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True):
@@ -168,7 +195,7 @@ class ChunkedPrefill:
     def merge(self, a, da, la, b, db, lb, out, dout, lout, stream=None):
         L.mla_merge_states(a, da, la, b, db, lb, self.T * self.H, out, dout, lout, stream)
 
-    def run(self, stream=None, timer=None):
+    def run(self, stream=None, timer=None, check=True):
         """One pass of the chunk loop. Chunk 0's attention writes the running
         fp32 state (acc). Each later chunk, and then the causal pass over the
         new tokens, is merged into it, either by mla_merge_states after the
@@ -176,7 +203,16 @@ class ChunkedPrefill:
         (mla_prefill_attn_merge): fuse_merge selects which merges are fused
         ("none", "final" = only the last, "all"). The last merge writes the
         bf16 result. With "all", the last chunk and the causal pass share
-        one launch (mla_prefill_attn_2seg)."""
+        one launch (mla_prefill_attn_2seg).
+
+        check: wait for the step and raise if the gather met a block id
+        outside the pool (skipped under graph capture; a caller timing steps
+        passes False and calls check() afterwards)."""
+        out = self._run(stream, timer)
+        self._finish(check, stream)
+        return out
+
+    def _run(self, stream, timer):
         if self.T == 0:
             return self.out, self.lse
         fuse_mid = self.fuse_merge == "all"
@@ -196,7 +232,7 @@ class ChunkedPrefill:
                 with _span(timer, "attn_ctx"):
                     self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
             elif fuse_mid:
-                with _span(timer, "attn_ctx"):
+                with _span(timer, "attn_ctx_merge"):
                     self.attend_merge(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l,
                                       stream)
             else:
@@ -233,17 +269,19 @@ class ChunkedPrefill:
         dec_tok = int(C.sum() + E.sum())
         ctx_pairs = int((C * E).sum())
         ext_pairs = int((E * (E + 1) // 2).sum())
-        # context pairs of the last chunk (its pass also takes the new
-        # tokens when the chunk loop ends in one two-segment launch)
-        last_pairs = 0
-        if self.chunks:
-            c = len(self.chunks) - 1
-            last_pairs = int((np.clip(C - c * self.S, 0, self.S) * E).sum())
+        # context pairs per chunk: chunk 0's plain pass, the merging passes
+        # of the chunks after it, and the last chunk (whose pass also takes
+        # the new tokens when the chunk loop ends in one two-segment launch)
+        pairs = [int((np.clip(C - c * self.S, 0, self.S) * E).sum()) for c in range(len(self.chunks))]
+        last_pairs = pairs[-1] if pairs else 0
+        first_pairs = pairs[0] if pairs and not (self.two_seg and len(pairs) == 1) else 0
+        mid_pairs = ctx_pairs - first_pairs - (last_pairs if self.two_seg else 0)
         n_merge = max(len(self.chunks) - 1, 0) + (1 if self.chunks else 0)
         return dict(
             dec_flops=2 * 512 * 256 * H * dec_tok,
             attn_flops=640 * H * (ctx_pairs + ext_pairs),
-            ctx_attn_flops=640 * H * (ctx_pairs - last_pairs if self.two_seg else ctx_pairs),
+            ctx_attn_flops=640 * H * first_pairs,
+            ctx_merge_attn_flops=640 * H * mid_pairs,
             ext_attn_flops=0 if self.two_seg else 640 * H * ext_pairs,
             last_attn_flops=640 * H * (last_pairs + ext_pairs) if self.two_seg else 0,
             gather_tokens=int(C.sum()),
@@ -252,7 +290,7 @@ class ChunkedPrefill:
         )
 
 
-class ReusePrefill:
+class ReusePrefill(_DeviceStatus):
     """Head-partitioned reuse over one or more documents stored at canonical
     positions. Each document is visited in turn: the queries are relocated by
     its request offset (and re-absorbed for the Local rows), then its chunks
@@ -299,6 +337,8 @@ class ReusePrefill:
         if self.fallback is not None:
             prot_rows = np.arange(prob.T, dtype=np.int64)
             local_path = "decompressed"
+        if len(prot_rows) and (np.any(np.diff(prot_rows) <= 0) or prot_rows[0] < 0 or prot_rows[-1] >= prob.T):
+            raise ValueError("ReusePrefill: protected rows must be strictly increasing row indices below T")
         self.device = device
         self.local_path = local_path
         self.absorbed = local_path == "absorbed"
@@ -467,7 +507,13 @@ class ReusePrefill:
                                lo, stream)
             n = m
 
-    def run(self, stream=None, timer=None):
+    def run(self, stream=None, timer=None, check=True):
+        """One reuse step; returns y. check as in ChunkedPrefill.run."""
+        y = self._run(stream, timer)
+        self._finish(check, stream)
+        return y
+
+    def _run(self, stream, timer):
         p = self.prob
         H, HL, HG, T, P = self.H, self.HL, self.HG, self.T, self.P
         cur_doc = -1
@@ -587,7 +633,7 @@ def artifact_meta(tokens, generation, H, n_local, rope_base=10000.0, n_layers=1,
                           reserved=0, layer_mask=mask)
 
 
-class ArtifactBuilder:
+class ArtifactBuilder(_DeviceStatus):
     """MLA-Off: one document processed alone at canonical position zero,
     Local heads only (RedKnot-MLA Abstract and section 2).
 
@@ -664,7 +710,16 @@ class ArtifactBuilder:
         else:
             L.mla_prefill_attn(*common, out, odt, HL * D_V, lse, HL, stream)
 
-    def run(self, stream=None, timer=None) -> Artifact:
+    def run(self, stream=None, timer=None, check=True) -> Artifact:
+        """Build the artifact. check: wait for the build and raise before the
+        Artifact is returned if the gather met a block id outside the pool
+        (an artifact built from zero records must not be handed out);
+        skipped under graph capture."""
+        art = self._run(stream, timer)
+        self._finish(check, stream)
+        return art
+
+    def _run(self, stream, timer) -> Artifact:
         n_ch = len(self.chunks)
         if n_ch == 0 and self.R > 0 and self.HL > 0:
             # an empty document: every row sees no key, so the attention over

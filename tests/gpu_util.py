@@ -11,15 +11,44 @@ BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
 LSE_ABS = 1e-3
 FP8_REL_L2 = 2e-2
-# Edge-case problems (not the standard workloads): rows that see fewer than
-# FEW_KEYS keys have an lse dominated by a handful of scores. A score's error
-# from rounding a decompressed key to bf16 (unit roundoff 2^-8) is up to
-# scale * 2^-8 * sum_d |q_d k_d|, about 2.3e-2 for N(0,1) data at d = 128 (an
-# fp8 cache adds the same again from rounding the dequantised latent), and
-# with few keys it is not averaged away. Such rows are held to LSE_FEW_KEYS;
-# every row of the standard workloads sees >= 257 keys and is held to LSE_ABS.
+# Rows of an lse check that see fewer than FEW_KEYS keys with a random
+# kv_b_proj take a bound derived from their own data (kv_rounding_lse_bound);
+# every other row is held to LSE_ABS. Edge-case problems use a selection
+# kv_b_proj (exact decompressed keys) and hold every row to LSE_ABS.
 FEW_KEYS = 256
-LSE_FEW_KEYS = 3e-2
+# unit roundoff of bf16 (8 significant bits), and the first-order error
+# factor of a 512-term fp32 dot product
+U_BF16 = 2.0 ** -8
+GAMMA_512 = 512 * 2.0 ** -24
+# allowance for the attention kernel's own fp32 arithmetic (scores, exp2,
+# sums, log) in a derived lse bound: half the lse bar
+ATTN_ALLOW = 5e-4
+
+
+def kv_rounding_lse_bound(q, c_kv, W, H, h, scale, visible=None, dequant_rounding=False):
+    """Bound on |lse_gpu - lse_oracle| per query row of head h when the
+    oracle scores the exact decompressed keys k = c_kv W_UK^h and the GPU
+    the bf16 ones it stores.
+
+    The GPU key is bf16(fp32 sum): |k~_d - k_d| <= U |k_d| + 1.01 (GAMMA +
+    U') sum_i |c_i W_id|, where U' = U when the latent itself was rounded to
+    bf16 first (a dequantised fp8 cache) and 0 otherwise. A score moves by at
+    most scale * sum_d |q_d| |k~_d - k_d|, and the lse, being 1-Lipschitz in
+    the max-norm of the scores, by at most the largest such move over the
+    visible keys. q: [R, >=128] fp64 (nope part first), c_kv [N, 512] fp64,
+    W [512, H*256] fp64, visible [R, N] bool or None. Returns [R]."""
+    q = np.asarray(q, np.float64)
+    R = q.shape[0]
+    if c_kv.shape[0] == 0:
+        return np.full(R, ATTN_ALLOW)
+    Wk = W[:, h * 128:(h + 1) * 128]
+    k = c_kv @ Wk
+    a = np.abs(c_kv) @ np.abs(Wk)
+    dk = U_BF16 * np.abs(k) + 1.01 * (GAMMA_512 + (U_BF16 if dequant_rounding else 0.0)) * a
+    ds = scale * (np.abs(q[:, :128]) @ dk.T)
+    if visible is not None:
+        ds = np.where(visible, ds, 0.0)
+    return ds.max(axis=1) + ATTN_ALLOW
 
 
 def require_gpu():

@@ -227,3 +227,33 @@ def test_attn_merge_cache_absorbed_validation(lib):
     assert mla.mla_absorbed_attn(None, 0, None, 576, None, 0, 0.07, None, 0, None, stream=0) == 0
     assert _err(mla.mla_absorb_out, FAKE, 4, FAKE, 8, 0, 8, FAKE, 100)[0] == _lib.MLA_ERR_INVALID_ARG
     assert _err(mla.mla_absorb_out, FAKE, 4, FAKE, 8, 2, 9, FAKE, 1024)[0] == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_device_status_raises_only_on_error():
+    """The drivers' check() turns a non-zero device status word into MlaError
+    (the decision is host logic; a GPU test drives it with a bad block id)."""
+    _lib.raise_on_device_status(0, "step")
+    with pytest.raises(mla.MlaError) as ei:
+        _lib.raise_on_device_status(_lib.MLA_ERR_OUT_OF_RANGE, "ChunkedPrefill")
+    assert ei.value.code == _lib.MLA_ERR_OUT_OF_RANGE and "outside the pool" in str(ei.value)
+
+
+def _absorbed_dma_keys(n_k, tile=32, stages=4, rows=32):
+    """Host model of the keys the absorbed-attention kernel's DMA reads for a
+    piece of n_k keys: the prologue fills stages-1 stages and every step one
+    more, each with the tile index clamped to the last tile and every key
+    clamped to the last key; an empty piece issues none."""
+    ntiles = (n_k + tile - 1) // tile
+    keys = set()
+    if ntiles > 0:
+        for t in list(range(stages - 1)) + [t + stages - 1 for t in range(ntiles)]:
+            kt0 = min(t, ntiles - 1) * tile
+            keys |= {min(kt0 + r, n_k - 1) for r in range(rows)}
+    return keys
+
+
+@pytest.mark.parametrize("n_k", [0, 1, 31, 32, 33, 100])
+def test_absorbed_dma_stays_inside_the_piece(n_k):
+    keys = _absorbed_dma_keys(n_k)
+    assert all(0 <= k < n_k for k in keys)
+    assert keys == set(range(n_k))
