@@ -382,6 +382,27 @@ int mla_head_partition_merge(const void* art_out, const void* rec_out,
                              int d_mid, int d_model, void* z, void* y, void* stream);
 
 /*
+ * mla_head_partition_merge_noalloc -- mla_head_partition_merge without the z
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the intermediate z lives in a scratch array inside the
+ * library, 8 MiB per device (T * d_mid <= 4194304 bf16 elements; larger
+ * calls return MLA_ERR_INVALID_ARG and enqueue nothing). The array is
+ * loaded with the library on each device it runs on and held until the
+ * process ends; its device address is taken on the first call on a device
+ * (no allocation). Every call on one device shares that device's array:
+ * calls that overlap on one device (several streams, several threads) race
+ * and must be ordered by the caller. z is fully written before it is read,
+ * so nothing needs clearing between calls. Arguments, results and errors
+ * otherwise as mla_head_partition_merge; MLA_ERR_LAUNCH if the scratch
+ * array's address cannot be obtained.
+ */
+int mla_head_partition_merge_noalloc(const void* art_out, const void* rec_out,
+                                     const int32_t* prot_rows, int P, const void* glob_out,
+                                     const void* wa_t, const void* wb_t, int T, int HL, int HG,
+                                     int d_mid, int d_model, void* y, void* stream);
+
+/*
  * Validation of an offline Local-head artifact before it is reused
  * ([REDKNOT] section 2, "Canonical offline artifacts": each document is
  * processed alone at canonical position zero and its Local-head results are

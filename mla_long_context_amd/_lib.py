@@ -30,7 +30,7 @@ EXPORTS = (
     "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_prefill_attn_2seg", "mla_absorb_q",
     "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states", "mla_merge_states_n",
     "mla_rope_relocate_q",
-    "mla_head_partition_merge", "mla_token_hash", "mla_artifact_check",
+    "mla_head_partition_merge", "mla_head_partition_merge_noalloc", "mla_token_hash", "mla_artifact_check",
 )
 
 # reasons written by mla_artifact_check
@@ -100,6 +100,7 @@ _SIGS = {
     "mla_merge_states_n": [P, I32, P, I32, I64, P, I32, P, P],
     "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
     "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
+    "mla_head_partition_merge_noalloc": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P],
     "mla_artifact_check": [ctypes.POINTER(ArtifactMeta), ctypes.POINTER(ArtifactMeta), ctypes.POINTER(I32)],
 }
 
@@ -246,6 +247,12 @@ def mla_head_partition_merge(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_
     return _call("mla_head_partition_merge", _ptr(art_out), _ptr(rec_out), _ptr(prot_rows), P,
                  _ptr(glob_out), _ptr(wa_t), _ptr(wb_t), T, HL, HG, d_mid, d_model, _ptr(z),
                  _ptr(y), _stream(stream))
+
+
+def mla_head_partition_merge_noalloc(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_t, T, HL, HG,
+                                     d_mid, d_model, y, stream=None):
+    return _call("mla_head_partition_merge_noalloc", _ptr(art_out), _ptr(rec_out), _ptr(prot_rows), P,
+                 _ptr(glob_out), _ptr(wa_t), _ptr(wb_t), T, HL, HG, d_mid, d_model, _ptr(y), _stream(stream))
 
 
 def mla_token_hash(tokens) -> int:

@@ -20,6 +20,7 @@
 // which the epilogue packs into 8-byte LDS writes before 16-byte coalesced
 // global stores.
 #include <algorithm>
+#include <mutex>
 
 #include "mla_internal.h"
 
@@ -581,30 +582,103 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
   return mla_check_launch("mla_decompress");
 }
 
+namespace {
+
+// Sliced projection then shared projection through the intermediate z
+// (bf16 [T][d_mid], device memory of at least T * d_mid elements).
+int head_partition_merge_impl(const void* art_out, const void* rec_out, const int32_t* prot_rows, int P,
+                              const void* glob_out, const void* wa_t, const void* wb_t, int T, int HL, int HG,
+                              int d_mid, int d_model, void* z, void* y, void* stream, const char* name) {
+  MLA_REQUIRE(T >= 0 && P >= 0 && P <= T && HL >= 0 && HG >= 0 && HL + HG > 0, MLA_ERR_INVALID_ARG,
+              "%s: need T >= 0, 0 <= P <= T, HL, HG >= 0, HL + HG > 0", name);
+  if (T == 0) return MLA_OK;
+  MLA_REQUIRE(wa_t && wb_t && z && y && (HL == 0 || art_out) && (HG == 0 || glob_out) &&
+                  (P == 0 || (rec_out && prot_rows)),
+              MLA_ERR_INVALID_ARG, "%s: null pointer argument", name);
+  MLA_REQUIRE(d_mid > 0 && d_model > 0 && d_mid % kTileMin == 0 && d_model % kTileMin == 0, MLA_ERR_UNSUPPORTED,
+              "%s: d_mid (%d) and d_model (%d) must be multiples of 128", name, d_mid, d_model);
+  MLA_REQUIRE((HL * kDv) % BK == 0, MLA_ERR_UNSUPPORTED, "%s: HL*128 must be a multiple of 64", name);
+  const void* ptrs[] = {art_out, rec_out, glob_out, wa_t, wb_t, z, y};
+  for (const void* q : ptrs) MLA_REQUIRE(!q || mla_aligned16(q), MLA_ERR_INVALID_ARG,
+                                         "%s: pointers must be 16-byte aligned", name);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  SlicedProjP p1{static_cast<const uint16_t*>(art_out), static_cast<const uint16_t*>(rec_out), prot_rows, P,
+                 static_cast<const uint16_t*>(glob_out), T, HL, HG, static_cast<const uint16_t*>(wa_t),
+                 (HL + HG) * kDv, static_cast<uint16_t*>(z), d_mid};
+  int rc = launch_gemm(p1, T, d_mid, s, name);
+  if (rc != MLA_OK) return rc;
+  PlainP p2{static_cast<const uint16_t*>(z), T, d_mid, static_cast<const uint16_t*>(wb_t),
+            static_cast<uint16_t*>(y), d_model};
+  return launch_gemm(p2, T, d_model, s, name);
+}
+
+}  // namespace
+
 extern "C" int mla_head_partition_merge(const void* art_out, const void* rec_out,
                                         const int32_t* prot_rows, int P, const void* glob_out,
                                         const void* wa_t, const void* wb_t, int T, int HL, int HG,
                                         int d_mid, int d_model, void* z, void* y, void* stream) {
   mla_begin_call();
-  MLA_REQUIRE(T >= 0 && P >= 0 && P <= T && HL >= 0 && HG >= 0 && HL + HG > 0, MLA_ERR_INVALID_ARG,
-              "mla_head_partition_merge: need T >= 0, 0 <= P <= T, HL, HG >= 0, HL + HG > 0");
-  if (T == 0) return MLA_OK;
-  MLA_REQUIRE(wa_t && wb_t && z && y && (HL == 0 || art_out) && (HG == 0 || glob_out) &&
-                  (P == 0 || (rec_out && prot_rows)),
-              MLA_ERR_INVALID_ARG, "mla_head_partition_merge: null pointer argument");
-  MLA_REQUIRE(d_mid > 0 && d_model > 0 && d_mid % kTileMin == 0 && d_model % kTileMin == 0, MLA_ERR_UNSUPPORTED,
-              "mla_head_partition_merge: d_mid (%d) and d_model (%d) must be multiples of 128", d_mid, d_model);
-  MLA_REQUIRE((HL * kDv) % BK == 0, MLA_ERR_UNSUPPORTED, "mla_head_partition_merge: HL*128 must be a multiple of 64");
-  const void* ptrs[] = {art_out, rec_out, glob_out, wa_t, wb_t, z, y};
-  for (const void* q : ptrs) MLA_REQUIRE(!q || mla_aligned16(q), MLA_ERR_INVALID_ARG,
-                                         "mla_head_partition_merge: pointers must be 16-byte aligned");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  SlicedProjP p1{static_cast<const uint16_t*>(art_out), static_cast<const uint16_t*>(rec_out), prot_rows, P,
-                 static_cast<const uint16_t*>(glob_out), T, HL, HG, static_cast<const uint16_t*>(wa_t),
-                 (HL + HG) * kDv, static_cast<uint16_t*>(z), d_mid};
-  int rc = launch_gemm(p1, T, d_mid, s, "mla_head_partition_merge (sliced projection)");
-  if (rc != MLA_OK) return rc;
-  PlainP p2{static_cast<const uint16_t*>(z), T, d_mid, static_cast<const uint16_t*>(wb_t),
-            static_cast<uint16_t*>(y), d_model};
-  return launch_gemm(p2, T, d_model, s, "mla_head_partition_merge (shared projection)");
+  return head_partition_merge_impl(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_t, T, HL, HG, d_mid,
+                                   d_model, z, y, stream, "mla_head_partition_merge");
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+//
+// The intermediate z of mla_head_partition_merge_noalloc lives in this
+// file-scope device array: one copy per device, loaded with the code object
+// and held until the process ends. Host code never passes its name to a
+// kernel (on the host the name is only a stand-in); it takes the device
+// address of the current device's copy with hipGetSymbolAddress, once per
+// device, and uses that address.
+constexpr int64_t kHpmScratchBytes = (int64_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kHpmScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// device address of the current device's scratch array, or nullptr (with
+// the error message set)
+void* scratch_on_current_device(const char* name) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    mla_set_error("%s: cannot tell the current device", name);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      mla_set_error("%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", name, dev,
+                    hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_addr[dev] = ptr;
+  }
+  return g_scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" int mla_head_partition_merge_noalloc(const void* art_out, const void* rec_out,
+                                                const int32_t* prot_rows, int P, const void* glob_out,
+                                                const void* wa_t, const void* wb_t, int T, int HL, int HG,
+                                                int d_mid, int d_model, void* y, void* stream) {
+  mla_begin_call();
+  const char* name = "mla_head_partition_merge_noalloc";
+  MLA_REQUIRE(T >= 0 && d_mid > 0, MLA_ERR_INVALID_ARG, "%s: need T >= 0 and d_mid > 0", name);
+  MLA_REQUIRE((int64_t)T * d_mid * 2 <= kHpmScratchBytes, MLA_ERR_INVALID_ARG,
+              "%s: T * d_mid (%lld) exceeds the scratch array's %lld bf16 elements; use "
+              "mla_head_partition_merge with a workspace",
+              name, (long long)T * d_mid, (long long)(kHpmScratchBytes / 2));
+  if (T == 0) return head_partition_merge_impl(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_t, T, HL, HG,
+                                               d_mid, d_model, nullptr, y, stream, name);
+  void* z = scratch_on_current_device(name);
+  if (!z) return MLA_ERR_LAUNCH;
+  return head_partition_merge_impl(art_out, rec_out, prot_rows, P, glob_out, wa_t, wb_t, T, HL, HG, d_mid,
+                                   d_model, z, y, stream, name);
 }

@@ -257,3 +257,13 @@ def test_absorbed_dma_stays_inside_the_piece(n_k):
     keys = _absorbed_dma_keys(n_k)
     assert all(0 <= k < n_k for k in keys)
     assert keys == set(range(n_k))
+
+
+def test_noalloc_merge_rejects_sizes_beyond_its_scratch(lib):
+    # T * d_mid above 4194304 bf16 elements is refused before anything else
+    code, msg = _err(mla.mla_head_partition_merge_noalloc, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2049, 7, 1,
+                     2048, 128, FAKE)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "scratch" in msg
+    # an empty call is a no-op
+    assert mla.mla_head_partition_merge_noalloc(None, None, None, 0, None, FAKE, FAKE, 0, 7, 1, 2048, 128, FAKE,
+                                                stream=0) == 0
