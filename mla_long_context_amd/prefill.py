@@ -124,19 +124,41 @@ class ChunkedPrefill(_DeviceStatus):
         C = prob.ctx_len.astype(np.int64)
         n_chunks = int(max((int(c) + self.S - 1) // self.S for c in C)) if self.B else 0
         self.chunks = []
+        off = 0
+        starts, lens = [], []
         for c in range(n_chunks):
             start = np.full(self.B, c * self.S, dtype=np.int64)
             ln = np.clip(C - c * self.S, 0, self.S)
             self.chunks.append(dict(start=_i32(start, device), len=_i32(ln, device),
-                                    cu=_i32(_cu(ln), device), n=int(ln.sum()), max_len=int(ln.max())))
+                                    cu=_i32(_cu(ln), device), n=int(ln.sum()), max_len=int(ln.max()),
+                                    lat_off=off))
+            starts.append(start)
+            lens.append(ln)
+            off += int(ln.sum())
         max_ctx_tok = max([ch["n"] for ch in self.chunks] + [1])
+        # Every chunk's records are gathered by one launch at the start of a
+        # step, into one workspace where chunk c's records start at row
+        # lat_off: each (chunk, request) is a request of that launch, with
+        # the request's block-table row repeated per chunk.
+        self.gather_once = bool(self.chunks) and n_chunks * self.B <= 65535
+        if self.gather_once:
+            self.g_start = _i32(np.concatenate(starts), device)
+            self.g_len = _i32(np.concatenate(lens), device)
+            self.g_cu = _i32(_cu(np.concatenate(lens)), device)
+            self.g_bt = _i32(np.tile(prob.block_table, (n_chunks, 1)), device)
+            self.g_batch = n_chunks * self.B
+            self.g_max = max(int(np.concatenate(lens).max()), 0)
+        else:
+            for ch in self.chunks:
+                ch["lat_off"] = 0
         # With every merge fused, the last chunk's pass also covers the new
         # tokens (mla_prefill_attn_2seg): their keys are decompressed behind
         # the chunk's, at token offset ext_off of the same workspaces.
         self.two_seg = two_segment and fuse_merge == "all" and bool(self.chunks)
         self.ext_off = max_ctx_tok if self.two_seg else 0
         self.max_tok = max([ch["n"] for ch in self.chunks] + [self.ext_off + self.T, 1])
-        self.lat_ws = torch.empty((max_ctx_tok, D_LAT), dtype=torch.bfloat16, device=device)
+        lat_rows = max(off, 1) if self.gather_once else max_ctx_tok
+        self.lat_ws = torch.empty((lat_rows, D_LAT), dtype=torch.bfloat16, device=device)
         self.k_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
         self.v_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
         self.hstride = self.max_tok * D_V
@@ -152,9 +174,20 @@ class ChunkedPrefill(_DeviceStatus):
 
     # one step of the path per call
     def gather(self, ch, stream=None):
+        """The records of chunk ch (when they are not gathered all at once)."""
         L.mla_gather_context(self.pool, self.cache_dtype, self.prob.num_blocks, self.bt,
                              self.bt.shape[1], ch["start"], ch["len"], ch["cu"], self.B,
                              ch["max_len"], self.lat_ws, self.dev_status, stream)
+
+    def gather_all(self, stream=None):
+        """Every chunk's records in one launch (chunk c's from row lat_off)."""
+        L.mla_gather_context(self.pool, self.cache_dtype, self.prob.num_blocks, self.g_bt,
+                             self.g_bt.shape[1], self.g_start, self.g_len, self.g_cu, self.g_batch,
+                             self.g_max, self.lat_ws, self.dev_status, stream)
+
+    def _lat(self, ch):
+        # device address of chunk ch's first record in the latent workspace
+        return self.lat_ws.data_ptr() + ch["lat_off"] * D_LAT * 2
 
     def decompress(self, latent, n, stream=None, off=0):
         """k_nope / v of n tokens into the workspaces from token `off` on."""
@@ -171,7 +204,7 @@ class ChunkedPrefill(_DeviceStatus):
         (causal) in one pass, merged into the running state when `merge`;
         writes the bf16 result."""
         L.mla_prefill_attn_2seg(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
-                                self.v_ws, self.hstride, self.lat_ws, D_LAT, ch["cu"],
+                                self.v_ws, self.hstride, self._lat(ch), D_LAT, ch["cu"],
                                 self._at(self.k_ws, self.ext_off), self.hstride,
                                 self._at(self.v_ws, self.ext_off), self.hstride, self.ext, D_LAT,
                                 self.cu_ext, self.cu_ext, self.B, self.maxE, self.prob.scale,
@@ -217,11 +250,16 @@ class ChunkedPrefill(_DeviceStatus):
             return self.out, self.lse
         fuse_mid = self.fuse_merge == "all"
         fuse_last = self.fuse_merge in ("all", "final")
-        for ci, ch in enumerate(self.chunks):
+        if self.gather_once:
             with _span(timer, "gather"):
-                self.gather(ch, stream)
+                self.gather_all(stream)
+        for ci, ch in enumerate(self.chunks):
+            if not self.gather_once:
+                with _span(timer, "gather"):
+                    self.gather(ch, stream)
+            lat = self._lat(ch)
             with _span(timer, "decompress"):
-                self.decompress(self.lat_ws, ch["n"], stream)
+                self.decompress(lat, ch["n"], stream)
             if self.two_seg and ci == len(self.chunks) - 1:
                 with _span(timer, "decompress"):
                     self.decompress(self.ext, self.T, stream, off=self.ext_off)
@@ -230,14 +268,13 @@ class ChunkedPrefill(_DeviceStatus):
                 return self.out, self.lse
             if ci == 0:
                 with _span(timer, "attn_ctx"):
-                    self.attend(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
+                    self.attend(lat, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
             elif fuse_mid:
                 with _span(timer, "attn_ctx_merge"):
-                    self.attend_merge(self.lat_ws, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l,
-                                      stream)
+                    self.attend_merge(lat, ch["cu"], 0, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)
             else:
                 with _span(timer, "attn_ctx"):
-                    self.attend(self.lat_ws, ch["cu"], 0, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
+                    self.attend(lat, ch["cu"], 0, self.tmp_o, L.DTYPE_BF16, self.tmp_l, stream)
                 with _span(timer, "merge"):
                     self.merge(self.acc_o, L.DTYPE_FP32, self.acc_l, self.tmp_o, L.DTYPE_BF16,
                                self.tmp_l, self.acc_o, L.DTYPE_FP32, self.acc_l, stream)

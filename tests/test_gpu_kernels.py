@@ -56,6 +56,37 @@ def test_gather_bit_exact(dtype):
     assert not np.any(np.isnan(f64(out[:-1])))
 
 
+def test_gather_fp8_every_code():
+    """Every E4M3FN code (subnormals, both zeros, +-448 and the two NaN codes)
+    in every byte position of a record, under several scales, dequantised
+    bit for bit as the oracle's bf16_rne(fp32_rne(decode(code) * scale))."""
+    require_gpu()
+    rng = np.random.default_rng(43)
+    nb = 2
+    pool = np.zeros((nb, orc.fp8_block_bytes()), dtype=np.uint8)
+    codes = np.zeros((nb, 64, 512), dtype=np.uint8)
+    for blk in range(nb):
+        for slot in range(64):
+            codes[blk, slot] = np.roll(np.tile(np.arange(256, dtype=np.uint8), 2), 7 * slot + 3 * blk)
+    pool[:, :mi.FP8_ROPE_OFF] = codes.reshape(nb, -1)
+    pool[:, mi.FP8_ROPE_OFF:mi.FP8_SCALE_OFF] = np.frombuffer(
+        mi.f32_to_bf16_bits(rng.standard_normal((nb, 64, 64)).astype(np.float32)).tobytes(),
+        dtype=np.uint8).reshape(nb, -1)
+    scales = np.array([1.0, 1 / 448, 0.37, 2.5e-3, 7.0, 1e-6, 3.3e4, 0.0] * 16, dtype=np.float32).reshape(nb, 64)
+    pool[:, mi.FP8_SCALE_OFF:] = scales.view(np.uint8).reshape(nb, -1)
+    bt = np.array([[1, 0]], dtype=np.int32)
+    out = torch.empty((128, 576), dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_gather_context(torch.from_numpy(pool).cuda(), mla.DTYPE_FP8_E4M3, nb, _i32(bt), 2, _i32([0]), _i32([128]),
+                           _i32([0, 128]), 1, 128, out, status)
+    torch.cuda.synchronize()
+    ref = orc.gather_fp8_expected_bits(pool, bt, 0, 0, 128)
+    got = bits(out)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} differing elements, first {bad[:4].tolist()}"
+    assert int(status.item()) == 0
+
+
 def test_gather_out_of_range_block_sets_status_and_writes_zeros():
     require_gpu()
     prob = mi.make_problem(1, [128], [1], 64, "bf16", seed=42)
