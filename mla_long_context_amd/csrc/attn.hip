@@ -419,7 +419,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     if (kt0 < (s2 ? wave_kend2 : wave_kend)) {
       qk(stage(kt));
       softmax(kt0, s2);
+      // The PV products run at raised wave priority: of the two wavefronts
+      // a SIMD holds (two workgroups per CU), the one with products ready
+      // keeps the matrix core fed while the other computes its softmax.
+      __builtin_amdgcn_s_setprio(1);
       pv(stage(kt) + kKTile);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
   // no DMA may still be writing this workgroup's LDS when it ends
