@@ -71,7 +71,7 @@ typedef enum {
 /* Message describing the last error returned on this thread ("" if none). */
 const char* mla_last_error(void);
 
-/* ABI version, currently 1. */
+/* ABI version, currently 2. */
 int mla_abi_version(void);
 
 /*
@@ -105,6 +105,28 @@ int mla_gather_context(const void* pool, int cache_dtype, int num_blocks,
                        const int32_t* chunk_start, const int32_t* chunk_len,
                        const int32_t* cu_out, int batch, int max_len,
                        void* out_latent, int32_t* dev_status, void* stream);
+
+/*
+ * mla_gather_context_fp8_raw -- mla_gather_context for an fp8 cache without
+ * dequantisation ([DSMLA] 4.4 step 1 with the fp8 storage of 2.2): the
+ * decompression then reads the codes itself (mla_decompress with row_scale),
+ * so c_kv moves as 512 bytes per token instead of 1024.
+ *
+ * Arguments as mla_gather_context (pool is the fp8 layout), and for output
+ * row o = cu_out[b] + (t - chunk_start[b]) of token t:
+ *   out_latent  device, rows of 576 bf16 elements (1152 bytes): bytes
+ *               0..511 of row o are the token's 512 E4M3FN codes of c_kv,
+ *               copied; elements 512..575 its bf16 k_rope, copied; bytes
+ *               512..1023 are not written.
+ *   out_scale   device fp32 [cu_out[batch]]: out_scale[o] is the token's scale.
+ * A block id outside [0, num_blocks) writes zero codes, scale 0 and zero
+ * k_rope for that token and stores MLA_ERR_OUT_OF_RANGE into *dev_status.
+ * Pointers 16-byte aligned.
+ */
+int mla_gather_context_fp8_raw(const void* pool, int num_blocks, const int32_t* block_table,
+                               int64_t bt_stride, const int32_t* chunk_start, const int32_t* chunk_len,
+                               const int32_t* cu_out, int batch, int max_len, void* out_latent,
+                               float* out_scale, int32_t* dev_status, void* stream);
 
 /*
  * mla_pack_weight_t -- weight layout transform done once at load time (not
@@ -148,7 +170,14 @@ int mla_cache_append(void* pool, int cache_dtype, int num_blocks, const int32_t*
  * mla_decompress -- [DSMLA] 4.4 step 2: kv = c_kv . kv_b_proj, split into
  * per-head k_nope and v.
  *
- *   latent      device bf16 [n_tokens][ld_latent]; c_kv = columns 0..511.
+ *   latent      device, rows of ld_latent bf16 elements (2 * ld_latent
+ *               bytes), n_tokens rows. Without row_scale: c_kv = elements
+ *               0..511 (bf16). With row_scale: c_kv of row t is
+ *               row_scale[t] times the E4M3FN codes in bytes 0..511 of the
+ *               row (as written by mla_gather_context_fp8_raw, [DSMLA] 2.2);
+ *               the codes enter the bf16 products exactly and the scale
+ *               multiplies the fp32 sums, before the one rounding to bf16.
+ *   row_scale   device fp32 [n_tokens] or NULL (4-byte aligned).
  *   w_t         device bf16 [H_total*256][512]: kv_b_proj packed by
  *               mla_pack_weight_t (row j = output column j; columns
  *               [0, H*128) are W_UK of heads 0..H-1, [H*128, H*256) W_UV).
@@ -159,7 +188,7 @@ int mla_cache_append(void* pool, int cache_dtype, int num_blocks, const int32_t*
  *               keys of a chunk are contiguous).
  * fp32 accumulation, one bf16 rounding of each output.
  */
-int mla_decompress(const void* latent, int64_t ld_latent, int n_tokens,
+int mla_decompress(const void* latent, int64_t ld_latent, const float* row_scale, int n_tokens,
                    const void* w_t, int H_total, int h_begin, int h_end,
                    void* k_nope, int64_t k_head_stride,
                    void* v, int64_t v_head_stride, void* stream);

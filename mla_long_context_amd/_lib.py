@@ -26,7 +26,8 @@ ROPE_INTERLEAVED = 0
 ROPE_HALF = 1
 
 EXPORTS = (
-    "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_cache_append", "mla_pack_weight_t",
+    "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_gather_context_fp8_raw", "mla_cache_append",
+    "mla_pack_weight_t",
     "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_prefill_attn_2seg", "mla_absorb_q",
     "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states", "mla_merge_states_n",
     "mla_rope_relocate_q",
@@ -85,7 +86,8 @@ _SIGS = {
     "mla_gather_context": [P, I32, I32, P, I64, P, P, P, I32, I32, P, P, P],
     "mla_cache_append": [P, I32, I32, P, I64, P, P, I32, I32, P, I64, P, P],
     "mla_pack_weight_t": [P, I32, I32, P, P],
-    "mla_decompress": [P, I64, I32, P, I32, I32, I32, P, I64, P, I64, P],
+    "mla_gather_context_fp8_raw": [P, I32, P, I64, P, P, P, I32, I32, P, P, P, P],
+    "mla_decompress": [P, I64, P, I32, P, I32, I32, I32, P, I64, P, I64, P],
     "mla_prefill_attn": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
                          I32, I32, F32, I32, P, I32, I64, P, I64, P],
     "mla_prefill_attn_merge": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P, P, P,
@@ -168,10 +170,17 @@ def mla_pack_weight_t(w, K, N, out, stream=None):
     return _call("mla_pack_weight_t", _ptr(w), K, N, _ptr(out), _stream(stream))
 
 
-def mla_decompress(latent, ld_latent, n_tokens, w_t, H_total, h_begin, h_end, k_nope,
+def mla_decompress(latent, ld_latent, row_scale, n_tokens, w_t, H_total, h_begin, h_end, k_nope,
                    k_head_stride, v, v_head_stride, stream=None):
-    return _call("mla_decompress", _ptr(latent), ld_latent, n_tokens, _ptr(w_t), H_total, h_begin,
-                 h_end, _ptr(k_nope), k_head_stride, _ptr(v), v_head_stride, _stream(stream))
+    return _call("mla_decompress", _ptr(latent), ld_latent, _ptr(row_scale), n_tokens, _ptr(w_t), H_total,
+                 h_begin, h_end, _ptr(k_nope), k_head_stride, _ptr(v), v_head_stride, _stream(stream))
+
+
+def mla_gather_context_fp8_raw(pool, num_blocks, block_table, bt_stride, chunk_start, chunk_len, cu_out, batch,
+                               max_len, out_latent, out_scale, dev_status=None, stream=None):
+    return _call("mla_gather_context_fp8_raw", _ptr(pool), num_blocks, _ptr(block_table), bt_stride,
+                 _ptr(chunk_start), _ptr(chunk_len), _ptr(cu_out), batch, max_len, _ptr(out_latent),
+                 _ptr(out_scale), _ptr(dev_status), _stream(stream))
 
 
 def mla_prefill_attn(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,

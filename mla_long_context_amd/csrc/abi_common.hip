@@ -55,4 +55,4 @@ int mla_num_cus() {
 
 extern "C" const char* mla_last_error(void) { return g_err; }
 
-extern "C" int mla_abi_version(void) { return 1; }
+extern "C" int mla_abi_version(void) { return 2; }

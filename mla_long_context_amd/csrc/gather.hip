@@ -52,11 +52,16 @@ __device__ __forceinline__ u32x4 dequant8(u32x2 codes, float sc) {
   return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-template <bool kFp8>
+// kRaw (fp8 cache only): the codes are copied as they are into the first
+// 512 bytes of each output row and the scales into out_scale; k_rope as
+// always at elements 512..575.
+template <bool kFp8, bool kRaw = false>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint8_t* __restrict__ pool, int num_blocks, const int32_t* __restrict__ bt,
     int64_t bt_stride, const int32_t* __restrict__ cstart, const int32_t* __restrict__ clen,
-    const int32_t* __restrict__ cu_out, uint16_t* __restrict__ out, int32_t* status) {
+    const int32_t* __restrict__ cu_out, uint16_t* __restrict__ out, int32_t* status,
+    float* __restrict__ out_scale = nullptr) {
+  static_assert(kFp8 || !kRaw, "raw copies are for the fp8 cache");
   const int b = blockIdx.y;
   const int len = clen[b];
   const int start = cstart[b];
@@ -114,9 +119,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
       const int cc = threadIdx.x + k * kThreads;
       const int i = cc >> 5, w = cc & 31;
       if (i >= ntok) continue;
-      // zeros stay zeros (a block outside the pool)
-      dst[i * kVecPerTok + 2 * w] = ok ? dequant8(u32x2{c16[k].x, c16[k].y}, sc[k]) : u32x4{0u, 0u, 0u, 0u};
-      dst[i * kVecPerTok + 2 * w + 1] = ok ? dequant8(u32x2{c16[k].z, c16[k].w}, sc[k]) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kRaw) {
+        // codes 16 w .. 16 w + 15 of the row's first 512 bytes (zeros for a
+        // block outside the pool)
+        reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(dst) + i * (kDlat * 2))[w] = c16[k];
+        if (w == 0) out_scale[(int64_t)cu_out[b] + (t0 - start) + i] = sc[k];
+      } else {
+        // zeros stay zeros (a block outside the pool)
+        dst[i * kVecPerTok + 2 * w] = ok ? dequant8(u32x2{c16[k].x, c16[k].y}, sc[k]) : u32x4{0u, 0u, 0u, 0u};
+        dst[i * kVecPerTok + 2 * w + 1] = ok ? dequant8(u32x2{c16[k].z, c16[k].w}, sc[k]) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int k = 0; k < kFp8RopeVPT; ++k) {
@@ -127,6 +139,32 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 }
 
 }  // namespace
+
+extern "C" int mla_gather_context_fp8_raw(const void* pool, int num_blocks, const int32_t* block_table,
+                                          int64_t bt_stride, const int32_t* chunk_start, const int32_t* chunk_len,
+                                          const int32_t* cu_out, int batch, int max_len, void* out_latent,
+                                          float* out_scale, int32_t* dev_status, void* stream) {
+  mla_begin_call();
+  MLA_REQUIRE(batch >= 0 && max_len >= 0, MLA_ERR_INVALID_ARG,
+              "mla_gather_context_fp8_raw: batch (%d) and max_len (%d) must be >= 0", batch, max_len);
+  if (batch == 0 || max_len == 0) return MLA_OK;
+  MLA_REQUIRE(pool && block_table && chunk_start && chunk_len && cu_out && out_latent && out_scale,
+              MLA_ERR_INVALID_ARG, "mla_gather_context_fp8_raw: null pointer argument");
+  MLA_REQUIRE(num_blocks > 0 && bt_stride > 0, MLA_ERR_INVALID_ARG,
+              "mla_gather_context_fp8_raw: num_blocks (%d) and bt_stride (%lld) must be > 0", num_blocks,
+              (long long)bt_stride);
+  MLA_REQUIRE(mla_aligned16(pool) && mla_aligned16(out_latent) && mla_aligned16(out_scale), MLA_ERR_INVALID_ARG,
+              "mla_gather_context_fp8_raw: pool, out_latent and out_scale must be 16-byte aligned");
+  MLA_REQUIRE(batch <= 65535, MLA_ERR_INVALID_ARG, "mla_gather_context_fp8_raw: batch (%d) must be <= 65535", batch);
+  MLA_REQUIRE((int64_t)max_len + kBlock < (int64_t)1 << 30, MLA_ERR_INVALID_ARG,
+              "mla_gather_context_fp8_raw: max_len (%d) too large for one call", max_len);
+  const int64_t gx = ((int64_t)max_len + kBlock - 1) / kBlock + 1;
+  hipLaunchKernelGGL((gather_kernel<true, true>), dim3((unsigned)gx, (unsigned)batch), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t*>(pool), num_blocks,
+                     block_table, bt_stride, chunk_start, chunk_len, cu_out, static_cast<uint16_t*>(out_latent),
+                     dev_status, out_scale);
+  return mla_check_launch("mla_gather_context_fp8_raw");
+}
 
 extern "C" int mla_gather_context(const void* pool, int cache_dtype, int num_blocks,
                                   const int32_t* block_table, int64_t bt_stride,

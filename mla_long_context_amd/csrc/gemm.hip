@@ -290,15 +290,37 @@ constexpr int kDEpB = 16 * 256;                // epilogue LDS bytes per wavefro
 static_assert(kDNS * kDStageB + 8 * kDEpB <= 160 * 1024 && (kDNS & (kDNS - 1)) == 0 && (kDSteps & (kDSteps - 1)) == 0,
               "decompression LDS ring");
 
+// fp8 (e4m3) A operand: rows of 64 bytes (one k step of codes), 4 chunks
+constexpr int kDRow8 = kDBK;                   // bytes per A row in LDS (fp8)
+constexpr int kDChunks8 = kDRow8 / 16;
+constexpr int kDRowsPerDma8 = 64 / kDChunks8;
+constexpr int kDOpB8 = kDT * kDRow8;           // A bytes per stage (fp8)
+constexpr int kDDmaOp8 = kDOpB8 / 1024 / 8;
+
 // LDS position of chunk c of row r: rows are swizzled so that the 16 rows
 // read by 16 consecutive lanes (same chunk) fall on 16 distinct 16-byte bank
 // groups of a 256-byte bank line
 __device__ __forceinline__ int dec_swz(int r, int c) {
   return c ^ ((r / (16 / kDChunks)) % kDChunks);
 }
+// the same for 64-byte fp8 rows: four rows share a bank line, and rows
+// 4 apart put a chunk on different bank groups
+__device__ __forceinline__ int dec_swz8(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// 8 e4m3 codes (two dwords) -> 8 bf16, exactly (v_cvt_scalef32_pk_bf16_fp8
+// with scale 1: every e4m3 value, subnormals included, is a bf16 value)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 c) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, false);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, true);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, false);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
 struct DecArgs {
   const uint16_t* lat; int64_t ld; int M;
+  const float* scale;                           // fp8 A: per-token scale, else unused
   const uint16_t* wt; int H_total, h_begin, Hsel;
   uint16_t* k; int64_t khs; uint16_t* v; int64_t vhs;
   int n_mt, n_nt;
@@ -320,7 +342,17 @@ __device__ __forceinline__ void dec_tile(int rank, int n_mt, int n_nt, int& mt, 
   nt = in_group / gm;
 }
 
+// kFp8A: the A rows are e4m3 codes (their first 512 bytes), DMA'd to LDS as
+// bytes and widened to bf16 at the fragment read (exactly); the token's
+// scale multiplies the fp32 sums in the epilogue.
+template <bool kFp8A>
 __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
+  constexpr int kARow = kFp8A ? kDRow8 : kDRow;           // A bytes per LDS row
+  constexpr int kAOp = kFp8A ? kDOpB8 : kDOpB;            // A bytes per stage
+  constexpr int kAChunks = kFp8A ? kDChunks8 : kDChunks;
+  constexpr int kARowsPerDma = kFp8A ? kDRowsPerDma8 : kDRowsPerDma;
+  constexpr int kADma = kFp8A ? kDDmaOp8 : kDDmaOp;       // A DMA instructions per wavefront per step
+  constexpr int kStageB = kAOp + kDOpB;                   // bytes per stage (A then W)
   extern __shared__ __attribute__((aligned(1024))) uint8_t dlds[];   // kDNS stages
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -344,16 +376,21 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
   // byte offsets (row kDRowsPerDma * i + lane / kDChunks of instruction
   // i = 8 i2 + wave, chunk lane % kDChunks at its swizzled position), fixed
   // for the tile; the k step only moves the uniform base.
-  uint32_t aof[kDDmaOp], bof[kDDmaOp];
+  uint32_t aof[kADma], bof[kDDmaOp];
   auto set_dma_tile = [&](int j) __attribute__((always_inline)) {
     int mt, nt;
     dec_tile(rbeg + slot + j * nslots, a.n_mt, a.n_nt, mt, nt);
 #pragma unroll
+    for (int i2 = 0; i2 < kADma; ++i2) {
+      const int r = kARowsPerDma * (i2 * 8 + wave) + lane / kAChunks;
+      const int gc = kFp8A ? dec_swz8(r, lane % kAChunks) : dec_swz(r, lane % kAChunks);
+      const int t = min(mt * kDT + r, a.M - 1);
+      aof[i2] = (uint32_t)t * (uint32_t)(a.ld * 2) + gc * 16;
+    }
+#pragma unroll
     for (int i2 = 0; i2 < kDDmaOp; ++i2) {
       const int r = kDRowsPerDma * (i2 * 8 + wave) + lane / kDChunks;
       const int gc = dec_swz(r, lane % kDChunks);
-      const int t = min(mt * kDT + r, a.M - 1);
-      aof[i2] = (uint32_t)t * (uint32_t)(a.ld * 2) + gc * 16;
       const int n = nt * kDT + r;               // output column -> packed weight row
       const int wrow = n < HK ? a.h_begin * kDnope + n : a.H_total * kDnope + a.h_begin * kDnope + (n - HK);
       bof[i2] = (uint32_t)wrow * (kDc * 2) + gc * 16;
@@ -364,15 +401,13 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
   int dj = 0, dkk = 0;
   set_dma_tile(0);
   auto dma_next = [&](int stage) __attribute__((always_inline)) {
-    uint8_t* st = dlds + stage * kDStageB;
-    const uint8_t* sa = reinterpret_cast<const uint8_t*>(a.lat) + dkk * (kDBK * 2);
+    uint8_t* st = dlds + stage * kStageB;
+    const uint8_t* sa = reinterpret_cast<const uint8_t*>(a.lat) + dkk * kARow;
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.wt) + dkk * (kDBK * 2);
 #pragma unroll
-    for (int i2 = 0; i2 < kDDmaOp; ++i2) {
-      const int i = i2 * 8 + wave;
-      dma16s(sa, aof[i2], st + i * 1024);
-      dma16s(sb, bof[i2], st + kDOpB + i * 1024);
-    }
+    for (int i2 = 0; i2 < kADma; ++i2) dma16s(sa, aof[i2], st + (i2 * 8 + wave) * 1024);
+#pragma unroll
+    for (int i2 = 0; i2 < kDDmaOp; ++i2) dma16s(sb, bof[i2], st + kAOp + (i2 * 8 + wave) * 1024);
     if (++dkk == kDSteps) {
       if (dj + 1 < my_tiles) {
         dkk = 0;
@@ -389,11 +424,23 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
 #pragma unroll
   for (int s2 = 0; s2 < kSub; ++s2) {
     const int pos = dec_swz(l32, 2 * s2 + g) * 16;
-    aoff[s2] = (wm * 64 + l32) * kDRow + pos;
-    boff[s2] = kDOpB + (wn * 128 + l32) * kDRow + pos;
+    // fp8 rows: the 8 codes of k = 16 s2 + 8 g .. are half g of chunk s2
+    aoff[s2] = kFp8A ? (wm * 64 + l32) * kDRow8 + dec_swz8(l32, s2) * 16 + 8 * g : (wm * 64 + l32) * kDRow + pos;
+    boff[s2] = kAOp + (wn * 128 + l32) * kDRow + pos;
   }
 
   f32x16 acc[4][2];
+  // fp8 A: the scales of this lane's two tokens of the tile being computed,
+  // loaded in the tile's first step (after that step's DMA and the previous
+  // tile's stores, so the step waits that follow count them in order) and
+  // used by its epilogue
+  float tile_scale[2] = {1.f, 1.f};
+  auto load_scales = [&](int j) __attribute__((always_inline)) {
+    int mt, nt;
+    dec_tile(rbeg + slot + j * nslots, a.n_mt, a.n_nt, mt, nt);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) tile_scale[tb] = a.scale[min(mt * kDT + wm * 64 + tb * 32 + l32, a.M - 1)];
+  };
   auto zero = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -407,10 +454,20 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
   // each writing four whole 256-byte rows (this wavefront's 128 columns of
   // four tokens). The accumulators are regrouped through a 4 KB LDS slice per
   // wavefront, 16 tokens at a time.
-  uint8_t* ep = dlds + kDNS * kDStageB + wave * kDEpB;
+  uint8_t* ep = dlds + kDNS * kStageB + wave * kDEpB;
   auto store_tile = [&](int j) __attribute__((always_inline)) {
     int mt, nt;
     dec_tile(rbeg + slot + j * nslots, a.n_mt, a.n_nt, mt, nt);
+    if constexpr (kFp8A) {
+      // the fp32 sums of this lane's token (column l32 of token block tb)
+      // times the token's scale, before the bf16 rounding
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][tb][i] *= tile_scale[tb];
+    }
     const int n0 = nt * kDT + wn * 128;         // first column of this wavefront
     const bool is_v = n0 >= HK;
     const int hs = (is_v ? n0 - HK : n0) / kDnope;
@@ -484,12 +541,19 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
       store_tile(s / kDSteps - 1);
       zero();
     }
-    const uint8_t* st = dlds + (s & (kDNS - 1)) * kDStageB;
+    if constexpr (kFp8A)
+      if (kk == 0) load_scales(s / kDSteps);
+    const uint8_t* st = dlds + (s & (kDNS - 1)) * kStageB;
 #pragma unroll
     for (int s2 = 0; s2 < kSub; ++s2) {
       bf16x8 af[2], bf[4];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) af[tb] = *reinterpret_cast<const bf16x8*>(st + aoff[s2] + tb * 32 * kDRow);
+      for (int tb = 0; tb < 2; ++tb) {
+        if constexpr (kFp8A)
+          af[tb] = e4m3x8_to_bf16(*reinterpret_cast<const u32x2*>(st + aoff[s2] + tb * 32 * kDRow8));
+        else
+          af[tb] = *reinterpret_cast<const bf16x8*>(st + aoff[s2] + tb * 32 * kDRow);
+      }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) bf[nb] = *reinterpret_cast<const bf16x8*>(st + boff[s2] + nb * 32 * kDRow);
 #pragma unroll
@@ -537,7 +601,7 @@ extern "C" int mla_pack_weight_t(const void* w, int K, int N, void* out, void* s
   return mla_check_launch("mla_pack_weight_t");
 }
 
-extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_tokens,
+extern "C" int mla_decompress(const void* latent, int64_t ld_latent, const float* row_scale, int n_tokens,
                               const void* w_t, int H_total, int h_begin, int h_end,
                               void* k_nope, int64_t k_head_stride,
                               void* v, int64_t v_head_stride, void* stream) {
@@ -547,6 +611,8 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
               "mla_decompress: need 0 <= h_begin (%d) < h_end (%d) <= H_total (%d)", h_begin, h_end, H_total);
   if (n_tokens == 0) return MLA_OK;
   MLA_REQUIRE(latent && w_t && k_nope && v, MLA_ERR_INVALID_ARG, "mla_decompress: null pointer argument");
+  MLA_REQUIRE(!row_scale || (reinterpret_cast<uintptr_t>(row_scale) & 3u) == 0, MLA_ERR_INVALID_ARG,
+              "mla_decompress: row_scale must be 4-byte aligned");
   MLA_REQUIRE(mla_aligned16(latent) && mla_aligned16(w_t) && mla_aligned16(k_nope) && mla_aligned16(v),
               MLA_ERR_INVALID_ARG, "mla_decompress: pointers must be 16-byte aligned");
   MLA_REQUIRE(ld_latent >= kDc && ld_latent % 8 == 0, MLA_ERR_INVALID_ARG,
@@ -561,15 +627,17 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
   MLA_REQUIRE(k_head_stride >= (int64_t)n_tokens * kDnope && v_head_stride >= (int64_t)n_tokens * kDv &&
                   k_head_stride % 8 == 0 && v_head_stride % 8 == 0,
               MLA_ERR_INVALID_ARG, "mla_decompress: head strides must be >= n_tokens*128 and multiples of 8");
-  DecArgs d{static_cast<const uint16_t*>(latent), ld_latent, n_tokens,
+  DecArgs d{static_cast<const uint16_t*>(latent), ld_latent, n_tokens, row_scale,
             static_cast<const uint16_t*>(w_t), H_total, h_begin, Hsel,
             static_cast<uint16_t*>(k_nope), k_head_stride, static_cast<uint16_t*>(v), v_head_stride,
             (n_tokens + kDT - 1) / kDT, Hsel * 2 * kDnope / kDT};
   const int64_t total = (int64_t)d.n_mt * d.n_nt;
   MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_decompress: problem too large");
-  const size_t lds = (size_t)kDNS * kDStageB + 8 * kDEpB;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decompress_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+  const bool fp8 = row_scale != nullptr;
+  const size_t lds = (size_t)kDNS * (fp8 ? kDOpB8 + kDOpB : kDStageB) + 8 * kDEpB;
+  const void* kern = fp8 ? reinterpret_cast<const void*>(&decompress_kernel<true>)
+                         : reinterpret_cast<const void*>(&decompress_kernel<false>);
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
     mla_set_error("mla_decompress: cannot reserve %zu bytes of LDS", lds);
     return MLA_ERR_LAUNCH;
   }
@@ -577,8 +645,12 @@ extern "C" int mla_decompress(const void* latent, int64_t ld_latent, int n_token
   const int ncu = mla_num_cus();
   MLA_REQUIRE(ncu > 0, MLA_ERR_LAUNCH, "mla_decompress: cannot query the compute-unit count");
   const unsigned grid = (unsigned)std::min<int64_t>(total, ncu);
-  hipLaunchKernelGGL(decompress_kernel, dim3(grid), dim3(kDThreads), lds,
-                     reinterpret_cast<hipStream_t>(stream), d);
+  if (fp8)
+    hipLaunchKernelGGL(decompress_kernel<true>, dim3(grid), dim3(kDThreads), lds,
+                       reinterpret_cast<hipStream_t>(stream), d);
+  else
+    hipLaunchKernelGGL(decompress_kernel<false>, dim3(grid), dim3(kDThreads), lds,
+                       reinterpret_cast<hipStream_t>(stream), d);
   return mla_check_launch("mla_decompress");
 }
 

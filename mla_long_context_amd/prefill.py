@@ -103,15 +103,21 @@ class _DeviceStatus:
 class ChunkedPrefill(_DeviceStatus):
     """Configs with a paged context and new (extend) tokens per request."""
 
-    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True):
+    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True, fp8_mode="raw"):
+        """fp8_mode (fp8 caches): "raw" gathers the codes and scales as they
+        are and the decompression reads the codes (mla_gather_context_fp8_raw,
+        mla_decompress with row_scale); "dequant" has the gather write the
+        dequantised bf16 latent instead."""
         self.prob = prob
         self.device = device
         assert fuse_merge in ("none", "final", "all")
+        assert fp8_mode in ("raw", "dequant")
         self.fuse_merge = fuse_merge
         H = self.H = prob.H
         self.B = prob.B
         self.S = int(chunk or prob.chunk)
         self.cache_dtype = L.DTYPE_BF16 if prob.cache_dtype == "bf16" else L.DTYPE_FP8_E4M3
+        self.fp8_raw = prob.cache_dtype == "fp8" and fp8_mode == "raw"
         self.pool = upload_pool(prob, device)
         self.bt = _i32(prob.block_table, device)
         self.ext = _bf16(prob.ext_latent, device)
@@ -159,6 +165,8 @@ class ChunkedPrefill(_DeviceStatus):
         self.max_tok = max([ch["n"] for ch in self.chunks] + [self.ext_off + self.T, 1])
         lat_rows = max(off, 1) if self.gather_once else max_ctx_tok
         self.lat_ws = torch.empty((lat_rows, D_LAT), dtype=torch.bfloat16, device=device)
+        # raw fp8 records: codes in the rows' first 512 bytes, scales here
+        self.scale_ws = torch.empty(lat_rows, dtype=torch.float32, device=device) if self.fp8_raw else None
         self.k_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
         self.v_ws = torch.empty((H, self.max_tok, D_V), dtype=torch.bfloat16, device=device)
         self.hstride = self.max_tok * D_V
@@ -173,25 +181,34 @@ class ChunkedPrefill(_DeviceStatus):
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
 
     # one step of the path per call
+    def _gather(self, bt, start, ln, cu, batch, max_len, stream):
+        if self.fp8_raw:
+            L.mla_gather_context_fp8_raw(self.pool, self.prob.num_blocks, bt, bt.shape[1], start, ln, cu, batch,
+                                         max_len, self.lat_ws, self.scale_ws, self.dev_status, stream)
+        else:
+            L.mla_gather_context(self.pool, self.cache_dtype, self.prob.num_blocks, bt, bt.shape[1], start, ln,
+                                 cu, batch, max_len, self.lat_ws, self.dev_status, stream)
+
     def gather(self, ch, stream=None):
         """The records of chunk ch (when they are not gathered all at once)."""
-        L.mla_gather_context(self.pool, self.cache_dtype, self.prob.num_blocks, self.bt,
-                             self.bt.shape[1], ch["start"], ch["len"], ch["cu"], self.B,
-                             ch["max_len"], self.lat_ws, self.dev_status, stream)
+        self._gather(self.bt, ch["start"], ch["len"], ch["cu"], self.B, ch["max_len"], stream)
 
     def gather_all(self, stream=None):
         """Every chunk's records in one launch (chunk c's from row lat_off)."""
-        L.mla_gather_context(self.pool, self.cache_dtype, self.prob.num_blocks, self.g_bt,
-                             self.g_bt.shape[1], self.g_start, self.g_len, self.g_cu, self.g_batch,
-                             self.g_max, self.lat_ws, self.dev_status, stream)
+        self._gather(self.g_bt, self.g_start, self.g_len, self.g_cu, self.g_batch, self.g_max, stream)
 
     def _lat(self, ch):
         # device address of chunk ch's first record in the latent workspace
         return self.lat_ws.data_ptr() + ch["lat_off"] * D_LAT * 2
 
-    def decompress(self, latent, n, stream=None, off=0):
-        """k_nope / v of n tokens into the workspaces from token `off` on."""
-        L.mla_decompress(latent, D_LAT, n, self.w_t, self.H, 0, self.H, self._at(self.k_ws, off),
+    def _scale(self, ch):
+        # device address of chunk ch's first scale (raw fp8 records), or None
+        return None if not self.fp8_raw else self.scale_ws.data_ptr() + ch["lat_off"] * 4
+
+    def decompress(self, latent, n, stream=None, off=0, row_scale=None):
+        """k_nope / v of n tokens into the workspaces from token `off` on
+        (row_scale: the rows hold fp8 codes, see mla_decompress)."""
+        L.mla_decompress(latent, D_LAT, row_scale, n, self.w_t, self.H, 0, self.H, self._at(self.k_ws, off),
                          self.hstride, self._at(self.v_ws, off), self.hstride, stream)
 
     @staticmethod
@@ -259,7 +276,7 @@ class ChunkedPrefill(_DeviceStatus):
                     self.gather(ch, stream)
             lat = self._lat(ch)
             with _span(timer, "decompress"):
-                self.decompress(lat, ch["n"], stream)
+                self.decompress(lat, ch["n"], stream, row_scale=self._scale(ch))
             if self.two_seg and ci == len(self.chunks) - 1:
                 with _span(timer, "decompress"):
                     self.decompress(self.ext, self.T, stream, off=self.ext_off)
@@ -322,7 +339,7 @@ class ChunkedPrefill(_DeviceStatus):
             ext_attn_flops=0 if self.two_seg else 640 * H * ext_pairs,
             last_attn_flops=640 * H * (last_pairs + ext_pairs) if self.two_seg else 0,
             gather_tokens=int(C.sum()),
-            gather_bytes=int(C.sum()) * (2304 if p.cache_dtype == "bf16" else 644 + 1152),
+            gather_bytes=int(C.sum()) * (2304 if p.cache_dtype == "bf16" else 644 + (644 if self.fp8_raw else 1152)),
             new_tokens=int(E.sum()), ctx_tokens=int(C.sum()), merges=n_merge,
         )
 
@@ -574,7 +591,7 @@ class ReusePrefill(_DeviceStatus):
                                      self.dev_status, stream)
             if self.kv_h0 < H:
                 with _span(timer, "decompress"):
-                    L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, H, self.kv_h0, H, self.k_ws,
+                    L.mla_decompress(self.lat_ws, D_LAT, None, ch["n"], self.w_t, H, self.kv_h0, H, self.k_ws,
                                      self.hstride, self.v_ws, self.hstride, stream)
             if HG > 0 and T > 0:
                 with _span(timer, "attn_global"):
@@ -774,7 +791,7 @@ class ArtifactBuilder(_DeviceStatus):
             if self.HL == 0:
                 continue
             with _span(timer, "decompress"):
-                L.mla_decompress(self.lat_ws, D_LAT, ch["n"], self.w_t, self.H, 0, self.HL, self.k_ws,
+                L.mla_decompress(self.lat_ws, D_LAT, None, ch["n"], self.w_t, self.H, 0, self.HL, self.k_ws,
                                  self.hstride, self.v_ws, self.hstride, stream)
             n_after = self.R - ch["a0"]
             if n_after > 0:

@@ -135,6 +135,23 @@ def gather_fp8_f64(pool: np.ndarray, block_table: np.ndarray, req: int,
     return out
 
 
+def gather_fp8_raw(pool: np.ndarray, block_table: np.ndarray, req: int, start: int, length: int):
+    """The stored parts of an fp8 cache's records for tokens [start,
+    start+length) of a request, as they are in the blocks (layout reading
+    R16): codes uint8 [length, 512], k_rope bf16 bits [length, 64], scales
+    fp32 [length]. A gather that leaves dequantisation to the decompression
+    copies exactly these ([DSMLA] 4.4 step 1 with the fp8 storage of 2.2)."""
+    t = np.arange(start, start + length)
+    blk, slot = token_to_slot(block_table, req, t)
+    rows = pool[blk]
+    codes = rows[np.arange(length)[:, None], slot[:, None] * D_C + np.arange(D_C)[None, :]]
+    rope = np.ascontiguousarray(rows[:, FP8_ROPE_OFF:FP8_SCALE_OFF].reshape(length, BLOCK, D_ROPE * 2)
+                                [np.arange(length), slot]).view(np.uint16)
+    sc = np.ascontiguousarray(rows[:, FP8_SCALE_OFF:].reshape(length, BLOCK, 4)[np.arange(length), slot]).view(
+        np.float32)[:, 0]
+    return codes, rope, sc
+
+
 def gather_fp8_expected_bits(pool, block_table, req, start, length) -> np.ndarray:
     """The bf16 record a gather that dequantises an fp8 cache must write,
     bit for bit (reading R17): c_kv = bf16_rne(fp32_rne(decode(code) *

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
 
 
 def _err(fn, *args):
@@ -58,15 +58,20 @@ def test_gather_validation(lib):
 
 
 def test_decompress_validation(lib):
-    code, _ = _err(mla.mla_decompress, FAKE, 576, 10, FAKE, 8, 3, 3, FAKE, 1280, FAKE, 1280)
+    code, _ = _err(mla.mla_decompress, FAKE, 576, None, 10, FAKE, 8, 3, 3, FAKE, 1280, FAKE, 1280)
     assert code == _lib.MLA_ERR_INVALID_ARG                      # empty head range
-    code, _ = _err(mla.mla_decompress, FAKE, 576, 10, FAKE, 8, 0, 9, FAKE, 1280, FAKE, 1280)
+    code, _ = _err(mla.mla_decompress, FAKE, 576, None, 10, FAKE, 8, 0, 9, FAKE, 1280, FAKE, 1280)
     assert code == _lib.MLA_ERR_INVALID_ARG                      # h_end > H
-    code, _ = _err(mla.mla_decompress, FAKE, 500, 10, FAKE, 8, 0, 8, FAKE, 1280, FAKE, 1280)
+    code, _ = _err(mla.mla_decompress, FAKE, 500, None, 10, FAKE, 8, 0, 8, FAKE, 1280, FAKE, 1280)
     assert code == _lib.MLA_ERR_INVALID_ARG                      # ld < 512
-    code, _ = _err(mla.mla_decompress, FAKE, 576, 10, FAKE, 8, 0, 8, FAKE, 1000, FAKE, 1280)
+    code, _ = _err(mla.mla_decompress, FAKE, 576, None, 10, FAKE, 8, 0, 8, FAKE, 1000, FAKE, 1280)
     assert code == _lib.MLA_ERR_INVALID_ARG                      # head stride too small
-    assert mla.mla_decompress(None, 576, 0, None, 8, 0, 8, None, 0, None, 0, stream=0) == 0
+    code, _ = _err(mla.mla_decompress, FAKE, 576, FAKE + 2, 10, FAKE, 8, 0, 8, FAKE, 1280, FAKE, 1280)
+    assert code == _lib.MLA_ERR_INVALID_ARG                      # misaligned row_scale
+    assert mla.mla_decompress(None, 576, None, 0, None, 8, 0, 8, None, 0, None, 0, stream=0) == 0
+    code, msg = _err(mla.mla_gather_context_fp8_raw, FAKE, 4, FAKE, 4, FAKE, FAKE, FAKE, 1, 64, FAKE, None, None)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "null" in msg    # no scale output
+    assert mla.mla_gather_context_fp8_raw(None, 0, None, 0, None, None, None, 0, 0, None, None, stream=0) == 0
 
 
 def test_attn_validation(lib):

@@ -294,7 +294,7 @@ def test_decompress(H, h0, h1, n):
     hst = (n + 3) * 128
     k = torch.zeros((Hs, n + 3, 128), dtype=torch.bfloat16, device="cuda")
     v = torch.zeros((Hs, n + 3, 128), dtype=torch.bfloat16, device="cuda")
-    mla.mla_decompress(bf16_dev(lat), 576, n, w_t, H, h0, h1, k, hst, v, hst)
+    mla.mla_decompress(bf16_dev(lat), 576, None, n, w_t, H, h0, h1, k, hst, v, hst)
     torch.cuda.synchronize()
     # packing itself is exact
     assert np.array_equal(bits(w_t), W.T)
@@ -312,6 +312,110 @@ def test_decompress(H, h0, h1, n):
             bad = np.abs(g - ref) > bound
             assert not bad.any(), f"{name} head {h}: {int(bad.sum())} elements beyond the rounding bound"
         assert np.all(f64(k[hs, n:]) == 0) and np.all(f64(v[hs, n:]) == 0)   # no write past n
+
+
+def _fp8_rows(rng, n, codes_kind):
+    """n latent rows of 1152 bytes whose first 512 bytes are E4M3FN codes
+    (every finite code, or random finite codes), rope elements 512..575 bf16,
+    bytes 512..1023 poisoned (0xFF: NaN codes, never to be read), and fp32
+    scales."""
+    rows = np.full((n, 1152), 0xFF, dtype=np.uint8)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    if codes_kind == "all":
+        codes = np.stack([np.roll(np.resize(finite, 512), 5 * i) for i in range(n)])
+    else:
+        codes = rng.choice(finite, size=(n, 512))
+    rows[:, :512] = codes
+    rows[:, 1024:] = np.frombuffer(mi.f32_to_bf16_bits(rng.standard_normal((n, 64)).astype(np.float32)).tobytes(),
+                                   dtype=np.uint8).reshape(n, 128)
+    scales = (np.exp(rng.uniform(-6, 2, size=n)) / 448).astype(np.float32)
+    return rows, codes, scales
+
+
+@pytest.mark.parametrize("H,h0,h1,n", [(4, 0, 4, 300), (16, 3, 14, 8300)])
+def test_decompress_fp8_rows(H, h0, h1, n):
+    """mla_decompress with row_scale: the A rows are E4M3FN codes and the
+    scale multiplies the fp32 sums. Random weights: the bar and the
+    per-element rounding bound against the exact dequantised product."""
+    require_gpu()
+    say(f"decompress fp8 rows H={H} heads [{h0},{h1}) n={n}")
+    rng = np.random.default_rng(46)
+    rows, codes, scales = _fp8_rows(rng, n, "random")
+    W = mi.f32_to_bf16_bits((rng.standard_normal((512, H * 256)) / math.sqrt(512)).astype(np.float32))
+    w_t = pf.pack_weight(W, "cuda")
+    Hs = h1 - h0
+    hst = (n + 3) * 128
+    k = torch.zeros((Hs, n + 3, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((Hs, n + 3, 128), dtype=torch.bfloat16, device="cuda")
+    mla.mla_decompress(torch.from_numpy(rows).cuda(), 576, torch.from_numpy(scales).cuda(), n, w_t, H, h0, h1,
+                       k, hst, v, hst)
+    torch.cuda.synchronize()
+    Wf = orc.bf16_to_f64(W)
+    C = orc.e4m3fn_to_f64(codes) * scales.astype(np.float64)[:, None]
+    for hs, h in enumerate(range(h0, h1)):
+        kr, vr = orc.decompress_head(C, Wf, H, h)
+        ka, va = orc.decompress_head(np.abs(C), np.abs(Wf), H, h)
+        for name, got, ref, absum in (("k", k, kr, ka), ("v", v, vr, va)):
+            g = f64(got[hs, :n])
+            check_out(g, ref, what=f"{name} head {h}")
+            # fp32 sum of the exact products, one fp32 product with the
+            # scale, one bf16 rounding
+            bound = U_BF16 * np.abs(ref) + 1.01 * (GAMMA_512 + 2.0 ** -24) * absum
+            bad = np.abs(g - ref) > bound
+            assert not bad.any(), f"{name} head {h}: {int(bad.sum())} elements beyond the rounding bound"
+        assert np.all(f64(k[hs, n:]) == 0) and np.all(f64(v[hs, n:]) == 0)
+
+
+def test_decompress_fp8_rows_exact():
+    """Every finite E4M3FN code through a selection kv_b_proj: each output is
+    one code times a power of two times the scale, which the GPU rounds to
+    fp32 once and to bf16 once; the oracle does the same two roundings."""
+    require_gpu()
+    rng = np.random.default_rng(47)
+    H, n = 4, 200
+    rows, codes, scales = _fp8_rows(rng, n, "all")
+    W = mi.selection_kv_b_proj(rng, H)
+    w_t = pf.pack_weight(W, "cuda")
+    k = torch.empty((H, n, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((H, n, 128), dtype=torch.bfloat16, device="cuda")
+    mla.mla_decompress(torch.from_numpy(rows).cuda(), 576, torch.from_numpy(scales).cuda(), n, w_t, H, 0, H,
+                       k, n * 128, v, n * 128)
+    torch.cuda.synchronize()
+    Wf = orc.bf16_to_f64(W)
+    Cx = orc.e4m3fn_to_f64(codes)                 # code values: the products with W are exact
+    for h in range(H):
+        kr, vr = orc.decompress_head(Cx, Wf, H, h)
+        for name, got, ref in (("k", k, kr), ("v", v, vr)):
+            exp = orc.f32_to_bf16_bits_rne(orc.f64_to_f32_rne(ref * scales.astype(np.float64)[:, None]))
+            # equal values (a zero's sign depends on the order of the zero terms)
+            assert np.array_equal(f64(got[h]), orc.bf16_to_f64(exp)), f"{name} head {h}"
+
+
+def test_gather_fp8_raw_bit_exact():
+    require_gpu()
+    prob = mi.make_problem(4, [256, 64 * 7, 0, 128], [1, 1, 1, 1], 128, "fp8", seed=41, extra_blocks=5, poison=True)
+    pool = pf.upload_pool(prob, "cuda")
+    bt = _i32(prob.block_table)
+    starts = np.array([3, 70, 0, 64]); lens = np.array([250, 301, 0, 64])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    out = torch.full((int(cu[-1]) + 1, 576), -7.0, dtype=torch.bfloat16, device="cuda")
+    sc = torch.full((int(cu[-1]) + 1,), -3.0, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mla.mla_gather_context_fp8_raw(pool, prob.num_blocks, bt, bt.shape[1], _i32(starts), _i32(lens), _i32(cu), 4,
+                                   int(lens.max()), out, sc, status)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.uint8).numpy()          # [rows, 1152] bytes
+    gs = sc.cpu().numpy()
+    for r in range(4):
+        codes, rope, scl = orc.gather_fp8_raw(prob.pool, prob.block_table, r, int(starts[r]), int(lens[r]))
+        rows = slice(cu[r], cu[r + 1])
+        assert np.array_equal(got[rows, :512], codes), f"request {r} codes"
+        assert np.array_equal(got[rows, 1024:].view(np.uint16), rope), f"request {r} rope"
+        assert np.array_equal(gs[rows].view(np.uint32), scl.view(np.uint32)), f"request {r} scales"
+        # bytes 512..1023 are not written
+        assert np.all(got[rows, 512:1024].view(np.uint16) == bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0])
+    assert np.all(f64(out[-1]) == -7.0) and gs[-1] == -3.0
+    assert int(status.item()) == 0
 
 
 # ---------------------------------------------------------------- attention

@@ -116,17 +116,19 @@ def test_ragged_multichunk_bf16(chunk, fuse, two_seg, weights):
     _compare_chunked(prob, pre, exact=weights == "selection")
 
 
-@pytest.mark.parametrize("exact", [True, False])
-def test_ragged_multichunk_fp8(exact):
+@pytest.mark.parametrize("exact,mode", [(True, "raw"), (False, "raw"), (True, "dequant"), (False, "dequant")])
+def test_ragged_multichunk_fp8(exact, mode):
     """exact: selection kv_b_proj and records whose scale is 2^-6, so every
     dequantised latent and decompressed key is exact in bf16 and every row is
     held to the bar; otherwise random weights and scales, with the derived
-    bound for the few-key rows."""
+    bound for the few-key rows. mode: the decompression reads the fp8 codes
+    (raw, the default) or the gather dequantises them."""
     require_gpu()
-    say(f"ragged fp8 exact={exact}")
+    say(f"ragged fp8 exact={exact} mode={mode}")
     prob = mi.make_problem(4, [64 * 11, 128, 0], [40, 257, 3], 256, "fp8", seed=72,
                            weights="selection" if exact else "normal", exact_dequant=exact)
-    pre = ChunkedPrefill(prob)
+    pre = ChunkedPrefill(prob, fp8_mode=mode)
+    assert pre.fp8_raw == (mode == "raw")
     _run(pre)
     _compare_chunked(prob, pre, exact=exact)
     _compare_chunked(prob, pre, rl2=FP8_REL_L2, exact=exact)

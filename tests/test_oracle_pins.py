@@ -715,3 +715,25 @@ def test_artifact_for_request_rows_equals_their_full_recompute():
     WaL, WaG, Wb = (orc.bf16_to_f64(x) for x in (prob.WaL, prob.WaG, prob.Wb))
     y = orc.head_partition_merge(O_L, full["O_G"], WaL, WaG, Wb)
     np.testing.assert_allclose(y, full["y"], rtol=1e-9, atol=1e-12)
+
+
+def test_fp8_raw_gather_is_the_stored_record():
+    """The raw fp8 gather's three parts are the bytes the block layout puts
+    at each token: decoding the codes times the scale gives the dequantised
+    c_kv of gather_fp8_f64 exactly, and the rope bits are the same; by brute
+    force over the byte offsets of reading R16."""
+    import mla_inputs as mi
+    prob = mi.make_problem(2, [192, 64 * 5], [1, 1], 128, "fp8", seed=13, extra_blocks=2)
+    for r, (s0, n) in enumerate([(5, 150), (64, 256)]):
+        codes, rope, sc = orc.gather_fp8_raw(prob.pool, prob.block_table, r, s0, n)
+        x = orc.gather_fp8_f64(prob.pool, prob.block_table, r, s0, n)
+        assert np.array_equal(orc.e4m3fn_to_f64(codes) * sc.astype(np.float64)[:, None], x[:, :512])
+        assert np.array_equal(orc.bf16_to_f64(rope), x[:, 512:])
+        for i in (0, n // 2, n - 1):
+            t = s0 + i
+            blk = prob.block_table[r, t // 64]
+            base = prob.pool[blk]
+            slot = t % 64
+            assert np.array_equal(codes[i], base[slot * 512:(slot + 1) * 512])
+            assert rope[i].tobytes() == base[32768 + slot * 128:32768 + (slot + 1) * 128].tobytes()
+            assert sc[i].tobytes() == base[40960 + slot * 4:40960 + slot * 4 + 4].tobytes()
