@@ -209,12 +209,18 @@ def step_stats(step_ms):
     return {"median_ms_per_step": round(statistics.median(step_ms), 4), "min_ms_per_step": round(min(step_ms), 4)}
 
 
-def gemm_reference(torch, n=8192, reps=10):
+def gemm_reference(torch, n=8192, reps=10, zeros=False):
     """The bf16 rate of the vendor GEMM (torch.matmul, hipBLASLt) on an
     n x n x n product on this GPU: a measured ceiling for MFMA kernels at the
-    clock the GPU sustains under load, beside the published peak."""
-    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    clock the GPU sustains under load, beside the published peak. zeros: the
+    same product on all-zero operands (the clock the GPU holds when the matrix
+    cores' data does not toggle)."""
+    if zeros:
+        a = torch.zeros(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.zeros(n, n, device="cuda", dtype=torch.bfloat16)
+    else:
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
     for _ in range(3):
         c = a @ b
     torch.cuda.synchronize()
@@ -226,7 +232,8 @@ def gemm_reference(torch, n=8192, reps=10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del a, b, c
-    return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
+    return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt){', zero operands' if zeros else ''}",
+            "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
 
 
 def mfma_calibration(torch):
@@ -248,6 +255,41 @@ def mfma_calibration(torch):
     if lib.mla_calib_mfma_bf16(out.data_ptr(), wgs, 20000, 3, ctypes.byref(r)) != 0:
         return None
     return {"op": "independent v_mfma_f32_32x32x16_bf16 chains, 16 wavefronts per CU", "tflops": round(r.value, 1)}
+
+
+def mfma_feed_calibration(torch):
+    """The products of the attention loop's feed pattern without its data
+    dependences (libmla_calib.so, mla_calib_mfma_fed): A operands from
+    registers, from LDS at 1 KB per product, from LDS with a softmax's worth
+    of independent VALU work, and from LDS with random operand bits (the
+    matrix cores draw more power on toggling data, and the clock follows), at
+    one and two wavefronts per SIMD. Each
+    rate is also given as a fraction of the register-operand rate at two
+    wavefronts per SIMD."""
+    import ctypes
+    path = os.path.join(ROOT, "mla_long_context_amd", "libmla_calib.so")
+    if not os.path.exists(path):
+        raise SystemExit("libmla_calib.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.mla_calib_mfma_fed.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.mla_calib_mfma_fed.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(2 * cus * 256, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    names = {0: "A from registers", 1: "A from LDS, 1 KB per product", 2: "A from LDS + independent softmax VALU",
+             3: "A from LDS, 1 KB per product, random operand bits"}
+    rows = []
+    for per_cu in (1, 2):
+        for mode in (0, 1, 2, 3):
+            r = ctypes.c_double(0.0)
+            if lib.mla_calib_mfma_fed(out.data_ptr(), per_cu * cus, mode, 2000, 4, ctypes.byref(r)) != 0:
+                raise SystemExit("mla_calib_mfma_fed failed")
+            rows.append({"feed": names[mode], "wavefronts_per_simd": per_cu, "tflops": round(r.value, 1)})
+    ref = next(x["tflops"] for x in rows if x["wavefronts_per_simd"] == 2 and x["feed"] == names[0])
+    for x in rows:
+        x["of_register_rate"] = round(x["tflops"] / ref, 3)
+    return rows
 
 
 # ---------------------------------------------------------------- the oracle on the host's cores
@@ -660,6 +702,8 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="device buffer (MB) overwritten before every timed step, outside its events, "
                          "so the Infinity Cache holds nothing of the previous step (0: off)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="only measure the MFMA rate under the attention loop's operand feed (calibration library)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy kernel (for HBM counter scaling)")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
@@ -676,6 +720,12 @@ def main():
               "(how the path would shard is described in the design notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_mfma:
+        import torch
+        print(json.dumps({"mfma_feed": mfma_feed_calibration(torch), "mfma_sustained": mfma_calibration(torch),
+                          "gemm_reference": [gemm_reference(torch), gemm_reference(torch, zeros=True)]}))
+        return
 
     if args.calibrate_copy:
         import torch
