@@ -423,10 +423,16 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
   int aoff[kSub], boff[kSub];
 #pragma unroll
   for (int s2 = 0; s2 < kSub; ++s2) {
-    const int pos = dec_swz(l32, 2 * s2 + g) * 16;
-    // fp8 rows: the 8 codes of k = 16 s2 + 8 g .. are half g of chunk s2
-    aoff[s2] = kFp8A ? (wm * 64 + l32) * kDRow8 + dec_swz8(l32, s2) * 16 + 8 * g : (wm * 64 + l32) * kDRow + pos;
-    boff[s2] = kAOp + (wn * 128 + l32) * kDRow + pos;
+    // bf16 rows: sub-step s2 takes k = 16 s2 + 8 g .. + 7 in lane half g.
+    // fp8 rows: lane half g reads all 16 codes of chunk (s2 & ~1) + g with
+    // one 16-byte read (8-byte reads of half a chunk use half the banks and
+    // conflict two ways); codes 0-7 feed sub-step s2 & ~1, codes 8-15 the
+    // next one, so sub-step s2 takes k = 16 ((s2 & ~1) + g) + 8 (s2 & 1) ..
+    // + 7, and the weight fragments are read for the same k.
+    const int bchunk = kFp8A ? 2 * ((s2 & ~1) + g) + (s2 & 1) : 2 * s2 + g;
+    aoff[s2] = kFp8A ? (wm * 64 + l32) * kDRow8 + dec_swz8(l32, (s2 & ~1) + g) * 16
+                     : (wm * 64 + l32) * kDRow + dec_swz(l32, 2 * s2 + g) * 16;
+    boff[s2] = kAOp + (wn * 128 + l32) * kDRow + dec_swz(l32, bchunk) * 16;
   }
 
   f32x16 acc[4][2];
@@ -544,15 +550,18 @@ __global__ __launch_bounds__(kDThreads, 1) void decompress_kernel(DecArgs a) {
     if constexpr (kFp8A)
       if (kk == 0) load_scales(s / kDSteps);
     const uint8_t* st = dlds + (s & (kDNS - 1)) * kStageB;
+    u32x4 a16[2];                              // fp8: the 16 codes of two sub-steps
 #pragma unroll
     for (int s2 = 0; s2 < kSub; ++s2) {
       bf16x8 af[2], bf[4];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        if constexpr (kFp8A)
-          af[tb] = e4m3x8_to_bf16(*reinterpret_cast<const u32x2*>(st + aoff[s2] + tb * 32 * kDRow8));
-        else
+        if constexpr (kFp8A) {
+          if ((s2 & 1) == 0) a16[tb] = *reinterpret_cast<const u32x4*>(st + aoff[s2] + tb * 32 * kDRow8);
+          af[tb] = e4m3x8_to_bf16((s2 & 1) ? u32x2{a16[tb].z, a16[tb].w} : u32x2{a16[tb].x, a16[tb].y});
+        } else {
           af[tb] = *reinterpret_cast<const bf16x8*>(st + aoff[s2] + tb * 32 * kDRow);
+        }
       }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) bf[nb] = *reinterpret_cast<const bf16x8*>(st + boff[s2] + nb * 32 * kDRow);
