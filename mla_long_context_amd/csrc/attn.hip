@@ -118,7 +118,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   int qt = j % a.n_qt;
   const int hs = bh % a.Hsel;
   const int b = bh / a.Hsel;
-  if (kCausal) qt = a.n_qt - 1 - qt;   // longest rows first
+  // longest rows first: later row tiles see more keys of a causal segment
+  if (kCausal || kSeg2) qt = a.n_qt - 1 - qt;
 
   const int q0 = a.cu_q[b];
   const int n_q = a.cu_q[b + 1] - q0;
