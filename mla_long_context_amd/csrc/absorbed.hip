@@ -163,12 +163,18 @@ __global__ __launch_bounds__(kAW * 64, 1) void absorbed_attn_kernel(AbsAttnArgs 
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  // row tiles of one piece stay on one XCD (they share the piece's keys);
-  // pieces are dealt to the XCDs round-robin
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int pc = (j / a.n_rt) * 8 + xcd;
-  if (pc >= a.pieces) return;
-  const int rt = j % a.n_rt;
+  // Work items (piece, row tile), piece-major, are dealt to the 8 XCDs
+  // (workgroup b runs on XCD b % 8) in contiguous ranges of equal size: the
+  // row tiles of a piece share its keys in one XCD's L2 except where a range
+  // boundary cuts the piece (a piece whose row tiles fit in a range lies on
+  // at most two XCDs), and a launch of at most one workgroup per compute
+  // unit runs in a single round whatever the piece count.
+  const int n_items = a.pieces * a.n_rt;
+  const int per_xcd = (n_items + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + slot;
+  if (slot >= per_xcd || item >= n_items) return;
+  const int pc = item / a.n_rt, rt = item % a.n_rt;
   const int k0 = a.cu_k[pc];
   const int n_k = a.cu_k[pc + 1] - k0;
   const int row = rt * kARows + wave * 32 + l32;
@@ -424,7 +430,7 @@ extern "C" int mla_absorbed_attn(const void* q_abs, int R, const void* latent, i
               "mla_absorbed_attn: ld_latent (%lld) must be a multiple of 8 and >= 576", (long long)ld_latent);
   MLA_REQUIRE(scale > 0.f && scale < 1e30f, MLA_ERR_INVALID_ARG, "mla_absorbed_attn: scale must be positive");
   const int n_rt = (R + kARows - 1) / kARows;
-  const int64_t total = ((int64_t)pieces + 7) / 8 * 8 * n_rt;
+  const int64_t total = ((int64_t)pieces * n_rt + 7) / 8 * 8;   // 8 equal per-XCD ranges of work items
   MLA_REQUIRE(total < (int64_t)1 << 31, MLA_ERR_INVALID_ARG, "mla_absorbed_attn: problem too large");
   AbsAttnArgs a{static_cast<const uint16_t*>(q_abs), R, static_cast<const uint16_t*>(latent), ld_latent,
                 cu_k, pieces, n_rt, scale * kLog2e, out_lat, lse4};

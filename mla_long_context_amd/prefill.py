@@ -366,7 +366,7 @@ class ReusePrefill(_DeviceStatus):
     equals the chunk-by-chunk merge."""
 
     def __init__(self, prob, device="cuda", chunk=None, split=4096, local_path="absorbed",
-                 split_local=8192, artifact=None, request=None, merge="one_pass"):
+                 split_local=None, artifact=None, request=None, merge="one_pass"):
         assert prob.is_reuse
         assert local_path in ("absorbed", "decompressed")
         assert merge in ("one_pass", "tree")
@@ -400,9 +400,20 @@ class ReusePrefill(_DeviceStatus):
         self.HL, self.HG = prob.n_local, H - prob.n_local
         self.S = int(chunk or prob.chunk)
         self.split = max(64, int(split) // 64 * 64)
-        # the absorbed Local rows fill the GPU with fewer, longer pieces (56
-        # row tiles per piece at 56 heads x 64 rows): fewer partial states
-        self.split_L = max(64, int(split_local) // 64 * 64) if local_path == "absorbed" else self.split
+        # The absorbed Local rows take 128 (row, head) pairs per workgroup and
+        # one workgroup per compute unit (its LDS ring fills most of a CU).
+        # By default a chunk is cut into as many pieces as fill the GPU in one
+        # round with its row tiles, floor(CUs / row tiles), of at least 2048
+        # keys each; split_local (keys per piece) overrides.
+        if local_path == "absorbed":
+            if split_local is None:
+                n_rt = -(-(len(prot_rows) * prob.n_local) // 128)
+                cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+                per_chunk = max(1, cus // max(n_rt, 1))
+                split_local = max(2048, -(-(-(-self.S // per_chunk)) // 64) * 64)
+            self.split_L = max(64, int(split_local) // 64 * 64)
+        else:
+            self.split_L = self.split
         # documents: each its own pool and block table, canonical positions,
         # request offset delta (RedKnot-MLA section 2: segmented reuse; the
         # per-document states merge like the pieces of one document)

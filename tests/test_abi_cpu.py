@@ -264,6 +264,36 @@ def test_absorbed_dma_stays_inside_the_piece(n_k):
     assert keys == set(range(n_k))
 
 
+def _absorbed_items(pieces, n_rt):
+    """Host model of the absorbed-attention launch: the grid is the work
+    items (piece, row tile) rounded up to 8 equal per-XCD ranges; workgroup b
+    (XCD b % 8, slot b // 8) takes item (b % 8) * per_xcd + b // 8 when that
+    is an item."""
+    n_items = pieces * n_rt
+    per_xcd = (n_items + 7) // 8
+    grid = per_xcd * 8
+    taken = []
+    for b in range(grid):
+        slot, item = b >> 3, (b & 7) * per_xcd + (b >> 3)
+        if slot < per_xcd and item < n_items:
+            taken.append((item // n_rt, item % n_rt, b & 7))
+    return taken
+
+
+@pytest.mark.parametrize("pieces,n_rt", [(1, 1), (1, 28), (8, 28), (9, 28), (36, 28), (3, 5), (17, 1), (2, 129)])
+def test_absorbed_work_items_each_once(pieces, n_rt):
+    taken = _absorbed_items(pieces, n_rt)
+    pairs = [(p, r) for p, r, _ in taken]
+    assert sorted(pairs) == [(p, r) for p in range(pieces) for r in range(n_rt)]
+    # no XCD gets more than its equal share, and a piece whose row tiles fit
+    # in one XCD's range lies on at most two XCDs
+    per_xcd = (pieces * n_rt + 7) // 8
+    assert max(sum(1 for *_, x in taken if x == k) for k in range(8)) <= per_xcd
+    if n_rt <= per_xcd:
+        for p in range(pieces):
+            assert len({x for q, _, x in taken if q == p}) <= 2
+
+
 def test_noalloc_merge_rejects_sizes_beyond_its_scratch(lib):
     # T * d_mid above 4194304 bf16 elements is refused before anything else
     code, msg = _err(mla.mla_head_partition_merge_noalloc, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2049, 7, 1,
