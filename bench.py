@@ -263,16 +263,16 @@ def mfma_feed_calibration(torch):
     registers, from LDS at 1 KB per product, from LDS with a softmax's worth
     of independent VALU work, and from LDS with random operand bits (the
     matrix cores draw more power on toggling data, and the clock follows), at
-    one and two wavefronts per SIMD. Each
-    rate is also given as a fraction of the register-operand rate at two
-    wavefronts per SIMD."""
+    one workgroup per CU (one wavefront per SIMD) and two. Each rate is also
+    given as a fraction of the register-operand rate at two wavefronts per
+    SIMD."""
     import ctypes
     path = os.path.join(ROOT, "mla_long_context_amd", "libmla_calib.so")
     if not os.path.exists(path):
         raise SystemExit("libmla_calib.so is not built (run __graft_entry__.build())")
     lib = ctypes.CDLL(path)
     lib.mla_calib_mfma_fed.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.POINTER(ctypes.c_double)]
+                                       ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.mla_calib_mfma_fed.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(2 * cus * 256, dtype=torch.float32, device="cuda")
@@ -283,7 +283,8 @@ def mfma_feed_calibration(torch):
     for per_cu in (1, 2):
         for mode in (0, 1, 2, 3):
             r = ctypes.c_double(0.0)
-            if lib.mla_calib_mfma_fed(out.data_ptr(), per_cu * cus, mode, 2000, 4, ctypes.byref(r)) != 0:
+            if lib.mla_calib_mfma_fed(out.data_ptr(), per_cu * cus, mode, 2000, 4, int(per_cu == 1),
+                                      ctypes.byref(r)) != 0:
                 raise SystemExit("mla_calib_mfma_fed failed")
             rows.append({"feed": names[mode], "wavefronts_per_simd": per_cu, "tflops": round(r.value, 1)})
     ref = next(x["tflops"] for x in rows if x["wavefronts_per_simd"] == 2 and x["feed"] == names[0])

@@ -135,21 +135,31 @@ extern "C" int mla_calib_mfma_bf16(float* out, int workgroups, int iters, int re
 // mode 0: A operand from registers; 1: A operand from LDS, 1 KB per product;
 // 2: as 1 plus the independent VALU work; 3: as 1 with random operand bits
 // (random signs and mantissas, as real data has) instead of near-constant
-// ones. out: device float buffer of
-// workgroups * 256 elements (caller owned). Returns 0, or -1 on bad
-// arguments or a HIP error.
-extern "C" int mla_calib_mfma_fed(float* out, int workgroups, int mode, int iters, int reps, double* tflops) {
+// ones. exclusive != 0 adds 40 KB of unused dynamic LDS to each workgroup so
+// that no two share a CU (one wavefront per SIMD); otherwise two fit in a
+// CU's 160 KB. out: device float buffer of workgroups * 256 elements (caller
+// owned). Returns 0, or -1 on bad arguments or a HIP error.
+extern "C" int mla_calib_mfma_fed(float* out, int workgroups, int mode, int iters, int reps, int exclusive,
+                                  double* tflops) {
   if (!out || !tflops || workgroups <= 0 || iters <= 0 || reps <= 0 || mode < 0 || mode > 3) return -1;
+  const unsigned dyn = exclusive ? 40u * 1024u : 0u;
+  if (exclusive) {
+    const void* kerns[4] = {reinterpret_cast<const void*>(&mfma_fed<0, false>),
+                            reinterpret_cast<const void*>(&mfma_fed<1, false>),
+                            reinterpret_cast<const void*>(&mfma_fed<1, true>),
+                            reinterpret_cast<const void*>(&mfma_fed<1, false, true>)};
+    if (hipFuncSetAttribute(kerns[mode], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) != hipSuccess) return -1;
+  }
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return -1;
   if (hipEventCreate(&e1) != hipSuccess) return -1;
   double best = 0.0;
   for (int r = 0; r < reps; ++r) {
     hipEventRecord(e0, 0);
-    if (mode == 0) hipLaunchKernelGGL((mfma_fed<0, false>), dim3(workgroups), dim3(256), 0, 0, out, iters);
-    else if (mode == 1) hipLaunchKernelGGL((mfma_fed<1, false>), dim3(workgroups), dim3(256), 0, 0, out, iters);
-    else if (mode == 2) hipLaunchKernelGGL((mfma_fed<1, true>), dim3(workgroups), dim3(256), 0, 0, out, iters);
-    else hipLaunchKernelGGL((mfma_fed<1, false, true>), dim3(workgroups), dim3(256), 0, 0, out, iters);
+    if (mode == 0) hipLaunchKernelGGL((mfma_fed<0, false>), dim3(workgroups), dim3(256), dyn, 0, out, iters);
+    else if (mode == 1) hipLaunchKernelGGL((mfma_fed<1, false>), dim3(workgroups), dim3(256), dyn, 0, out, iters);
+    else if (mode == 2) hipLaunchKernelGGL((mfma_fed<1, true>), dim3(workgroups), dim3(256), dyn, 0, out, iters);
+    else hipLaunchKernelGGL((mfma_fed<1, false, true>), dim3(workgroups), dim3(256), dyn, 0, out, iters);
     hipEventRecord(e1, 0);
     if (hipEventSynchronize(e1) != hipSuccess) return -1;
     float ms = 0.f;
