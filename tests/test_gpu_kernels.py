@@ -628,13 +628,16 @@ def test_attention_two_segments(case):
 
 # ---------------------------------------------------------------- absorbed-form attention
 
-@pytest.mark.parametrize("n_rows,pieces", [(37, [0, 300, 364, 1000, 1000]), (64, [0, 2048]), (130, [0, 31, 97])])
+@pytest.mark.parametrize("n_rows,pieces", [(37, [0, 300, 364, 1000, 1000]), (64, [0, 2048]), (130, [0, 31, 97]),
+                                           (70, [0, 100, 100, 250, 400, 401, 700, 900, 1100, 1300])])
 def test_absorbed_path(n_rows, pieces):
     """mla_absorb_q -> mla_absorbed_attn over key pieces (ragged, a 64-key
-    piece, an empty one) -> the pieces merged with mla_merge_states as four
-    128-wide states per row -> mla_absorb_out, against the oracle's absorbed
-    definition per head over all keys; each piece's (o_lat, lse) is also
-    checked against the plain softmax over that piece."""
+    piece, an empty one, a one-key one) -> the pieces merged with
+    mla_merge_states as four 128-wide states per row -> mla_absorb_out,
+    against the oracle's absorbed definition per head over all keys; each
+    piece's (o_lat, lse) is also checked against the plain softmax over that
+    piece. The last case has 9 pieces of 3 row tiles: 27 work items in
+    per-XCD ranges of 4, so ranges cut pieces at several places."""
     require_gpu()
     say(f"absorbed path rows={n_rows} pieces={pieces}")
     rng = np.random.default_rng(75 + n_rows)
