@@ -1,0 +1,130 @@
+"""Host logic of the benchmark: the algorithmic work the headline rate
+divides by, and the HBM traffic records built from rocprofv3 counters.
+No GPU is used."""
+import csv
+import json
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from mla_long_context_amd.prefill import ChunkedPrefill  # noqa: E402
+
+
+def _work(ctx, ext, S, two_seg=True, H=8, cache="bf16", raw=True):
+    """ChunkedPrefill.work() of a chunk plan, without device memory: work()
+    reads only the lengths, the chunk count, the head count and the launch
+    arrangement."""
+    pre = object.__new__(ChunkedPrefill)
+    pre.prob = types.SimpleNamespace(ctx_len=np.asarray(ctx, np.int64), ext_len=np.asarray(ext, np.int64),
+                                     cache_dtype=cache)
+    pre.H, pre.S = H, S
+    n_chunks = max((int(c) + S - 1) // S for c in ctx) if len(ctx) else 0
+    pre.chunks = [None] * n_chunks
+    pre.two_seg = two_seg and bool(pre.chunks)
+    pre.fp8_raw = cache == "fp8" and raw
+    return pre.work()
+
+
+def _visible_pairs(ctx, ext):
+    """(row, key) pairs one head attends over, counted one by one: a new row
+    sees every cached context key and the new tokens up to itself (DeepSeek
+    MLA -- Prefix Cache and Chunked Prefill, section 4.2)."""
+    n = 0
+    for C, E in zip(ctx, ext):
+        for i in range(E):
+            for j in range(C + E):
+                n += (j < C) or (j - C <= i)
+    return n
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_work_is_the_visible_pair_count(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 5))
+    ctx = [int(x) for x in rng.integers(0, 300, B)]
+    ext = [int(x) for x in rng.integers(1, 40, B)]
+    if max(ctx) == 0:
+        ctx[0] = 1
+    S = int(rng.choice([16, 64, 100, 512]))
+    H = 8
+    for two_seg in (True, False):
+        w = _work(ctx, ext, S, two_seg, H)
+        assert w["attn_flops"] == 640 * H * _visible_pairs(ctx, ext)
+        # the launches' shares partition the step's attention work
+        parts = w["ctx_attn_flops"] + w["ctx_merge_attn_flops"] + w["ext_attn_flops"] + w["last_attn_flops"]
+        assert parts == w["attn_flops"]
+        assert w["dec_flops"] == 2 * 512 * 256 * H * (sum(ctx) + sum(ext))
+        assert w["new_tokens"] == sum(ext) and w["ctx_tokens"] == sum(ctx)
+
+
+def test_attention_work_by_chunk():
+    # chunk c of a request holds its context keys [c S, min((c+1) S, C)); the
+    # first chunk's pass, the merging passes and the last pass share them
+    ctx, ext, S, H = [10, 70, 200], [3, 5, 7], 64, 2
+    w = _work(ctx, ext, S, True, H)
+    per_chunk = [sum(max(0, min(S, C - c * S)) * E for C, E in zip(ctx, ext)) for c in range(4)]
+    assert w["ctx_attn_flops"] == 640 * H * per_chunk[0]
+    assert w["ctx_merge_attn_flops"] == 640 * H * (per_chunk[1] + per_chunk[2])
+    ext_pairs = sum(E * (E + 1) // 2 for E in ext)
+    assert w["last_attn_flops"] == 640 * H * (per_chunk[3] + ext_pairs)
+
+
+def test_dsv3_workload_flops():
+    # 128 heads, 4 requests of 8192 cached and 1024 new tokens, chunk 4096
+    w = _work([8192] * 4, [1024] * 4, 4096, True, 128)
+    assert w["dec_flops"] == 2 * 512 * 256 * 128 * 4 * 9216 == 1_236_950_581_248
+    assert w["attn_flops"] == 640 * 128 * 4 * (8192 * 1024 + 1024 * 1025 // 2) == 2_920_745_533_440
+    assert w["dec_flops"] + w["attn_flops"] == 4_157_696_114_688
+
+
+def test_gather_bytes_per_token():
+    # bf16 records move 1152 bytes in and out; fp8 records 644 in (512 codes,
+    # 128 rope bytes, a 4-byte scale) and 644 out as raw codes, or 1152 out
+    # when widened to bf16
+    assert _work([100], [4], 64, cache="bf16")["gather_bytes"] == 100 * 2304
+    assert _work([100], [4], 64, cache="fp8", raw=True)["gather_bytes"] == 100 * (644 + 644)
+    assert _work([100], [4], 64, cache="fp8", raw=False)["gather_bytes"] == 100 * (644 + 1152)
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for k, c, v in rows:
+            wr.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_traffic_record_scaling_and_staleness(tmp_path, monkeypatch):
+    kname = bench.SPAN_KERNEL["attn_ctx_merge"][0]
+    gib_kib = 1 << 20
+    # the copy: its fill dispatch reads almost nothing; FETCH_SIZE reads half
+    # the copied GiB, WRITE_SIZE all of it
+    _counter_csv(tmp_path / "cf.csv", [("fill", "FETCH_SIZE", 10)] + [("copy", "FETCH_SIZE", gib_kib // 2)] * 3)
+    _counter_csv(tmp_path / "cw.csv", [("fill", "WRITE_SIZE", gib_kib)] + [("copy", "WRITE_SIZE", gib_kib)] * 3)
+    # two dispatches of the kernel, and one of another kernel that must be ignored
+    _counter_csv(tmp_path / "f.csv", [(f"void {kname}(AttnArgs)", "FETCH_SIZE", 1000),
+                                      (f"void {kname}(AttnArgs)", "FETCH_SIZE", 3000),
+                                      ("void gather_kernel<true, true>", "FETCH_SIZE", 99999)])
+    _counter_csv(tmp_path / "w.csv", [(f"void {kname}(AttnArgs)", "WRITE_SIZE", 500),
+                                      (f"void {kname}(AttnArgs)", "WRITE_SIZE", 500)])
+    out = tmp_path / "traffic.json"
+    bench.write_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                        str(tmp_path / "cw.csv"), 4, "attn_ctx_merge", out=str(out))
+    rec = json.load(open(out))["w4:attn_ctx_merge"]
+    assert rec["fetch_bytes_per_launch"] == 2000 * 1024 * 2
+    assert rec["write_bytes_per_launch"] == 500 * 1024
+    assert rec["bytes_per_launch"] == 2000 * 1024 * 2 + 500 * 1024
+    assert rec["launches"] == {"fetch": 2, "write": 2}
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench.traffic_for(4, "attn_ctx_merge") == rec["bytes_per_launch"]
+    assert bench.traffic_for(2, "attn_ctx_merge") is None          # no record for that workload
+    d = json.load(open(out))
+    d["w4:attn_ctx_merge"]["source_sha256_16"] = "0" * 16        # the kernel source changed since
+    json.dump(d, open(out, "w"))
+    assert bench.traffic_for(4, "attn_ctx_merge") is None
