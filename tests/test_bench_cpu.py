@@ -128,3 +128,41 @@ def test_traffic_record_scaling_and_staleness(tmp_path, monkeypatch):
     d["w4:attn_ctx_merge"]["source_sha256_16"] = "0" * 16        # the kernel source changed since
     json.dump(d, open(out, "w"))
     assert bench.traffic_for(4, "attn_ctx_merge") is None
+
+
+def _reuse_work(absorbed, merge="one_pass", n_pieces=64, n_pieces_L=36):
+    """ReusePrefill.work() of the head-partitioned reuse workload's plan: 64
+    heads (56 Local, 8 Global), a 262144-token document, 512 query rows, 64
+    protected rows, W_a 8192 -> 2048, W_b 2048 -> 4096."""
+    from mla_long_context_amd.prefill import ReusePrefill
+    pre = object.__new__(ReusePrefill)
+    pre.H, pre.HL, pre.HG, pre.T, pre.P, pre.Ldoc = 64, 56, 8, 512, 64, 262144
+    pre.n_pieces, pre.n_pieces_L = n_pieces, n_pieces_L
+    pre.absorbed, pre.merge_mode = absorbed, merge
+    pre.d_mid, pre.d_model = 2048, 4096
+    pre.docs = [None]
+    return pre.work()
+
+
+def test_reuse_workload_flops():
+    # decompressed Local rows: every head decompressed over the document,
+    # 640 flop per (row, key, head) for the 512 Global rows x 8 heads and the
+    # 64 protected rows x 56 Local heads, and the two projections of
+    # Equation 4 (RedKnot-MLA, section 2)
+    w = _reuse_work(absorbed=False)
+    L = 262144
+    assert w["dec_flops"] == 2 * 512 * 256 * 64 * L
+    assert w["global_attn_flops"] == 640 * L * 512 * 8
+    assert w["local_attn_flops"] == 640 * L * 64 * 56
+    assert w["proj_flops"] == 2 * 512 * (64 * 128 * 2048 + 2048 * 4096)
+    total = w["dec_flops"] + w["attn_flops"] + w["proj_flops"]
+    assert abs(total - 5.71e12) < 0.01e12
+    # absorbed Local rows: only the Global heads are decompressed; a Local
+    # (row, key, head) costs 2*576 for the scores over the latent and 2*512
+    # for the latent-space values; the query absorption and the W_UV product
+    # cost 2*128*512 each per (row, head)
+    a = _reuse_work(absorbed=True)
+    assert a["dec_flops"] == 2 * 512 * 256 * 8 * L
+    assert a["local_attn_flops"] == (2 * 576 + 2 * 512) * L * 64 * 56
+    assert a["absorb_flops"] == 2 * (2 * 128 * 512) * 64 * 56
+    assert a["global_attn_flops"] == w["global_attn_flops"]
