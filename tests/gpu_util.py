@@ -1,10 +1,13 @@
-"""Helpers shared by the GPU parity tests (no method arithmetic here)."""
+"""Helpers shared by the GPU parity tests: comparisons, and tolerance bounds
+derived from the oracle's exact values (none of the path's arithmetic)."""
 import os
 import sys
 
 import numpy as np
 import pytest
 import torch
+
+from oracle import mla_oracle as orc
 
 # tolerances for floating-point outputs against the fp64 oracle
 BF16_MAX_ABS = 2e-2
@@ -49,6 +52,53 @@ def kv_rounding_lse_bound(q, c_kv, W, H, h, scale, visible=None, dequant_roundin
     if visible is not None:
         ds = np.where(visible, ds, 0.0)
     return ds.max(axis=1) + ATTN_ALLOW
+
+
+def relocated_rope_rounding(q_rope, delta, base=10000.0):
+    """What the relocation does to a query's rope part, per element, as
+    (err, err_max): q_rel - q_rot where the kernel's result is determined
+    (err_max 0 there), else 0 and the larger of the two possible |q_rel -
+    q_rot|. q_rot is the exact rotation by -delta (interleaved pairs); the
+    kernel computes y0 = fma(x0, c, -x1 s), y1 = fma(x0, s, x1 c) in fp32
+    with fp32 cos/sin of fp64 angles, within 4 * 2^-24 (|x0| + |x1|) of
+    q_rot, and rounds that to bf16 (nearest even). Where the whole interval
+    rounds to one bf16 value, that value is q_rel. q_rope: [R, 64] fp64 of
+    bf16 values."""
+    q = np.asarray(q_rope, np.float64)
+    y = orc.relocate_q(q, int(delta), base)
+    pair = 4.0 * 2.0 ** -24 * (np.abs(q[:, 0::2]) + np.abs(q[:, 1::2]))
+    eps = np.repeat(pair, 2, axis=1)
+    from mla_inputs import f32_to_bf16_bits
+    lo = orc.bf16_to_f64(f32_to_bf16_bits((y - eps).astype(np.float32)))
+    hi = orc.bf16_to_f64(f32_to_bf16_bits((y + eps).astype(np.float32)))
+    det = lo == hi
+    err = np.where(det, lo - y, 0.0)
+    err_max = np.where(det, 0.0, np.maximum(np.abs(lo - y), np.abs(hi - y)))
+    return err, err_max
+
+
+def relocation_lse_bound(prob, q_rows, h):
+    """Bound on |lse_gpu - lse_oracle| per query row of head h of a reuse
+    problem whose keys are exact (a selection kv_b_proj): the path rotates a
+    query's rope part by -delta_d for document d and stores it in bf16, the
+    dtype its products take, while the oracle rotates the keys by +delta_d
+    exactly. A score against key j of document d then moves by
+    scale * (err . k_j) for the determined elements plus at most
+    scale * sum err_max |k_j| for the others (relocated_rope_rounding); the
+    lse, 1-Lipschitz in the max-norm of the scores, by at most the largest
+    such move, plus the attention's own fp32 arithmetic. q_rows: row indices
+    into prob.q. Returns [len(q_rows)]."""
+    q = orc.bf16_to_f64(prob.q[np.asarray(q_rows), h, 128:])
+    bound = np.zeros(len(q))
+    for d in prob.documents():
+        L = int(d["L"])
+        if L == 0:
+            continue
+        k = orc.bf16_to_f64(orc.gather_bf16_bits(d["pool"], d["block_table"], 0, 0, L))[:, 512:]
+        err, err_max = relocated_rope_rounding(q, int(d["delta"]), prob.rope_base)
+        ds = prob.scale * (np.abs(err @ k.T) + err_max @ np.abs(k).T)
+        bound = np.maximum(bound, ds.max(axis=1) * (1 + 1e-12))
+    return bound + ATTN_ALLOW
 
 
 def require_gpu():

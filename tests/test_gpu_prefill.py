@@ -16,7 +16,7 @@ from mla_long_context_amd.prefill import ChunkedPrefill, ReusePrefill
 from oracle import mla_oracle as orc
 
 from gpu_util import (FEW_KEYS, FP8_REL_L2, LSE_ABS, bits, check_lse, check_out, f64, kv_rounding_lse_bound,
-                      require_gpu, say)
+                      relocation_lse_bound, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -211,6 +211,40 @@ def test_reuse_with_empty_documents(local):
         check_lse(f64(pre.lse_G), ref["lse_G"], what="lse_G")
         check_out(f64(pre.rec_out), ref["rec"], what="rec")
         check_lse(f64(pre.lse_L), ref["rec_lse"], what="rec_lse")
+        check_out(f64(y), ref["y"], what="y")
+
+
+@pytest.mark.parametrize("local", ["absorbed", "decompressed"])
+def test_reuse_tiny_documents(local):
+    """Documents of 1 and 25 keys, and 1-, 3- and 40-key documents together.
+    A selection kv_b_proj keeps every key exact, so only the relocated query
+    differs from the oracle's exact rotation: the path stores it in bf16, and
+    a row over so few keys keeps that rounding in its lse (over many keys it
+    averages out). Outputs and y are held to the bar; lse to the bar or, if
+    larger, the bound that rounding allows (relocation_lse_bound)."""
+    require_gpu()
+    say(f"reuse with tiny documents ({local})")
+    for prob in (mi.make_reuse_problem(H=4, n_local=3, L=1, T=40, delta=4096, P=5, d_mid=128, d_model=128,
+                                       chunk=256, seed=51, weights="selection"),
+                 mi.make_reuse_problem(H=4, n_local=2, L=25, T=40, delta=1, P=5, d_mid=128, d_model=128,
+                                       chunk=256, seed=52, weights="selection"),
+                 mi.make_multidoc_problem(H=4, n_local=2, doc_lens=(1, 3, 40), T=30, P=4, seed=53, d_mid=128,
+                                          d_model=128, weights="selection")):
+        pre = ReusePrefill(prob, split=64, split_local=64, local_path=local)
+        y = pre.run()
+        torch.cuda.synchronize()
+        pre.check()
+        ref = orc.reuse_reference(prob)
+        HL, H = prob.n_local, prob.H
+        prot = np.asarray(prob.prot_rows)
+        tol_g = np.stack([np.maximum(LSE_ABS, relocation_lse_bound(prob, np.arange(prob.T), h))
+                          for h in range(HL, H)], axis=1)
+        tol_l = np.stack([np.maximum(LSE_ABS, relocation_lse_bound(prob, prot, h)) for h in range(HL)], axis=1)
+        say(f"  lse bounds: Global up to {tol_g.max():.2e}, Local up to {tol_l.max():.2e}")
+        check_out(f64(pre.glob_out), ref["O_G"], what="O_G")
+        check_lse(f64(pre.lse_G), ref["lse_G"], tol=tol_g, what="lse_G")
+        check_out(f64(pre.rec_out), ref["rec"], what="rec")
+        check_lse(f64(pre.lse_L), ref["rec_lse"], tol=tol_l, what="rec_lse")
         check_out(f64(y), ref["y"], what="y")
 
 
