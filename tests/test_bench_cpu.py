@@ -166,3 +166,25 @@ def test_reuse_workload_flops():
     assert a["local_attn_flops"] == (2 * 576 + 2 * 512) * L * 64 * 56
     assert a["absorb_flops"] == 2 * (2 * 128 * 512) * 64 * 56
     assert a["global_attn_flops"] == w["global_attn_flops"]
+
+
+def test_oracle_units_cover_the_workload_once():
+    # the cpu baseline's units are (request, head) pairs of the tiny workload,
+    # each carrying its share of the same algorithmic count as the GPU's value
+    import mla_inputs as mi
+    prob = mi.make_config(1)
+    units = bench.oracle_units(prob)
+    assert sorted(u for u, _ in units) == [(r, h) for r in range(prob.B) for h in range(prob.H)]
+    w = _work(list(prob.ctx_len), list(prob.ext_len), prob.chunk, True, prob.H)
+    assert sum(f for _, f in units) == w["dec_flops"] + w["attn_flops"]
+    assert units == bench.oracle_units(prob)            # seeded order
+
+
+def test_oracle_pool_reports_the_rate_of_the_units_it_ran():
+    import mla_inputs as mi
+    prob = mi.make_config(1)
+    pool = bench.OraclePool(prob)
+    rec = pool.run(budget_s=3.0)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s" and rec["value"] > 0
+    assert rec["cores"] == min(len(os.sched_getaffinity(0)), 16)
+    assert f"of {prob.B * prob.H} " in rec["sample"]
