@@ -410,7 +410,8 @@ class ReusePrefill(_DeviceStatus):
                 n_rt = -(-(len(prot_rows) * prob.n_local) // 128)
                 cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
                 per_chunk = max(1, cus // max(n_rt, 1))
-                split_local = max(2048, -(-(-(-self.S // per_chunk)) // 64) * 64)
+                keys = (self.S + per_chunk - 1) // per_chunk            # keys per piece, rounded up
+                split_local = max(2048, (keys + 63) // 64 * 64)         # to whole 64-key blocks
             self.split_L = max(64, int(split_local) // 64 * 64)
         else:
             self.split_L = self.split
