@@ -35,6 +35,7 @@ import argparse
 import contextlib
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -562,10 +563,12 @@ KERNEL_NAMES = {
 }
 
 
-def run_workload(k, prob, args, torch, steps, warmup, graph=False):
+def run_workload(k, prob, args, torch, steps, warmup, graph=False, min_ms=0.0):
     """Time one standard workload: `steps` timed steps (mean, median, min),
     then the same number again with events around every launch for the
-    per-kernel breakdown and the dominant kernel's roofline."""
+    per-kernel breakdown and the dominant kernel's roofline. With min_ms,
+    the step count is raised until the timed steps take at least that long
+    (from a step timed after the warm-up)."""
     from mla_long_context_amd.prefill import ChunkedPrefill, GraphStep, ReusePrefill
     import mla_inputs
     reuse = bool(getattr(prob, "is_reuse", False))
@@ -585,6 +588,9 @@ def run_workload(k, prob, args, torch, steps, warmup, graph=False):
     step = GraphStep(pre).replay if graph else (lambda: pre.run(check=False))
     for _ in range(warmup):
         step()
+    if min_ms > 0:
+        est, _ = timed_steps(torch, step, 2)
+        steps = max(steps, min(200, math.ceil(1.1 * min_ms / max(est, 1e-3))))   # 10% margin on the estimate
 
     # Timed steps for the value: events only between steps (events around
     # every launch would add a fence between kernels); the value uses the
@@ -684,7 +690,8 @@ def main():
                     help=f"time one standard workload alone (default: workload {HEADLINE}, the headline, "
                          f"with sub-records for workloads {', '.join(map(str, SUB_WORKLOADS))})")
     ap.add_argument("--no-sub", action="store_true", help="headline only, no sub-records")
-    ap.add_argument("--sub-steps", type=int, default=10, help="timed steps per sub-record workload")
+    ap.add_argument("--sub-steps", type=int, default=20,
+                    help="timed steps per sub-record workload (at least 20, raised to 200 ms of timed steps)")
     ap.add_argument("--chunk", type=int, default=None, help="context chunk override (tokens)")
     ap.add_argument("--split", type=int, default=None,
                     help="reuse workload: keys per attention piece (default: the driver's)")
@@ -788,7 +795,7 @@ def main():
             pj = mla_inputs.make_config(j)
             print(f"# inputs ready in {time.time() - t_gen:.1f}s: {mla_inputs.CONFIG_NAMES[j]}",
                   file=sys.stderr, flush=True)
-            r = run_workload(j, pj, args, torch, args.sub_steps, args.warmup, args.graph)
+            r = run_workload(j, pj, args, torch, args.sub_steps, args.warmup, args.graph, min_ms=200.0)
             print(f"# workload {j}: {r['ms_per_step']} ms/step, {r['value']} TFLOP/s", file=sys.stderr, flush=True)
             res["workloads"][str(j)] = r
             del pj
