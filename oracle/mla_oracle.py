@@ -23,10 +23,10 @@ that definition states. Pages cited:
 * Cache write path: [PAGED] "Position independence beats prefix matching"
   (records written into blocks that are sealed when full), [DSMLA] 2.2
   (fp8 storage of the latent; its content is missing from the page, so the
-  per-token scale follows reading R14).
+  per-token scale is a reading, R14, stated in quantize_token_e4m3).
 
-Readings where the pages are silent are listed in the module docstrings of
-the functions that take them (R-numbers match the design doc).
+Each reading taken where the pages are silent is stated in the docstring of
+the function that takes it, under a label R<n>.
 
 Parity unpinned: the synthetic Local-head artifact and the protected-row
 choice of the head-partitioned reuse workload are inputs by construction;
