@@ -211,7 +211,9 @@ extern "C" int mla_merge_states(const void* out_a, int dtype_a, const float* lse
               "mla_merge_states: dtypes must be bf16 or fp32 (got %d, %d, %d)", dtype_a, dtype_b, dtype_out);
   MLA_REQUIRE(mla_aligned16(out_a) && mla_aligned16(out_b) && mla_aligned16(out), MLA_ERR_INVALID_ARG,
               "mla_merge_states: state pointers must be 16-byte aligned");
-  MLA_REQUIRE(rows <= (int64_t)1 << 40, MLA_ERR_INVALID_ARG, "mla_merge_states: rows too large");
+  // 16 lanes per row: the grid has rows / 16 workgroups, at most 2^31 - 1
+  MLA_REQUIRE(rows <= (int64_t)1 << 34, MLA_ERR_INVALID_ARG, "mla_merge_states: rows (%lld) too large for one call",
+              (long long)rows);
   const int64_t threads = rows * 16;
   dim3 g((unsigned)((threads + kThreads - 1) / kThreads));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

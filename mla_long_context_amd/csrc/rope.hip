@@ -92,6 +92,9 @@ extern "C" int mla_rope_relocate_q(const void* q_in, void* q_out, int64_t q_row_
               "mla_rope_relocate_q: unknown pairing %d", pairing);
   MLA_REQUIRE(rope_base > 1.0 && isfinite(rope_base), MLA_ERR_INVALID_ARG,
               "mla_rope_relocate_q: rope_base must be finite and > 1");
+  // 8 lanes per (row, head): the grid has T * H / 32 workgroups, at most 2^31 - 1
+  MLA_REQUIRE((int64_t)T * H <= (int64_t)1 << 34, MLA_ERR_INVALID_ARG,
+              "mla_rope_relocate_q: T * H (%lld) too large for one call", (long long)T * H);
   RopeTable tab;
   for (int k = 0; k < 32; ++k) {
     const double theta = pow(rope_base, -2.0 * k / 64.0);
