@@ -34,9 +34,10 @@
  *     on the host before anything is enqueued; on error nothing is enqueued
  *     and mla_last_error() describes the problem (thread-local string).
  *     A problem whose grid would exceed the launch limits (2^31 - 1
- *     workgroups, or 65535 in a second grid dimension) is refused with
- *     MLA_ERR_INVALID_ARG ("too large"), never truncated; split it over
- *     several calls.
+ *     workgroups, or 65535 in a second grid dimension) is refused, never
+ *     truncated: with MLA_ERR_INVALID_ARG ("too large") by the argument
+ *     checks, or with MLA_ERR_LAUNCH where the runtime's own check of the
+ *     grid rejects it; split such a problem over several calls.
  *   - Geometry is fixed: d_c = 512, d_rope = 64, d_nope = d_v = 128,
  *     d_qk = 192, block = 64 tokens. Strides are in ELEMENTS of the stated
  *     dtype. Base pointers must be 16-byte aligned and row strides multiples

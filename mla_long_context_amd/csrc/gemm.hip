@@ -604,9 +604,6 @@ extern "C" int mla_pack_weight_t(const void* w, int K, int N, void* out, void* s
   MLA_REQUIRE(K > 0 && N > 0 && K % 8 == 0 && N % 8 == 0, MLA_ERR_INVALID_ARG,
               "mla_pack_weight_t: K (%d) and N (%d) must be positive multiples of 8", K, N);
   MLA_REQUIRE(w != out, MLA_ERR_INVALID_ARG, "mla_pack_weight_t: in-place transpose is not supported");
-  // one workgroup per 64 x 64 tile; the grid's second dimension (K / 64) is
-  // limited to 65535
-  MLA_REQUIRE(K / kTr < 65535, MLA_ERR_INVALID_ARG, "mla_pack_weight_t: K (%d) too large", K);
   dim3 g((N + kTr - 1) / kTr, (K + kTr - 1) / kTr);
   hipLaunchKernelGGL(transpose_kernel, g, dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(w), K, N, static_cast<uint16_t*>(out));

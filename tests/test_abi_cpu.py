@@ -132,8 +132,7 @@ def test_merge_rope_partition_pack_validation(lib):
     assert _err(mla.mla_pack_weight_t, FAKE, 16, 16, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG   # in place
     # sizes whose grids would not fit the launch limits are refused, not truncated
     for fn, args in [(mla.mla_merge_states, (FAKE, 0, FAKE, FAKE, 0, FAKE, (1 << 34) + 1, FAKE, 0, FAKE)),
-                     (mla.mla_rope_relocate_q, (FAKE, FAKE, 1024 * 192, 1 << 25, 1024, 4096, 10000.0, 0)),
-                     (mla.mla_pack_weight_t, (FAKE, 64 * 65535, 16, FAKE + 16))]:
+                     (mla.mla_rope_relocate_q, (FAKE, FAKE, 1024 * 192, 1 << 25, 1024, 4096, 10000.0, 0))]:
         code, msg = _err(fn, *args)
         assert code == _lib.MLA_ERR_INVALID_ARG and "too large" in msg, msg
 
