@@ -51,11 +51,12 @@ HEADLINE = 4                   # the fp8 ragged batch: the largest single-GPU wo
 SUB_WORKLOADS = (2, 3, 5)
 CSRC = os.path.join(ROOT, "mla_long_context_amd", "csrc")
 # timer span -> (kernel name in rocprofv3 traces, source file) for the HBM
-# counter records
+# counter records (the chunked workloads' default schedule: every context
+# pass is mla_prefill_attn_chunk, which routes each request's rows to the
+# bf16 result or the fp32 state)
 SPAN_KERNEL = {
-    "attn_ctx": ("attn_kernel<4, false, false, 2, false, false>", "attn.hip"),
-    "attn_ctx_merge": ("attn_kernel<4, false, false, 2, true, false>", "attn.hip"),
-    "attn_last": ("attn_kernel<4, false, false, 0, true, true>", "attn.hip"),
+    "attn_ctx": ("attn_kernel<4, false, false, 0, false, true>", "attn.hip"),
+    "attn_ctx_merge": ("attn_kernel<4, false, false, 0, true, true>", "attn.hip"),
     "attn_global": ("attn_kernel<8, false, true, 2, false, false>", "attn.hip"),
     "attn_local": ("absorbed_attn_kernel", "absorbed.hip"),
     "decompress": ("decompress_kernel", "gemm.hip"),
@@ -552,8 +553,9 @@ def bench_artifact(args, torch, mla, mla_inputs):
 
 
 KERNEL_NAMES = {
-    "attn_ctx": "mla_prefill_attn (first context chunk)",
-    "attn_ctx_merge": "mla_prefill_attn_merge (context chunks after the first)",
+    "attn_ctx": "mla_prefill_attn_chunk (first context chunk, with the new tokens of the requests it ends)",
+    "attn_ctx_merge": "mla_prefill_attn_chunk (context chunks after the first, merged into the state, "
+                      "with the new tokens of the requests each ends)",
     "attn_ext": "mla_prefill_attn (causal pass)",
     "attn_last": "mla_prefill_attn_2seg (last context chunk + causal pass)",
     "decompress": "mla_decompress", "attn_global": "mla_prefill_attn (Global heads)",

@@ -296,6 +296,47 @@ int mla_prefill_attn_2seg(const void* q, int64_t q_row_stride, int H_q, int h_be
                           float* lse, int64_t lse_row_stride, void* stream);
 
 /*
+ * mla_prefill_attn_chunk -- one pass of the [DSMLA] 4.4 chunk loop over a
+ * ragged batch in which each request's causal pass over its new tokens
+ * ([DSMLA] 4.2) joins the pass of that request's own last context chunk,
+ * instead of a separate pass after the loop. For request b:
+ *   last[b] == 0: segment 1 only (the chunk's context keys [cu_k[b],
+ *                 cu_k[b+1]), all visible); the result is merged into the
+ *                 running state (when merge != 0) and written back to
+ *                 state / state_lse in fp32;
+ *   last[b] != 0: segment 1 and segment 2 (the new tokens' keys [cu_k2[b],
+ *                 cu_k2[b+1]), causal as in mla_prefill_attn_2seg) in one
+ *                 online softmax, merged into the running state (when
+ *                 merge != 0); the final result goes to out (bf16) and its
+ *                 lse to state_lse.
+ * merge == 0 is the loop's first pass: no state is read. The state is read
+ * and written in place (state [rows][...] fp32 with state_row_stride,
+ * state_lse fp32 with state_lse_row_stride), so after the request's last
+ * pass state_lse holds its final lse. In a merging pass, a request with
+ * last[b] == 0 and no key in segment 1 leaves its state untouched (merging
+ * an empty key set is the identity), which skips requests whose last pass
+ * came earlier; in a first pass (merge == 0) such a request gets the empty
+ * state (0, -inf). Final rows leave state untouched, and the other rows out.
+ * order (nullable): a permutation of the requests 0..batch-1, the order in
+ * which their workgroups are dealt out (NULL: 0, 1, ...); listing the
+ * requests with the most keys in this pass first shortens its tail. It
+ * changes no result. Everything else (q, segments, strides, scale, cu_q,
+ * max_q) as in mla_prefill_attn_2seg; last, state and state_lse must not be
+ * NULL.
+ */
+int mla_prefill_attn_chunk(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                           const void* k_nope, int64_t k_head_stride,
+                           const void* v, int64_t v_head_stride,
+                           const void* latent, int64_t ld_latent, const int32_t* cu_k,
+                           const void* k_nope2, int64_t k_head_stride2,
+                           const void* v2, int64_t v_head_stride2,
+                           const void* latent2, int64_t ld_latent2, const int32_t* cu_k2,
+                           const int32_t* last, const int32_t* order, const int32_t* cu_q, int batch,
+                           int max_q, float scale, int merge, float* state, int64_t state_row_stride,
+                           float* state_lse, int64_t state_lse_row_stride,
+                           void* out, int64_t out_row_stride, void* stream);
+
+/*
  * Absorbed-form attention ([DSMLA] section 3: W_UK folded into the query,
  * W_UV applied after the attention, every head attends to the shared
  * 576-wide latent), for query sets small next to the key count: the

@@ -28,7 +28,8 @@ ROPE_HALF = 1
 EXPORTS = (
     "mla_last_error", "mla_abi_version", "mla_gather_context", "mla_gather_context_fp8_raw", "mla_cache_append",
     "mla_pack_weight_t",
-    "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_prefill_attn_2seg", "mla_absorb_q",
+    "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_prefill_attn_2seg", "mla_prefill_attn_chunk",
+    "mla_absorb_q",
     "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states", "mla_merge_states_n",
     "mla_rope_relocate_q",
     "mla_head_partition_merge", "mla_head_partition_merge_noalloc", "mla_token_hash", "mla_artifact_check",
@@ -95,6 +96,9 @@ _SIGS = {
     "mla_prefill_attn_2seg": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P,
                               P, I64, P, I64, P, I64, P, P, I32, I32, F32,
                               P, I64, P, I64, P, I32, I64, P, I64, P],
+    "mla_prefill_attn_chunk": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P,
+                               P, I64, P, I64, P, I64, P, P, P, P, I32, I32, F32,
+                               I32, P, I64, P, I64, P, I64, P],
     "mla_absorb_q": [P, I64, I32, I32, I32, P, I32, P, I32, P, P],
     "mla_absorbed_attn": [P, I32, P, I64, P, I32, F32, P, I32, P, P],
     "mla_absorb_out": [P, I32, P, I32, I32, I32, P, I64, P],
@@ -215,6 +219,19 @@ def mla_prefill_attn_2seg(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_s
                  _ptr(cu_k2), _ptr(cu_q), batch, max_q, float(scale), _ptr(prev_out), prev_row_stride,
                  _ptr(prev_lse), prev_lse_row_stride, _ptr(out), out_dtype, out_row_stride, _ptr(lse),
                  lse_row_stride, _stream(stream))
+
+
+def mla_prefill_attn_chunk(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,
+                           v_head_stride, latent, ld_latent, cu_k, k_nope2, k_head_stride2, v2,
+                           v_head_stride2, latent2, ld_latent2, cu_k2, last, order, cu_q, batch, max_q,
+                           scale, merge, state, state_row_stride, state_lse, state_lse_row_stride, out,
+                           out_row_stride, stream=None):
+    return _call("mla_prefill_attn_chunk", _ptr(q), q_row_stride, H_q, h_begin, h_end, _ptr(k_nope),
+                 k_head_stride, _ptr(v), v_head_stride, _ptr(latent), ld_latent, _ptr(cu_k),
+                 _ptr(k_nope2), k_head_stride2, _ptr(v2), v_head_stride2, _ptr(latent2), ld_latent2,
+                 _ptr(cu_k2), _ptr(last), _ptr(order), _ptr(cu_q), batch, max_q, float(scale), int(merge),
+                 _ptr(state), state_row_stride, _ptr(state_lse), state_lse_row_stride, _ptr(out),
+                 out_row_stride, _stream(stream))
 
 
 def mla_absorb_q(q, q_row_stride, H_q, h_begin, h_end, row_ids, n_rows, kv_b_proj, H_total, q_abs,

@@ -48,6 +48,14 @@ struct AttnArgs {
   // causal, with the same latent row stride
   const uint16_t* k2; int64_t khs2; const uint16_t* v2; int64_t vhs2; const uint16_t* lat2;
   const int32_t* cu_k2;
+  // two-segment kernel, per request (nullable: every request): nonzero when
+  // this pass is the request's last, which takes the second segment and
+  // writes the final result to out; the other requests' rows write the
+  // running fp32 state to state_out instead
+  const int32_t* last; float* state_out; int64_t state_rs;
+  // nullable: the order in which requests are dealt out (a permutation of
+  // 0..batch-1), longest first to shorten the launch's tail
+  const int32_t* order;
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if (bh >= n_bh) return;
   int qt = j % a.n_qt;
   const int hs = bh % a.Hsel;
-  const int b = bh / a.Hsel;
+  const int b = a.order ? a.order[bh / a.Hsel] : bh / a.Hsel;
   // longest rows first: later row tiles see more keys of a causal segment
   if (kCausal || kSeg2) qt = a.n_qt - 1 - qt;
 
@@ -133,9 +141,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int ntiles1 = kend > 0 ? (kend + kTileK - 1) / kTileK : 0;   // tiles of the first segment
   int ntiles = ntiles1;
   int k02 = 0, n_k2 = 0, shift2 = 0;
+  bool fin = true;                           // this pass writes the request's final result
   if constexpr (kSeg2) {
+    fin = a.last == nullptr || a.last[b] != 0;
     k02 = a.cu_k2[b];
-    n_k2 = a.cu_k2[b + 1] - k02;
+    n_k2 = fin ? a.cu_k2[b + 1] - k02 : 0;
     shift2 = n_k2 - n_q;
     const int kend2 = min(n_k2, r0 + ROWS + shift2);
     ntiles += kend2 > 0 ? (kend2 + kTileK - 1) / kTileK : 0;
@@ -148,6 +158,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if constexpr (kMerge && kOutDt == MLA_DTYPE_FP32) {
     if (ntiles == 0 && a.out == static_cast<const void*>(a.prev) && a.out_rs == a.prev_rs &&
         a.lse == a.prev_lse && a.lse_rs == a.prev_lse_rs)
+      return;
+  }
+  if constexpr (kMerge && kSeg2) {
+    // a request whose last pass came earlier: its state is no longer read
+    if (!fin && ntiles == 0 && a.state_out == a.prev && a.state_rs == a.prev_rs && a.lse == a.prev_lse &&
+        a.lse_rs == a.prev_lse_rs)
       return;
   }
 
@@ -481,7 +497,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         o0 = fmaf(c_prev, pv.x, o0); o1 = fmaf(c_prev, pv.y, o1);
         o2 = fmaf(c_prev, pv.z, o2); o3 = fmaf(c_prev, pv.w, o3);
       }
-      if (kOutDt == MLA_DTYPE_FP32) {
+      if (kSeg2 && !fin) {
+        // not this request's last pass: the running fp32 state
+        float* op = a.state_out + orow * a.state_rs + (int64_t)hs * kDv + dv;
+        *reinterpret_cast<f32x4*>(op) = f32x4{o0, o1, o2, o3};
+      } else if (kOutDt == MLA_DTYPE_FP32) {
         float* op = static_cast<float*>(a.out) + orow * a.out_rs + (int64_t)hs * kDv + dv;
         *reinterpret_cast<f32x4*>(op) = f32x4{o0, o1, o2, o3};
       } else {
@@ -505,10 +525,14 @@ void launch_seg2m(bool merge, int out_dt, dim3 g, hipStream_t s, const AttnArgs&
   else launch_seg2<NW, false>(out_dt, g, s, a);
 }
 
-// second key segment of mla_prefill_attn_2seg
+// second key segment of mla_prefill_attn_2seg and mla_prefill_attn_chunk;
+// the latter also passes the per-request last-pass flags and the fp32 state
+// the other requests' rows write
 struct Seg2 {
   const void* k_nope; int64_t k_head_stride; const void* v; int64_t v_head_stride;
   const void* latent; int64_t ld_latent; const int32_t* cu_k;
+  const int32_t* last = nullptr; float* state = nullptr; int64_t state_rs = 0;
+  const int32_t* order = nullptr;
 };
 
 template <int NW, bool kCausal, bool kRowIds, bool kMerge>
@@ -575,6 +599,12 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
     MLA_REQUIRE(seg2->ld_latent == ld_latent, MLA_ERR_UNSUPPORTED,
                 "%s: both segments' latents need the same row stride (%lld != %lld)", fn,
                 (long long)seg2->ld_latent, (long long)ld_latent);
+    if (seg2->last) {
+      MLA_REQUIRE(seg2->state, MLA_ERR_INVALID_ARG, "%s: null state", fn);
+      MLA_REQUIRE(mla_aligned16(seg2->state) && seg2->state_rs % 4 == 0 && seg2->state_rs >= (int64_t)Hsel * kDv,
+                  MLA_ERR_INVALID_ARG, "%s: state must be 16-byte aligned with row stride >= Hsel*128 (multiple of 4)",
+                  fn);
+    }
   }
   if (merge) {
     MLA_REQUIRE(prev && prev_lse, MLA_ERR_INVALID_ARG, "%s: null previous state", fn);
@@ -607,7 +637,7 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
              cu_q, cu_k, q_row_ids, batch, n_qt, scale * kLog2e,
              out, out_row_stride, lse, lse_row_stride,
              prev, prev_row_stride, prev_lse, prev_lse_row_stride,
-             nullptr, 0, nullptr, 0, nullptr, nullptr};
+             nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
   if (seg2) {
     a.k2 = static_cast<const uint16_t*>(seg2->k_nope);
     a.khs2 = seg2->k_head_stride;
@@ -615,6 +645,10 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
     a.vhs2 = seg2->v_head_stride;
     a.lat2 = static_cast<const uint16_t*>(seg2->latent);
     a.cu_k2 = seg2->cu_k;
+    a.last = seg2->last;
+    a.state_out = seg2->state;
+    a.state_rs = seg2->state_rs;
+    a.order = seg2->order;
   }
   dim3 g((unsigned)total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -677,4 +711,32 @@ extern "C" int mla_prefill_attn_2seg(const void* q, int64_t q_row_stride, int H_
                       v_head_stride, latent, ld_latent, cu_q, cu_k, nullptr, batch, max_q, scale, 0, out,
                       out_dtype, out_row_stride, lse, lse_row_stride, prev_out, prev_row_stride, prev_lse,
                       prev_lse_row_stride, merge, stream, &seg2);
+}
+
+extern "C" int mla_prefill_attn_chunk(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
+                                      const void* k_nope, int64_t k_head_stride, const void* v,
+                                      int64_t v_head_stride, const void* latent, int64_t ld_latent,
+                                      const int32_t* cu_k, const void* k_nope2, int64_t k_head_stride2,
+                                      const void* v2, int64_t v_head_stride2, const void* latent2,
+                                      int64_t ld_latent2, const int32_t* cu_k2, const int32_t* last,
+                                      const int32_t* order, const int32_t* cu_q, int batch, int max_q,
+                                      float scale, int merge,
+                                      float* state, int64_t state_row_stride, float* state_lse,
+                                      int64_t state_lse_row_stride, void* out, int64_t out_row_stride,
+                                      void* stream) {
+  const char* fn = "mla_prefill_attn_chunk";
+  if (batch > 0 && max_q > 0 && !(last && state && state_lse)) {
+    mla_begin_call();
+    mla_set_error("%s: null last, state or state_lse", fn);
+    return MLA_ERR_INVALID_ARG;
+  }
+  Seg2 seg2{k_nope2, k_head_stride2, v2, v_head_stride2, latent2, ld_latent2, cu_k2};
+  seg2.last = last;
+  seg2.state = state;
+  seg2.state_rs = state_row_stride;
+  seg2.order = order;
+  return prefill_attn(fn, q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v, v_head_stride, latent,
+                      ld_latent, cu_q, cu_k, nullptr, batch, max_q, scale, 0, out, MLA_DTYPE_BF16, out_row_stride,
+                      state_lse, state_lse_row_stride, merge ? state : nullptr, state_row_stride,
+                      merge ? state_lse : nullptr, state_lse_row_stride, merge != 0, stream, &seg2);
 }

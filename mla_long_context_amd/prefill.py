@@ -103,11 +103,17 @@ class _DeviceStatus:
 class ChunkedPrefill(_DeviceStatus):
     """Configs with a paged context and new (extend) tokens per request."""
 
-    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True, fp8_mode="raw"):
+    def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True, fp8_mode="raw",
+                 fold_causal=True):
         """fp8_mode (fp8 caches): "raw" gathers the codes and scales as they
         are and the decompression reads the codes (mla_gather_context_fp8_raw,
         mla_decompress with row_scale); "dequant" has the gather write the
-        dequantised bf16 latent instead."""
+        dequantised bf16 latent instead.
+
+        With every merge fused and two_segment, each request's causal pass
+        over its new tokens runs in the pass of its own last context chunk
+        (fold_causal, mla_prefill_attn_chunk); fold_causal=False runs all of
+        them in the pass of the loop's last chunk (mla_prefill_attn_2seg)."""
         self.prob = prob
         self.device = device
         assert fuse_merge in ("none", "final", "all")
@@ -161,6 +167,20 @@ class ChunkedPrefill(_DeviceStatus):
         # tokens (mla_prefill_attn_2seg): their keys are decompressed behind
         # the chunk's, at token offset ext_off of the same workspaces.
         self.two_seg = two_segment and fuse_merge == "all" and bool(self.chunks)
+        # fold: request r's new tokens join the pass of its last chunk
+        # max(ceil(C_r / S) - 1, 0); last[c][r] marks it
+        self.fold = self.two_seg and fold_causal
+        if self.fold:
+            last_c = np.maximum((C + self.S - 1) // self.S - 1, 0)
+            self.last_flags = [_i32((last_c == c).astype(np.int32), device) for c in range(n_chunks)]
+            # each pass deals out the requests whose workgroups have the most
+            # keys first (this chunk's, plus the new tokens' where it is the
+            # last): the long ones start early and the launch ends evenly
+            E = prob.ext_len.astype(np.int64)
+            self.pass_order = []
+            for c in range(n_chunks):
+                keys = np.clip(C - c * self.S, 0, self.S) + np.where(last_c == c, E, 0)
+                self.pass_order.append(_i32(np.argsort(-keys, kind="stable").astype(np.int32), device))
         self.ext_off = max_ctx_tok if self.two_seg else 0
         self.max_tok = max([ch["n"] for ch in self.chunks] + [self.ext_off + self.T, 1])
         lat_rows = max(off, 1) if self.gather_once else max_ctx_tok
@@ -177,7 +197,8 @@ class ChunkedPrefill(_DeviceStatus):
             self.tmp_o = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
             self.tmp_l = torch.empty((T, H), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=device)
-        self.lse = torch.empty((T, H), dtype=torch.float32, device=device)
+        # folded passes write each request's final lse over its state's
+        self.lse = self.acc_l if self.fold else torch.empty((T, H), dtype=torch.float32, device=device)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=device)
 
     # one step of the path per call
@@ -229,6 +250,20 @@ class ChunkedPrefill(_DeviceStatus):
                                 self.acc_l if merge else None, self.H, self.out, L.DTYPE_BF16,
                                 self.H * D_V, self.lse, self.H, stream)
 
+    def attend_chunk(self, ci, ch, stream=None):
+        """Chunk ci's keys for every request, plus the new tokens' keys
+        (causal) of the requests whose last chunk this is; those rows get
+        their bf16 result, the others' running fp32 state is written (the
+        first chunk) or merged into (the chunks after it)."""
+        L.mla_prefill_attn_chunk(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
+                                 self.v_ws, self.hstride, self._lat(ch), D_LAT, ch["cu"],
+                                 self._at(self.k_ws, self.ext_off), self.hstride,
+                                 self._at(self.v_ws, self.ext_off), self.hstride, self.ext, D_LAT,
+                                 self.cu_ext, self.last_flags[ci], self.pass_order[ci], self.cu_ext, self.B,
+                                 self.maxE,
+                                 self.prob.scale, ci > 0, self.acc_o, self.H * D_V, self.acc_l, self.H,
+                                 self.out, self.H * D_V, stream)
+
     def attend(self, latent, cu_k, causal, out, out_dtype, lse, stream=None):
         L.mla_prefill_attn(self.q, self.H * D_QK, self.H, 0, self.H, self.k_ws, self.hstride,
                            self.v_ws, self.hstride, latent, D_LAT, self.cu_ext, cu_k, None, self.B,
@@ -252,8 +287,10 @@ class ChunkedPrefill(_DeviceStatus):
         attention wrote a bf16 chunk state, or inside the attention kernel
         (mla_prefill_attn_merge): fuse_merge selects which merges are fused
         ("none", "final" = only the last, "all"). The last merge writes the
-        bf16 result. With "all", the last chunk and the causal pass share
-        one launch (mla_prefill_attn_2seg).
+        bf16 result. With "all", the causal pass shares a launch with a
+        context chunk: by default each request's with the pass of its own
+        last chunk (mla_prefill_attn_chunk), with fold_causal=False all of
+        them with the pass of the loop's last chunk (mla_prefill_attn_2seg).
 
         check: wait for the step and raise if the gather met a block id
         outside the pool (skipped under graph capture; a caller timing steps
@@ -270,6 +307,19 @@ class ChunkedPrefill(_DeviceStatus):
         if self.gather_once:
             with _span(timer, "gather"):
                 self.gather_all(stream)
+        if self.fold:
+            # the new tokens' keys first: every chunk's pass may take some
+            with _span(timer, "decompress"):
+                self.decompress(self.ext, self.T, stream, off=self.ext_off)
+            for ci, ch in enumerate(self.chunks):
+                if not self.gather_once:
+                    with _span(timer, "gather"):
+                        self.gather(ch, stream)
+                with _span(timer, "decompress"):
+                    self.decompress(self._lat(ch), ch["n"], stream, row_scale=self._scale(ch))
+                with _span(timer, "attn_ctx" if ci == 0 else "attn_ctx_merge"):
+                    self.attend_chunk(ci, ch, stream)
+            return self.out, self.lse
         for ci, ch in enumerate(self.chunks):
             if not self.gather_once:
                 with _span(timer, "gather"):
@@ -327,6 +377,20 @@ class ChunkedPrefill(_DeviceStatus):
         # of the chunks after it, and the last chunk (whose pass also takes
         # the new tokens when the chunk loop ends in one two-segment launch)
         pairs = [int((np.clip(C - c * self.S, 0, self.S) * E).sum()) for c in range(len(self.chunks))]
+        if getattr(self, "fold", False):
+            # each request's causal pairs belong to the pass of its last chunk
+            last_c = np.maximum((C + self.S - 1) // self.S - 1, 0)
+            passes = [p + int((E * (E + 1) // 2)[last_c == c].sum()) for c, p in enumerate(pairs)]
+            return dict(
+                dec_flops=2 * 512 * 256 * H * dec_tok,
+                attn_flops=640 * H * (ctx_pairs + ext_pairs),
+                ctx_attn_flops=640 * H * passes[0],
+                ctx_merge_attn_flops=640 * H * sum(passes[1:]),
+                ext_attn_flops=0, last_attn_flops=0,
+                gather_tokens=int(C.sum()),
+                gather_bytes=int(C.sum()) * (2304 if p.cache_dtype == "bf16" else 644 + (644 if self.fp8_raw else 1152)),
+                new_tokens=int(E.sum()), ctx_tokens=int(C.sum()), merges=max(len(self.chunks) - 1, 0),
+            )
         last_pairs = pairs[-1] if pairs else 0
         first_pairs = pairs[0] if pairs and not (self.two_seg and len(pairs) == 1) else 0
         mid_pairs = ctx_pairs - first_pairs - (last_pairs if self.two_seg else 0)

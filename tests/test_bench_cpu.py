@@ -16,7 +16,7 @@ import bench  # noqa: E402
 from mla_long_context_amd.prefill import ChunkedPrefill  # noqa: E402
 
 
-def _work(ctx, ext, S, two_seg=True, H=8, cache="bf16", raw=True):
+def _work(ctx, ext, S, two_seg=True, H=8, cache="bf16", raw=True, fold=True):
     """ChunkedPrefill.work() of a chunk plan, without device memory: work()
     reads only the lengths, the chunk count, the head count and the launch
     arrangement."""
@@ -27,6 +27,7 @@ def _work(ctx, ext, S, two_seg=True, H=8, cache="bf16", raw=True):
     n_chunks = max((int(c) + S - 1) // S for c in ctx) if len(ctx) else 0
     pre.chunks = [None] * n_chunks
     pre.two_seg = two_seg and bool(pre.chunks)
+    pre.fold = pre.two_seg and fold
     pre.fp8_raw = cache == "fp8" and raw
     return pre.work()
 
@@ -53,8 +54,8 @@ def test_attention_work_is_the_visible_pair_count(seed):
         ctx[0] = 1
     S = int(rng.choice([16, 64, 100, 512]))
     H = 8
-    for two_seg in (True, False):
-        w = _work(ctx, ext, S, two_seg, H)
+    for two_seg, fold in ((True, True), (True, False), (False, False)):
+        w = _work(ctx, ext, S, two_seg, H, fold=fold)
         assert w["attn_flops"] == 640 * H * _visible_pairs(ctx, ext)
         # the launches' shares partition the step's attention work
         parts = w["ctx_attn_flops"] + w["ctx_merge_attn_flops"] + w["ext_attn_flops"] + w["last_attn_flops"]
@@ -67,12 +68,28 @@ def test_attention_work_by_chunk():
     # chunk c of a request holds its context keys [c S, min((c+1) S, C)); the
     # first chunk's pass, the merging passes and the last pass share them
     ctx, ext, S, H = [10, 70, 200], [3, 5, 7], 64, 2
-    w = _work(ctx, ext, S, True, H)
+    w = _work(ctx, ext, S, True, H, fold=False)
     per_chunk = [sum(max(0, min(S, C - c * S)) * E for C, E in zip(ctx, ext)) for c in range(4)]
     assert w["ctx_attn_flops"] == 640 * H * per_chunk[0]
     assert w["ctx_merge_attn_flops"] == 640 * H * (per_chunk[1] + per_chunk[2])
     ext_pairs = sum(E * (E + 1) // 2 for E in ext)
     assert w["last_attn_flops"] == 640 * H * (per_chunk[3] + ext_pairs)
+
+
+def test_folded_causal_work_goes_to_each_request_s_last_chunk():
+    # with the causal pass folded, request r's new-token pairs E(E+1)/2 are
+    # counted in the pass of its last chunk max(ceil(C/S) - 1, 0): requests
+    # of 0 and 10 context tokens end in chunk 0, the one of 70 in chunk 1,
+    # the one of 200 in chunk 3
+    ctx, ext, S, H = [10, 70, 200, 0], [3, 5, 7, 4], 64, 2
+    w = _work(ctx, ext, S, True, H)
+    per_chunk = [sum(max(0, min(S, C - c * S)) * E for C, E in zip(ctx, ext)) for c in range(4)]
+    causal = [E * (E + 1) // 2 for E in ext]
+    assert w["ctx_attn_flops"] == 640 * H * (per_chunk[0] + causal[0] + causal[3])
+    assert w["ctx_merge_attn_flops"] == 640 * H * (sum(per_chunk[1:]) + causal[1] + causal[2])
+    assert w["last_attn_flops"] == 0 and w["ext_attn_flops"] == 0
+    # 70 tokens is two chunks of 64: request 1 ends in chunk 1, a merging pass
+    assert _work([70], [5], 64, True, H)["ctx_merge_attn_flops"] == 640 * H * (6 * 5 + 15)
 
 
 def test_dsv3_workload_flops():

@@ -626,6 +626,100 @@ def test_attention_two_segments(case):
             check_lse(gl[rows, hs], rl, tol=LSE_ABS, what=f"b{b} h{hs} lse")
 
 
+# ---------------------------------------------------------------- one chunk pass with per-request last flags
+
+# (seed, nq, nA, nB, last, merge): nA plain keys (this chunk), nB causal keys
+# (the new tokens, taken only where last[b]), a previous state from nC
+# further keys when `merge`. Requests with last[b] == 0 and no key in this
+# chunk: in a merging pass their state is left as it was; in a first pass
+# they get the empty state (0, -inf). The even seeds deal the requests out
+# in a shuffled order, which must change nothing.
+CHUNK_PASS_CASES = [
+    (90, [300, 5, 0, 77, 40, 260], [700, 0, 5, 130, 0, 64], [300, 5, 0, 77, 43, 260], [1, 0, 1, 0, 0, 1], True),
+    (91, [300, 5, 0, 77, 40, 260], [700, 3, 5, 130, 9, 64], [300, 5, 0, 77, 43, 260], [0, 1, 1, 0, 1, 1], False),
+    (92, [100, 64, 7], [256, 0, 65], [100, 64, 7], [0, 1, 1], True),
+    (93, [33, 64, 1], [0, 129, 3], [33, 64, 1], [0, 0, 1], False),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_PASS_CASES, ids=[f"seed{c[0]}" for c in CHUNK_PASS_CASES])
+def test_attention_chunk_pass(case):
+    """mla_prefill_attn_chunk: requests whose last chunk this is take the new
+    tokens' keys (causal) too and get their final bf16 result (lse into the
+    state's lse); the others' running fp32 state is written or merged into.
+    Each row is checked against the plain softmax over its key sets, and
+    whatever a row must not write is checked unchanged, bit for bit."""
+    require_gpu()
+    seed, nq, nA, nB, last, merge = case
+    say(f"attn chunk pass seed={seed} nq={nq} last={last} merge={merge}")
+    rng = np.random.default_rng(seed)
+    H, h0, h1 = 3, 0, 3
+    Hs = h1 - h0
+    nC = [int(x) for x in rng.integers(1, 200, len(nq))] if merge else [0] * len(nq)
+    B = len(nq)
+    cu_q = np.concatenate([[0], np.cumsum(nq)])
+    T = int(cu_q[-1])
+    q = mi.f32_to_bf16_bits(rng.standard_normal((T, H, 192)).astype(np.float32))
+    scale = 1 / math.sqrt(192)
+
+    def segment(n):
+        cu = np.concatenate([[0], np.cumsum(n)]); NK = max(int(cu[-1]), 1)
+        kn = mi.f32_to_bf16_bits(rng.standard_normal((Hs, NK, 128)).astype(np.float32))
+        v = mi.f32_to_bf16_bits(rng.standard_normal((Hs, NK, 128)).astype(np.float32))
+        lat = mi.f32_to_bf16_bits(rng.standard_normal((NK, 576)).astype(np.float32))
+        return cu, NK, kn, v, lat
+
+    cuA, NKA, knA, vA, latA = segment(nA)
+    cuB, NKB, knB, vB, latB = segment(nB)
+    cuC, NKC, knC, vC, latC = segment(nC)
+    acc = torch.full((T, Hs, 128), float("nan"), dtype=torch.float32, device="cuda")
+    accl = torch.full((T, Hs), float("nan"), dtype=torch.float32, device="cuda")
+    if merge:
+        mla.mla_prefill_attn(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knC), NKC * 128, bf16_dev(vC),
+                             NKC * 128, bf16_dev(latC), 576, _i32(cu_q), _i32(cuC), None, B, max(nq), scale, 0,
+                             acc, mla.DTYPE_FP32, Hs * 128, accl, Hs)
+    torch.cuda.synchronize()
+    acc0, accl0 = acc.clone(), accl.clone()
+    out = torch.full((T, Hs, 128), 9.0, dtype=torch.bfloat16, device="cuda")
+    order = _i32(rng.permutation(B)) if seed % 2 == 0 else None
+    mla.mla_prefill_attn_chunk(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knA), NKA * 128, bf16_dev(vA),
+                               NKA * 128, bf16_dev(latA), 576, _i32(cuA), bf16_dev(knB), NKB * 128,
+                               bf16_dev(vB), NKB * 128, bf16_dev(latB), 576, _i32(cuB), _i32(last), order,
+                               _i32(cu_q), B, max(nq), scale, merge, acc, Hs * 128, accl, Hs, out, Hs * 128)
+    torch.cuda.synchronize()
+
+    def same_bits(a, b):
+        return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+    go, ga, gl = f64(out), f64(acc), f64(accl)
+    for b in range(B):
+        rows = np.arange(cu_q[b], cu_q[b + 1])
+        r = slice(int(cu_q[b]), int(cu_q[b + 1]))
+        kc = np.arange(cuC[b], cuC[b + 1]); ka = np.arange(cuA[b], cuA[b + 1])
+        kb = np.arange(cuB[b], cuB[b + 1]) if last[b] else np.arange(0)
+        if not last[b] and merge and nA[b] == 0:
+            assert same_bits(acc[r], acc0[r]) and same_bits(accl[r], accl0[r]), f"b{b}: state changed"
+            assert bool((out[r] == 9.0).all()), f"b{b}: out written"
+            continue
+        i = np.arange(nq[b])[:, None]
+        vis = np.concatenate([np.ones((nq[b], len(kc) + len(ka)), dtype=bool),
+                              np.arange(len(kb))[None, :] <= i + len(kb) - nq[b]], axis=1)
+        for hs in range(Hs):
+            kn = np.concatenate([knC[hs, kc], knA[hs, ka], knB[hs, kb]])
+            vv = np.concatenate([vC[hs, kc], vA[hs, ka], vB[hs, kb]])
+            kr = np.concatenate([latC[kc, 512:], latA[ka, 512:], latB[kb, 512:]])
+            ro, rl = orc.attend(orc.bf16_to_f64(q[rows, h0 + hs]), orc.bf16_to_f64(kn), orc.bf16_to_f64(kr),
+                                orc.bf16_to_f64(vv), scale, vis)
+            res = go if last[b] else ga
+            check_out(res[rows, hs], ro, what=f"b{b} h{hs} {'out' if last[b] else 'state'}")
+            check_lse(gl[rows, hs], rl, tol=LSE_ABS, what=f"b{b} h{hs} lse")
+        if last[b]:
+            # the final rows leave the fp32 state as it was
+            assert same_bits(acc[r], acc0[r]), f"b{b}: state written"
+        else:
+            assert bool((out[r] == 9.0).all()), f"b{b}: out written"
+
+
 # ---------------------------------------------------------------- absorbed-form attention
 
 @pytest.mark.parametrize("n_rows,pieces", [(37, [0, 300, 364, 1000, 1000]), (64, [0, 2048]), (130, [0, 31, 97]),

@@ -101,17 +101,25 @@ def test_config1_tiny_all_outputs():
 # 3 see 1..65 keys. With a selection kv_b_proj (the default here) the
 # decompressed keys are exact and every row is held to the lse bar; the
 # random-weight cases hold those rows to their derived bound instead.
-@pytest.mark.parametrize("chunk,fuse,two_seg,weights", [
-    (64, "all", True, "selection"), (100, "all", True, "selection"), (4096, "all", True, "selection"),
-    (64, "all", False, "selection"), (100, "all", False, "selection"), (64, "none", True, "selection"),
-    (100, "final", True, "selection"), (100, "all", True, "normal"), (64, "none", True, "normal")])
-def test_ragged_multichunk_bf16(chunk, fuse, two_seg, weights):
+#
+# fold: each request's causal pass runs in the pass of its own last chunk
+# (requests 1 and 3 end in chunk 0, requests 0 and 2 in different later
+# chunks); fold=False runs them all in the loop's last pass.
+@pytest.mark.parametrize("chunk,fuse,two_seg,weights,fold", [
+    (64, "all", True, "selection", True), (100, "all", True, "selection", True),
+    (4096, "all", True, "selection", True), (64, "all", True, "selection", False),
+    (100, "all", True, "selection", False), (4096, "all", True, "selection", False),
+    (64, "all", False, "selection", True), (100, "all", False, "selection", True),
+    (64, "none", True, "selection", True), (100, "final", True, "selection", True),
+    (100, "all", True, "normal", True), (100, "all", True, "normal", False), (64, "none", True, "normal", True)])
+def test_ragged_multichunk_bf16(chunk, fuse, two_seg, weights, fold):
     require_gpu()
-    say(f"ragged bf16 chunk={chunk} fuse_merge={fuse} two_segment={two_seg} weights={weights}")
+    say(f"ragged bf16 chunk={chunk} fuse_merge={fuse} two_segment={two_seg} weights={weights} fold={fold}")
     prob = mi.make_problem(4, [320, 0, 64 * 9, 64], [70, 5, 300, 1], chunk, "bf16", seed=71,
                            extra_blocks=3, poison=True, weights=weights)
-    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg)
+    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg, fold_causal=fold)
     assert pre.two_seg == (two_seg and fuse == "all")
+    assert pre.fold == (pre.two_seg and fold)
     _run(pre)
     _compare_chunked(prob, pre, exact=weights == "selection")
 

@@ -37,12 +37,14 @@ def test_random_chunked_prefill(seed):
     fuse = str(rng.choice(["all", "all", "final", "none"]))
     two_seg = bool(rng.integers(0, 4) > 0)
     mode = str(rng.choice(["raw", "raw", "dequant"]))
+    fold = bool(rng.integers(0, 3) > 0)
     say(f"random chunked prefill seed={seed}: H={H} ctx={ctx} ext={ext} chunk={chunk} {dtype} exact={exact} "
-        f"fuse={fuse} two_seg={two_seg} mode={mode}")
+        f"fuse={fuse} two_seg={two_seg} fold={fold} mode={mode}")
     prob = mi.make_problem(H, ctx, ext, chunk, dtype, seed=2000 + seed, extra_blocks=int(rng.integers(0, 4)),
                            poison=True, weights="selection" if exact else "normal",
                            exact_dequant=exact and dtype == "fp8")
-    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg, **({"fp8_mode": mode} if dtype == "fp8" else {}))
+    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg, fold_causal=fold,
+                         **({"fp8_mode": mode} if dtype == "fp8" else {}))
     _run(pre)
     _compare_chunked(prob, pre, exact=exact)
     if dtype == "fp8":
