@@ -317,12 +317,8 @@ int mla_prefill_attn_2seg(const void* q, int64_t q_row_stride, int H_q, int h_be
  * an empty key set is the identity), which skips requests whose last pass
  * came earlier; in a first pass (merge == 0) such a request gets the empty
  * state (0, -inf). Final rows leave state untouched, and the other rows out.
- * order (nullable): a permutation of the requests 0..batch-1, the order in
- * which their workgroups are dealt out (NULL: 0, 1, ...); listing the
- * requests with the most keys in this pass first shortens its tail. It
- * changes no result. Everything else (q, segments, strides, scale, cu_q,
- * max_q) as in mla_prefill_attn_2seg; last, state and state_lse must not be
- * NULL.
+ * Everything else (q, segments, strides, scale, cu_q, max_q) as in
+ * mla_prefill_attn_2seg; last, state and state_lse must not be NULL.
  */
 int mla_prefill_attn_chunk(const void* q, int64_t q_row_stride, int H_q, int h_begin, int h_end,
                            const void* k_nope, int64_t k_head_stride,
@@ -331,8 +327,8 @@ int mla_prefill_attn_chunk(const void* q, int64_t q_row_stride, int H_q, int h_b
                            const void* k_nope2, int64_t k_head_stride2,
                            const void* v2, int64_t v_head_stride2,
                            const void* latent2, int64_t ld_latent2, const int32_t* cu_k2,
-                           const int32_t* last, const int32_t* order, const int32_t* cu_q, int batch,
-                           int max_q, float scale, int merge, float* state, int64_t state_row_stride,
+                           const int32_t* last, const int32_t* cu_q, int batch, int max_q, float scale,
+                           int merge, float* state, int64_t state_row_stride,
                            float* state_lse, int64_t state_lse_row_stride,
                            void* out, int64_t out_row_stride, void* stream);
 

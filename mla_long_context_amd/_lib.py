@@ -97,7 +97,7 @@ _SIGS = {
                               P, I64, P, I64, P, I64, P, P, I32, I32, F32,
                               P, I64, P, I64, P, I32, I64, P, I64, P],
     "mla_prefill_attn_chunk": [P, I64, I32, I32, I32, P, I64, P, I64, P, I64, P,
-                               P, I64, P, I64, P, I64, P, P, P, P, I32, I32, F32,
+                               P, I64, P, I64, P, I64, P, P, P, I32, I32, F32,
                                I32, P, I64, P, I64, P, I64, P],
     "mla_absorb_q": [P, I64, I32, I32, I32, P, I32, P, I32, P, P],
     "mla_absorbed_attn": [P, I32, P, I64, P, I32, F32, P, I32, P, P],
@@ -223,13 +223,13 @@ def mla_prefill_attn_2seg(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_s
 
 def mla_prefill_attn_chunk(q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v,
                            v_head_stride, latent, ld_latent, cu_k, k_nope2, k_head_stride2, v2,
-                           v_head_stride2, latent2, ld_latent2, cu_k2, last, order, cu_q, batch, max_q,
-                           scale, merge, state, state_row_stride, state_lse, state_lse_row_stride, out,
+                           v_head_stride2, latent2, ld_latent2, cu_k2, last, cu_q, batch, max_q, scale,
+                           merge, state, state_row_stride, state_lse, state_lse_row_stride, out,
                            out_row_stride, stream=None):
     return _call("mla_prefill_attn_chunk", _ptr(q), q_row_stride, H_q, h_begin, h_end, _ptr(k_nope),
                  k_head_stride, _ptr(v), v_head_stride, _ptr(latent), ld_latent, _ptr(cu_k),
                  _ptr(k_nope2), k_head_stride2, _ptr(v2), v_head_stride2, _ptr(latent2), ld_latent2,
-                 _ptr(cu_k2), _ptr(last), _ptr(order), _ptr(cu_q), batch, max_q, float(scale), int(merge),
+                 _ptr(cu_k2), _ptr(last), _ptr(cu_q), batch, max_q, float(scale), int(merge),
                  _ptr(state), state_row_stride, _ptr(state_lse), state_lse_row_stride, _ptr(out),
                  out_row_stride, _stream(stream))
 

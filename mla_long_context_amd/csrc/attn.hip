@@ -53,9 +53,6 @@ struct AttnArgs {
   // writes the final result to out; the other requests' rows write the
   // running fp32 state to state_out instead
   const int32_t* last; float* state_out; int64_t state_rs;
-  // nullable: the order in which requests are dealt out (a permutation of
-  // 0..batch-1), longest first to shorten the launch's tail
-  const int32_t* order;
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -125,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if (bh >= n_bh) return;
   int qt = j % a.n_qt;
   const int hs = bh % a.Hsel;
-  const int b = a.order ? a.order[bh / a.Hsel] : bh / a.Hsel;
+  const int b = bh / a.Hsel;
   // longest rows first: later row tiles see more keys of a causal segment
   if (kCausal || kSeg2) qt = a.n_qt - 1 - qt;
 
@@ -532,7 +529,6 @@ struct Seg2 {
   const void* k_nope; int64_t k_head_stride; const void* v; int64_t v_head_stride;
   const void* latent; int64_t ld_latent; const int32_t* cu_k;
   const int32_t* last = nullptr; float* state = nullptr; int64_t state_rs = 0;
-  const int32_t* order = nullptr;
 };
 
 template <int NW, bool kCausal, bool kRowIds, bool kMerge>
@@ -637,7 +633,7 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
              cu_q, cu_k, q_row_ids, batch, n_qt, scale * kLog2e,
              out, out_row_stride, lse, lse_row_stride,
              prev, prev_row_stride, prev_lse, prev_lse_row_stride,
-             nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, nullptr, 0, nullptr};
+             nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, nullptr, 0};
   if (seg2) {
     a.k2 = static_cast<const uint16_t*>(seg2->k_nope);
     a.khs2 = seg2->k_head_stride;
@@ -648,7 +644,6 @@ int prefill_attn(const char* fn, const void* q, int64_t q_row_stride, int H_q, i
     a.last = seg2->last;
     a.state_out = seg2->state;
     a.state_rs = seg2->state_rs;
-    a.order = seg2->order;
   }
   dim3 g((unsigned)total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -719,8 +714,7 @@ extern "C" int mla_prefill_attn_chunk(const void* q, int64_t q_row_stride, int H
                                       const int32_t* cu_k, const void* k_nope2, int64_t k_head_stride2,
                                       const void* v2, int64_t v_head_stride2, const void* latent2,
                                       int64_t ld_latent2, const int32_t* cu_k2, const int32_t* last,
-                                      const int32_t* order, const int32_t* cu_q, int batch, int max_q,
-                                      float scale, int merge,
+                                      const int32_t* cu_q, int batch, int max_q, float scale, int merge,
                                       float* state, int64_t state_row_stride, float* state_lse,
                                       int64_t state_lse_row_stride, void* out, int64_t out_row_stride,
                                       void* stream) {
@@ -734,7 +728,6 @@ extern "C" int mla_prefill_attn_chunk(const void* q, int64_t q_row_stride, int H
   seg2.last = last;
   seg2.state = state;
   seg2.state_rs = state_row_stride;
-  seg2.order = order;
   return prefill_attn(fn, q, q_row_stride, H_q, h_begin, h_end, k_nope, k_head_stride, v, v_head_stride, latent,
                       ld_latent, cu_q, cu_k, nullptr, batch, max_q, scale, 0, out, MLA_DTYPE_BF16, out_row_stride,
                       state_lse, state_lse_row_stride, merge ? state : nullptr, state_row_stride,

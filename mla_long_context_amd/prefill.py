@@ -173,14 +173,6 @@ class ChunkedPrefill(_DeviceStatus):
         if self.fold:
             last_c = np.maximum((C + self.S - 1) // self.S - 1, 0)
             self.last_flags = [_i32((last_c == c).astype(np.int32), device) for c in range(n_chunks)]
-            # each pass deals out the requests whose workgroups have the most
-            # keys first (this chunk's, plus the new tokens' where it is the
-            # last): the long ones start early and the launch ends evenly
-            E = prob.ext_len.astype(np.int64)
-            self.pass_order = []
-            for c in range(n_chunks):
-                keys = np.clip(C - c * self.S, 0, self.S) + np.where(last_c == c, E, 0)
-                self.pass_order.append(_i32(np.argsort(-keys, kind="stable").astype(np.int32), device))
         self.ext_off = max_ctx_tok if self.two_seg else 0
         self.max_tok = max([ch["n"] for ch in self.chunks] + [self.ext_off + self.T, 1])
         lat_rows = max(off, 1) if self.gather_once else max_ctx_tok
@@ -259,8 +251,7 @@ class ChunkedPrefill(_DeviceStatus):
                                  self.v_ws, self.hstride, self._lat(ch), D_LAT, ch["cu"],
                                  self._at(self.k_ws, self.ext_off), self.hstride,
                                  self._at(self.v_ws, self.ext_off), self.hstride, self.ext, D_LAT,
-                                 self.cu_ext, self.last_flags[ci], self.pass_order[ci], self.cu_ext, self.B,
-                                 self.maxE,
+                                 self.cu_ext, self.last_flags[ci], self.cu_ext, self.B, self.maxE,
                                  self.prob.scale, ci > 0, self.acc_o, self.H * D_V, self.acc_l, self.H,
                                  self.out, self.H * D_V, stream)
 

@@ -114,23 +114,23 @@ def test_two_segment_attn_validation(lib):
 
 
 def test_chunk_pass_attn_validation(lib):
-    # q, q_rs, H_q, h0, h1, k, khs, v, vhs, lat, ld, cu_k, k2, khs2, v2, vhs2, lat2, ld2, cu_k2, last, order,
-    # cu_q, batch, max_q, scale, merge, state, state_rs, state_lse, state_lse_rs, out, out_rs
+    # q, q_rs, H_q, h0, h1, k, khs, v, vhs, lat, ld, cu_k, k2, khs2, v2, vhs2, lat2, ld2, cu_k2, last, cu_q,
+    # batch, max_q, scale, merge, state, state_rs, state_lse, state_lse_rs, out, out_rs
     base = [FAKE, 8 * 192, 8, 0, 8, FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE,
-            FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE, FAKE, None, FAKE, 1, 10, 0.07,
+            FAKE, 1280, FAKE, 1280, FAKE, 576, FAKE, FAKE, FAKE, 1, 10, 0.07,
             1, FAKE, 8 * 128, FAKE, 8, FAKE, 8 * 128]
-    for i, what in [(19, "last"), (26, "state"), (28, "state_lse")]:
+    for i, what in [(19, "last"), (25, "state"), (27, "state_lse")]:
         args = list(base); args[i] = None
         code, msg = _err(mla.mla_prefill_attn_chunk, *args)
         assert code == _lib.MLA_ERR_INVALID_ARG and "null" in msg, (what, msg)
-    args = list(base); args[27] = 8 * 128 - 4             # state rows narrower than the heads
+    args = list(base); args[26] = 8 * 128 - 4             # state rows narrower than the heads
     code, msg = _err(mla.mla_prefill_attn_chunk, *args)
     assert code == _lib.MLA_ERR_INVALID_ARG and "state" in msg
-    args = list(base); args[26] = FAKE + 4                # misaligned state
+    args = list(base); args[25] = FAKE + 4                # misaligned state
     assert _err(mla.mla_prefill_attn_chunk, *args)[0] == _lib.MLA_ERR_INVALID_ARG
     args = list(base); args[17] = 584                     # latents with different row strides
     assert _err(mla.mla_prefill_attn_chunk, *args)[0] == _lib.MLA_ERR_UNSUPPORTED
-    args = list(base); args[22] = 0                       # nothing to do
+    args = list(base); args[21] = 0                       # nothing to do
     assert mla.mla_prefill_attn_chunk(*args, stream=0) == 0
 
 

@@ -632,8 +632,7 @@ def test_attention_two_segments(case):
 # (the new tokens, taken only where last[b]), a previous state from nC
 # further keys when `merge`. Requests with last[b] == 0 and no key in this
 # chunk: in a merging pass their state is left as it was; in a first pass
-# they get the empty state (0, -inf). The even seeds deal the requests out
-# in a shuffled order, which must change nothing.
+# they get the empty state (0, -inf).
 CHUNK_PASS_CASES = [
     (90, [300, 5, 0, 77, 40, 260], [700, 0, 5, 130, 0, 64], [300, 5, 0, 77, 43, 260], [1, 0, 1, 0, 0, 1], True),
     (91, [300, 5, 0, 77, 40, 260], [700, 3, 5, 130, 9, 64], [300, 5, 0, 77, 43, 260], [0, 1, 1, 0, 1, 1], False),
@@ -681,10 +680,9 @@ def test_attention_chunk_pass(case):
     torch.cuda.synchronize()
     acc0, accl0 = acc.clone(), accl.clone()
     out = torch.full((T, Hs, 128), 9.0, dtype=torch.bfloat16, device="cuda")
-    order = _i32(rng.permutation(B)) if seed % 2 == 0 else None
     mla.mla_prefill_attn_chunk(bf16_dev(q), H * 192, H, h0, h1, bf16_dev(knA), NKA * 128, bf16_dev(vA),
                                NKA * 128, bf16_dev(latA), 576, _i32(cuA), bf16_dev(knB), NKB * 128,
-                               bf16_dev(vB), NKB * 128, bf16_dev(latB), 576, _i32(cuB), _i32(last), order,
+                               bf16_dev(vB), NKB * 128, bf16_dev(latB), 576, _i32(cuB), _i32(last),
                                _i32(cu_q), B, max(nq), scale, merge, acc, Hs * 128, accl, Hs, out, Hs * 128)
     torch.cuda.synchronize()
 
