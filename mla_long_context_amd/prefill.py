@@ -104,7 +104,7 @@ class ChunkedPrefill(_DeviceStatus):
     """Configs with a paged context and new (extend) tokens per request."""
 
     def __init__(self, prob, device="cuda", chunk=None, fuse_merge="all", two_segment=True, fp8_mode="raw",
-                 fold_causal=True):
+                 fold_causal=True, gather_all=None):
         """fp8_mode (fp8 caches): "raw" gathers the codes and scales as they
         are and the decompression reads the codes (mla_gather_context_fp8_raw,
         mla_decompress with row_scale); "dequant" has the gather write the
@@ -113,7 +113,11 @@ class ChunkedPrefill(_DeviceStatus):
         With every merge fused and two_segment, each request's causal pass
         over its new tokens runs in the pass of its own last context chunk
         (fold_causal, mla_prefill_attn_chunk); fold_causal=False runs all of
-        them in the pass of the loop's last chunk (mla_prefill_attn_2seg)."""
+        them in the pass of the loop's last chunk (mla_prefill_attn_2seg).
+
+        gather_all: gather every chunk's records in one launch at the start
+        of a step (None: whenever the chunks times the requests fit one
+        launch's grid), or each chunk's before its decompression (False)."""
         self.prob = prob
         self.device = device
         assert fuse_merge in ("none", "final", "all")
@@ -152,7 +156,7 @@ class ChunkedPrefill(_DeviceStatus):
         # step, into one workspace where chunk c's records start at row
         # lat_off: each (chunk, request) is a request of that launch, with
         # the request's block-table row repeated per chunk.
-        self.gather_once = bool(self.chunks) and n_chunks * self.B <= 65535
+        self.gather_once = bool(self.chunks) and n_chunks * self.B <= 65535 and gather_all is not False
         if self.gather_once:
             self.g_start = _i32(np.concatenate(starts), device)
             self.g_len = _i32(np.concatenate(lens), device)

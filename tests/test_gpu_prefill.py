@@ -117,26 +117,32 @@ def test_ragged_multichunk_bf16(chunk, fuse, two_seg, weights, fold):
     say(f"ragged bf16 chunk={chunk} fuse_merge={fuse} two_segment={two_seg} weights={weights} fold={fold}")
     prob = mi.make_problem(4, [320, 0, 64 * 9, 64], [70, 5, 300, 1], chunk, "bf16", seed=71,
                            extra_blocks=3, poison=True, weights=weights)
-    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg, fold_causal=fold)
+    # the 100-token chunks gather each chunk before its decompression
+    pre = ChunkedPrefill(prob, fuse_merge=fuse, two_segment=two_seg, fold_causal=fold,
+                         gather_all=False if chunk == 100 else None)
     assert pre.two_seg == (two_seg and fuse == "all")
     assert pre.fold == (pre.two_seg and fold)
     _run(pre)
     _compare_chunked(prob, pre, exact=weights == "selection")
 
 
-@pytest.mark.parametrize("exact,mode", [(True, "raw"), (False, "raw"), (True, "dequant"), (False, "dequant")])
-def test_ragged_multichunk_fp8(exact, mode):
+@pytest.mark.parametrize("exact,mode,gather_all", [(True, "raw", None), (False, "raw", None), (True, "dequant", None),
+                                                   (False, "dequant", None), (True, "raw", False),
+                                                   (True, "dequant", False)])
+def test_ragged_multichunk_fp8(exact, mode, gather_all):
     """exact: selection kv_b_proj and records whose scale is 2^-6, so every
     dequantised latent and decompressed key is exact in bf16 and every row is
     held to the bar; otherwise random weights and scales, with the derived
     bound for the few-key rows. mode: the decompression reads the fp8 codes
-    (raw, the default) or the gather dequantises them."""
+    (raw, the default) or the gather dequantises them. gather_all=False
+    gathers each chunk before its decompression instead of all at once."""
     require_gpu()
-    say(f"ragged fp8 exact={exact} mode={mode}")
+    say(f"ragged fp8 exact={exact} mode={mode} gather_all={gather_all}")
     prob = mi.make_problem(4, [64 * 11, 128, 0], [40, 257, 3], 256, "fp8", seed=72,
                            weights="selection" if exact else "normal", exact_dequant=exact)
-    pre = ChunkedPrefill(prob, fp8_mode=mode)
+    pre = ChunkedPrefill(prob, fp8_mode=mode, gather_all=gather_all)
     assert pre.fp8_raw == (mode == "raw")
+    assert pre.gather_once == (gather_all is None)
     _run(pre)
     _compare_chunked(prob, pre, exact=exact)
     _compare_chunked(prob, pre, rl2=FP8_REL_L2, exact=exact)
