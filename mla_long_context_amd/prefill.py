@@ -420,9 +420,10 @@ class ReusePrefill(_DeviceStatus):
     workgroup would leave most of the GPU idle: every chunk's keys are split
     into `split`-key pieces, each passed to mla_prefill_attn as a request of
     its own (the query rows repeated through q_row_ids), and the partial
-    (out, lse) states of all pieces of the document are merged at the end by
-    a log-depth tree of mla_merge_states calls. By the merge identity this
-    equals the chunk-by-chunk merge."""
+    (out, lse) states of all pieces are merged at the end, in one pass over
+    them (mla_merge_states_n; merge="tree" uses a log-depth tree of
+    mla_merge_states calls instead). By the merge identity this equals the
+    chunk-by-chunk merge."""
 
     def __init__(self, prob, device="cuda", chunk=None, split=4096, local_path="absorbed",
                  split_local=None, artifact=None, request=None, merge="one_pass"):
