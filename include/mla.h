@@ -413,6 +413,25 @@ int mla_merge_states_n(const void* outs, int dtype_in, const float* lses, int pi
                        void* out, int dtype_out, float* lse_out, void* stream);
 
 /*
+ * mla_merge_states_sets -- up to MLA_MERGE_MAX_SETS independent
+ * mla_merge_states_n merges in one launch (for example the Global heads'
+ * and the Local rows' partial states of a head-partitioned reuse step), each
+ * set with its own pieces, rows and pointers as there, and one dtype pair for
+ * all. Every set is checked as mla_merge_states_n checks its arguments;
+ * sets with rows = 0 are skipped. The sets must not overlap one another.
+ */
+#define MLA_MERGE_MAX_SETS 4
+typedef struct MlaMergeSet {
+  const void* outs;     /* pieces * rows states, dtype_in */
+  const float* lses;    /* pieces * rows */
+  int pieces;           /* >= 1 */
+  int64_t rows;
+  void* out;            /* rows states, dtype_out */
+  float* lse_out;       /* rows */
+} MlaMergeSet;
+int mla_merge_states_sets(const MlaMergeSet* sets, int n_sets, int dtype_in, int dtype_out, void* stream);
+
+/*
  * mla_rope_relocate_q -- [REDKNOT] Abstract and section 2 (query-side RoPE
  * relocation): for every row r < T and head h < H, the rope part
  * q[r * q_row_stride + h * 192 + 128 + (0..63)] is rotated by the angle

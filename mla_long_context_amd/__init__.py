@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     ROPE_HALF, ROPE_INTERLEAVED, ArtifactMeta, MlaError, load, mla_absorb_out, mla_absorb_q,
     mla_absorbed_attn, mla_artifact_check, mla_cache_append, mla_decompress, mla_gather_context,
     mla_gather_context_fp8_raw,
-    mla_head_partition_merge, mla_head_partition_merge_noalloc, mla_merge_states, mla_merge_states_n, mla_pack_weight_t, mla_prefill_attn,
+    mla_head_partition_merge, mla_head_partition_merge_noalloc, mla_merge_states, mla_merge_states_n, mla_merge_states_sets, mla_pack_weight_t, mla_prefill_attn,
     mla_prefill_attn_merge, mla_prefill_attn_2seg, mla_prefill_attn_chunk, mla_rope_relocate_q, mla_token_hash,
     raise_on_device_status,
 )

@@ -31,6 +31,7 @@ EXPORTS = (
     "mla_decompress", "mla_prefill_attn", "mla_prefill_attn_merge", "mla_prefill_attn_2seg", "mla_prefill_attn_chunk",
     "mla_absorb_q",
     "mla_absorbed_attn", "mla_absorb_out", "mla_merge_states", "mla_merge_states_n",
+    "mla_merge_states_sets",
     "mla_rope_relocate_q",
     "mla_head_partition_merge", "mla_head_partition_merge_noalloc", "mla_token_hash", "mla_artifact_check",
 )
@@ -53,6 +54,15 @@ class ArtifactMeta(ctypes.Structure):
                 ("d_c", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("rope_base", ctypes.c_double), ("n_layers", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("layer_mask", ctypes.c_uint64)]
+
+
+class MlaMergeSet(ctypes.Structure):
+    """One merge of mla_merge_states_sets (field meanings as in mla.h)."""
+    _fields_ = [("outs", ctypes.c_void_p), ("lses", ctypes.c_void_p), ("pieces", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p)]
+
+
+MERGE_MAX_SETS = 4
 
 
 class MlaError(RuntimeError):
@@ -104,6 +114,7 @@ _SIGS = {
     "mla_absorb_out": [P, I32, P, I32, I32, I32, P, I64, P],
     "mla_merge_states": [P, I32, P, P, I32, P, I64, P, I32, P, P],
     "mla_merge_states_n": [P, I32, P, I32, I64, P, I32, P, P],
+    "mla_merge_states_sets": [P, I32, I32, I32, P],
     "mla_rope_relocate_q": [P, P, I64, I32, I32, I64, F64, I32, P],
     "mla_head_partition_merge": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P, P],
     "mla_head_partition_merge_noalloc": [P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, P, P],
@@ -260,6 +271,16 @@ def mla_merge_states(out_a, dtype_a, lse_a, out_b, dtype_b, lse_b, rows, out, dt
 def mla_merge_states_n(outs, dtype_in, lses, pieces, rows, out, dtype_out, lse_out, stream=None):
     return _call("mla_merge_states_n", _ptr(outs), dtype_in, _ptr(lses), pieces, rows, _ptr(out), dtype_out,
                  _ptr(lse_out), _stream(stream))
+
+
+def mla_merge_states_sets(sets, dtype_in, dtype_out, stream=None):
+    """sets: (outs, lses, pieces, rows, out, lse_out) per merge, at most
+    MERGE_MAX_SETS of them."""
+    arr = (MlaMergeSet * max(len(sets), 1))()
+    for i, (outs, lses, pieces, rows, out, lse_out) in enumerate(sets):
+        arr[i] = MlaMergeSet(_ptr(outs), _ptr(lses), pieces, rows, _ptr(out), _ptr(lse_out))
+    return _call("mla_merge_states_sets", ctypes.cast(arr, ctypes.c_void_p), len(sets), dtype_in, dtype_out,
+                 _stream(stream))
 
 
 def mla_rope_relocate_q(q_in, q_out, q_row_stride, T, H, delta, rope_base=10000.0,

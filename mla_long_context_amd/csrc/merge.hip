@@ -117,13 +117,40 @@ int launch_b(int dtb, int dto, dim3 g, hipStream_t s, const void* oa, const floa
 constexpr int kMaxW = 8;    // wavefronts per workgroup, at most
 constexpr int kPer = 4;     // pieces whose loads one wavefront issues together
 
+// Several independent merges in one launch (the sets of
+// mla_merge_states_sets): set k owns workgroups [first[k], first[k+1]).
+// A wavefront of a set with fewer pieces than wavefronts folds nothing and
+// hands the empty state (-inf, 0, 0) to the combine.
+struct MergeSetDev {
+  const void* outs; const float* lses; int pieces; int64_t rows; void* out; float* lo;
+};
+struct MergeSetsDev {
+  MergeSetDev s[MLA_MERGE_MAX_SETS];
+  int64_t first[MLA_MERGE_MAX_SETS + 1];
+  int n;
+};
+
 template <int kDi, int kDo>
-__global__ __launch_bounds__(kMaxW * 64) void merge_n_kernel(const void* outs, const float* lses, int pieces,
-                                                              int64_t rows, void* out, float* lo) {
+__global__ __launch_bounds__(kMaxW * 64) void merge_n_kernel(MergeSetsDev ms) {
   __shared__ float sh[kMaxW - 1][10][64];      // [wavefront 1..W-1][m, s, r0..r7][lane]
+  // this workgroup's set (wavefront-uniform, a few scalar compares)
+  int64_t blk = blockIdx.x;
+  int k = 0;
+#pragma unroll
+  for (int j = 1; j < MLA_MERGE_MAX_SETS; ++j)
+    if (j < ms.n && blk >= ms.first[j]) k = j;
+  blk -= ms.first[k];
+  const void* outs = ms.s[0].outs; const float* lses = ms.s[0].lses; int pieces = ms.s[0].pieces;
+  int64_t rows = ms.s[0].rows; void* out = ms.s[0].out; float* lo = ms.s[0].lo;
+#pragma unroll
+  for (int j = 1; j < MLA_MERGE_MAX_SETS; ++j)
+    if (k == j) {
+      outs = ms.s[j].outs; lses = ms.s[j].lses; pieces = ms.s[j].pieces;
+      rows = ms.s[j].rows; out = ms.s[j].out; lo = ms.s[j].lo;
+    }
   const int W = (int)(blockDim.x >> 6);
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
-  const int64_t row = (int64_t)blockIdx.x * 4 + (lane >> 4);
+  const int64_t row = blk * 4 + (lane >> 4);
   const bool live = row < rows;
   const int64_t off = row * kDv + (lane & 15) * 8;
   float m = -INFINITY, s = 0.f, r[8];
@@ -222,38 +249,71 @@ extern "C" int mla_merge_states(const void* out_a, int dtype_a, const float* lse
   return launch_b<MLA_DTYPE_FP32>(dtype_b, dtype_out, g, s, out_a, lse_a, out_b, lse_b, rows, out, lse_out);
 }
 
+namespace {
+
+// validation and launch shared by mla_merge_states_n and mla_merge_states_sets
+int merge_sets(const char* fn, const MlaMergeSet* sets, int n_sets, int dtype_in, int dtype_out, void* stream) {
+  MLA_REQUIRE(ok_dt(dtype_in) && ok_dt(dtype_out), MLA_ERR_UNSUPPORTED,
+              "%s: dtypes must be bf16 or fp32 (got %d, %d)", fn, dtype_in, dtype_out);
+  MergeSetsDev ms{};
+  int64_t total = 0;
+  int W = 1;
+  for (int k = 0; k < n_sets; ++k) {
+    const MlaMergeSet& t = sets[k];
+    MLA_REQUIRE(t.rows >= 0 && t.pieces >= 1, MLA_ERR_INVALID_ARG,
+                "%s: set %d needs rows (%lld) >= 0 and pieces (%d) >= 1", fn, k, (long long)t.rows, t.pieces);
+    if (t.rows > 0) {
+      MLA_REQUIRE(t.outs && t.lses && t.out && t.lse_out, MLA_ERR_INVALID_ARG, "%s: set %d: null pointer", fn, k);
+      MLA_REQUIRE(mla_aligned16(t.outs) && mla_aligned16(t.out), MLA_ERR_INVALID_ARG,
+                  "%s: set %d: state pointers must be 16-byte aligned", fn, k);
+      MLA_REQUIRE(t.rows <= (int64_t)1 << 40 && (int64_t)t.pieces * t.rows <= (int64_t)1 << 40,
+                  MLA_ERR_INVALID_ARG, "%s: set %d: rows too large", fn, k);
+      // as many wavefronts per 4-row group as the set with most pieces has, up to 8
+      const int wk = t.pieces < kMaxW ? t.pieces : kMaxW;
+      if (wk > W) W = wk;
+    }
+    ms.s[k] = MergeSetDev{t.outs, t.lses, t.pieces, t.rows, t.out, t.lse_out};
+    ms.first[k] = total;
+    total += (t.rows + 3) / 4;
+  }
+  ms.first[n_sets] = total;
+  ms.n = n_sets;
+  if (total == 0) return MLA_OK;
+  MLA_REQUIRE(total <= 0x7fffffff, MLA_ERR_INVALID_ARG, "%s: rows too large for one call", fn);
+  dim3 g((unsigned)total), blk((unsigned)(W * 64));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype_in == MLA_DTYPE_BF16) {
+    if (dtype_out == MLA_DTYPE_BF16)
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_BF16>), g, blk, 0, s, ms);
+    else
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_FP32>), g, blk, 0, s, ms);
+  } else {
+    if (dtype_out == MLA_DTYPE_BF16)
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_BF16>), g, blk, 0, s, ms);
+    else
+      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_FP32>), g, blk, 0, s, ms);
+  }
+  return mla_check_launch(fn);
+}
+
+}  // namespace
+
 extern "C" int mla_merge_states_n(const void* outs, int dtype_in, const float* lses, int pieces, int64_t rows,
                                   void* out, int dtype_out, float* lse_out, void* stream) {
   mla_begin_call();
   MLA_REQUIRE(rows >= 0 && pieces >= 1, MLA_ERR_INVALID_ARG,
               "mla_merge_states_n: need rows (%lld) >= 0 and pieces (%d) >= 1", (long long)rows, pieces);
   if (rows == 0) return MLA_OK;
-  MLA_REQUIRE(outs && lses && out && lse_out, MLA_ERR_INVALID_ARG, "mla_merge_states_n: null pointer argument");
-  MLA_REQUIRE(ok_dt(dtype_in) && ok_dt(dtype_out), MLA_ERR_UNSUPPORTED,
-              "mla_merge_states_n: dtypes must be bf16 or fp32 (got %d, %d)", dtype_in, dtype_out);
-  MLA_REQUIRE(mla_aligned16(outs) && mla_aligned16(out), MLA_ERR_INVALID_ARG,
-              "mla_merge_states_n: state pointers must be 16-byte aligned");
-  MLA_REQUIRE(rows <= (int64_t)1 << 40 && (int64_t)pieces * rows <= (int64_t)1 << 40, MLA_ERR_INVALID_ARG,
-              "mla_merge_states_n: rows too large");
-  MLA_REQUIRE((rows + 3) / 4 <= 0x7fffffff, MLA_ERR_INVALID_ARG, "mla_merge_states_n: rows too large");
-  // as many wavefronts per 4-row group as pieces, up to 8
-  const int W = pieces < kMaxW ? pieces : kMaxW;
-  dim3 g((unsigned)((rows + 3) / 4)), blk((unsigned)(W * 64));
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype_in == MLA_DTYPE_BF16) {
-    if (dtype_out == MLA_DTYPE_BF16)
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_BF16>), g, blk, 0, s, outs, lses,
-                         pieces, rows, out, lse_out);
-    else
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_BF16, MLA_DTYPE_FP32>), g, blk, 0, s, outs, lses,
-                         pieces, rows, out, lse_out);
-  } else {
-    if (dtype_out == MLA_DTYPE_BF16)
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_BF16>), g, blk, 0, s, outs, lses,
-                         pieces, rows, out, lse_out);
-    else
-      hipLaunchKernelGGL((merge_n_kernel<MLA_DTYPE_FP32, MLA_DTYPE_FP32>), g, blk, 0, s, outs, lses,
-                         pieces, rows, out, lse_out);
-  }
-  return mla_check_launch("mla_merge_states_n");
+  const MlaMergeSet set{outs, lses, pieces, rows, out, lse_out};
+  return merge_sets("mla_merge_states_n", &set, 1, dtype_in, dtype_out, stream);
+}
+
+extern "C" int mla_merge_states_sets(const MlaMergeSet* sets, int n_sets, int dtype_in, int dtype_out,
+                                     void* stream) {
+  mla_begin_call();
+  MLA_REQUIRE(n_sets >= 0 && n_sets <= MLA_MERGE_MAX_SETS, MLA_ERR_INVALID_ARG,
+              "mla_merge_states_sets: n_sets (%d) must be in [0, %d]", n_sets, MLA_MERGE_MAX_SETS);
+  if (n_sets == 0) return MLA_OK;
+  MLA_REQUIRE(sets, MLA_ERR_INVALID_ARG, "mla_merge_states_sets: null sets");
+  return merge_sets("mla_merge_states_sets", sets, n_sets, dtype_in, dtype_out, stream);
 }

@@ -421,7 +421,7 @@ class ReusePrefill(_DeviceStatus):
     into `split`-key pieces, each passed to mla_prefill_attn as a request of
     its own (the query rows repeated through q_row_ids), and the partial
     (out, lse) states of all pieces are merged at the end, in one pass over
-    them (mla_merge_states_n; merge="tree" uses a log-depth tree of
+    them (mla_merge_states_sets; merge="tree" uses a log-depth tree of
     mla_merge_states calls instead). By the merge identity this equals the
     chunk-by-chunk merge."""
 
@@ -606,20 +606,15 @@ class ReusePrefill(_DeviceStatus):
         L.mla_absorbed_attn(self.q_abs, R, self.lat_ws, D_LAT, ch["cu_kL"], ch["pieces_L"], self.prob.scale,
                             out, odt, lse, stream)
 
-    def _merge_tree(self, part, partl, n_rows, fin, finl, stream, n_pieces=None):
-        """Merge the partial states of all pieces into (fin, finl): in one
-        pass over all of them (mla_merge_states_n, the default), or as a
-        tree of pairwise merges (merge="tree"), where each level merges the
+    def _merge_tree(self, part, partl, n_rows, fin, finl, stream, n):
+        """merge="tree": merge the n > 1 partial states of every row into
+        (fin, finl) by a tree of pairwise merges, where each level merges the
         first half of the remaining pieces with the last half in place (fp32;
         an odd middle piece waits for the next level) and the last level
-        writes the bf16 result."""
-        n = self.n_pieces if n_pieces is None else n_pieces
+        writes the bf16 result. (The default merges all pieces, of the
+        Global and the Local rows together, in one mla_merge_states_sets
+        launch.)"""
         heads = part.shape[1]
-        if n <= 1:
-            return          # a single piece was written to (fin, finl) directly
-        if self.merge_mode == "one_pass":
-            L.mla_merge_states_n(part, L.DTYPE_FP32, partl, n, n_rows * heads, fin, L.DTYPE_BF16, finl, stream)
-            return
         while n > 1:
             h = n // 2
             m = n - h
@@ -677,15 +672,24 @@ class ReusePrefill(_DeviceStatus):
                         self._attn_pieces(ch, 0, HL, P, ch["cu_qL"], ch["rid_L"], self.part_L,
                                           self.partl_L, self.rec_out, self._lse_L, stream, local=True)
         with _span(timer, "merge"):
+            merges = []          # (part, partl, rows of the partial buffers, result, its lse, pieces)
             if HG > 0 and T > 0:
-                self._merge_tree(self.part_G, self.partl_G, T, self.glob_out, self.lse_G, stream)
+                merges.append((self.part_G, self.partl_G, T, self.glob_out, self.lse_G, self.n_pieces))
             if HL > 0 and P > 0:
                 if self.absorbed:
-                    self._merge_tree(self.part_L, self.partl_L, HL * P, self.olat_L, self.lse4_L, stream,
-                                     self.n_pieces_L)
+                    merges.append((self.part_L, self.partl_L, HL * P, self.olat_L, self.lse4_L, self.n_pieces_L))
                 else:
-                    self._merge_tree(self.part_L, self.partl_L, P, self.rec_out, self._lse_L, stream,
-                                     self.n_pieces_L)
+                    merges.append((self.part_L, self.partl_L, P, self.rec_out, self._lse_L, self.n_pieces_L))
+            merges = [m for m in merges if m[5] > 1]   # one piece was written to its result directly
+            if self.merge_mode == "one_pass":
+                # the Global and the Local merges in one launch
+                if merges:
+                    L.mla_merge_states_sets([(part, partl, n, rows * part.shape[1], fin, finl)
+                                             for part, partl, rows, fin, finl, n in merges],
+                                            L.DTYPE_FP32, L.DTYPE_BF16, stream)
+            else:
+                for part, partl, rows, fin, finl, n in merges:
+                    self._merge_tree(part, partl, rows, fin, finl, stream, n)
         if self.absorbed and HL > 0 and P > 0:
             with _span(timer, "absorb"):
                 L.mla_absorb_out(self.olat_L, P, self.w_t, H, 0, HL, self.rec_out, HL * D_V, stream)

@@ -151,6 +151,16 @@ def test_merge_rope_partition_pack_validation(lib):
                 4096, FAKE, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG          # P > T
     assert _err(mla.mla_pack_weight_t, FAKE, 10, 16, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG
     assert _err(mla.mla_pack_weight_t, FAKE, 16, 16, FAKE)[0] == _lib.MLA_ERR_INVALID_ARG   # in place
+    # several merges in one launch: at most four sets, each checked as alone
+    S = (FAKE, FAKE, 3, 4, FAKE, FAKE)
+    assert mla.mla_merge_states_sets([], 0, 0, stream=0) == 0
+    assert _err(mla.mla_merge_states_sets, [S] * 5, 0, 0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _err(mla.mla_merge_states_sets, [S, S], 7, 0)[0] == _lib.MLA_ERR_UNSUPPORTED
+    code, msg = _err(mla.mla_merge_states_sets, [S, (FAKE, FAKE, 0, 4, FAKE, FAKE)], 0, 0)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "set 1" in msg
+    code, msg = _err(mla.mla_merge_states_sets, [S, (FAKE + 8, FAKE, 3, 4, FAKE, FAKE)], 0, 0)
+    assert code == _lib.MLA_ERR_INVALID_ARG and "aligned" in msg
+    assert mla.mla_merge_states_sets([(None, None, 3, 0, None, None)], 0, 0, stream=0) == 0   # no rows
     # sizes whose grids would not fit the launch limits are refused, not truncated
     for fn, args in [(mla.mla_merge_states, (FAKE, 0, FAKE, FAKE, 0, FAKE, (1 << 34) + 1, FAKE, 0, FAKE)),
                      (mla.mla_rope_relocate_q, (FAKE, FAKE, 1024 * 192, 1 << 25, 1024, 4096, 10000.0, 0))]:

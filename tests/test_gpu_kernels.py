@@ -252,6 +252,46 @@ def test_merge_states_n(pieces, di, do):
         assert torch.equal(to2[0], out) and torch.equal(tl2[0], lout)
 
 
+@pytest.mark.parametrize("di", [0, 2])
+def test_merge_states_sets(di):
+    """mla_merge_states_sets: four merges in one launch (64, 3, 36 and 9
+    pieces; 1031, 70, 513 and 0 rows) give each set exactly what
+    mla_merge_states_n gives it alone (a set with fewer pieces than the
+    launch's wavefronts folds its pieces in the same order), and match the
+    oracle's pairwise merge folded over the pieces."""
+    require_gpu()
+    rng = np.random.default_rng(46 + di)
+    tdt = {0: torch.bfloat16, 2: torch.float32}
+    sets, alone = [], []
+    for pieces, rows in [(64, 1031), (3, 70), (36, 513), (9, 0)]:
+        o = rng.standard_normal((pieces, max(rows, 1), 128)).astype(np.float32)
+        lse = (rng.standard_normal((pieces, max(rows, 1))) * 3 + 8).astype(np.float32)
+        lse[:, :2] = -np.inf                          # every piece empty
+        lse[0, 2:9] = -np.inf                         # some pieces empty
+        to = torch.tensor(o).to(tdt[di]).cuda()
+        tl = torch.tensor(lse).cuda()
+        out = torch.full((max(rows, 1), 128), 7.0, dtype=torch.bfloat16, device="cuda")
+        lout = torch.full((max(rows, 1),), 7.0, dtype=torch.float32, device="cuda")
+        ref = torch.empty_like(out); refl = torch.empty_like(lout)
+        mla.mla_merge_states_n(to, di, tl, pieces, rows, ref, 0, refl)
+        sets.append((to, tl, pieces, rows, out, lout))
+        alone.append((ref, refl, o, lse))
+    mla.mla_merge_states_sets(sets, di, 0)
+    torch.cuda.synchronize()
+    for (to, tl, pieces, rows, out, lout), (ref, refl, o, lse) in zip(sets, alone):
+        if rows == 0:
+            assert bool((out == 7.0).all()) and bool((lout == 7.0).all())
+            continue
+        assert torch.equal(out, ref) and torch.equal(lout, refl), f"{pieces} pieces"
+        go = f64(to)
+        ref_o, ref_l = np.zeros((rows, 128)), np.full(rows, -np.inf)
+        for p in range(pieces):
+            ref_o, ref_l = orc.merge_states(ref_o, ref_l, go[p], lse[p].astype(np.float64))
+        got = f64(out)
+        assert np.max(np.abs(got - ref_o) / np.maximum(np.abs(ref_o), 1.0)) <= 2 ** -8
+        check_lse(f64(lout), ref_l, tol=1e-5)
+
+
 # ---------------------------------------------------------------- rope relocation
 
 @pytest.mark.parametrize("delta", [0, 1, 4096, 2 ** 18])
