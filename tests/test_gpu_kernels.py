@@ -691,9 +691,15 @@ def test_attention_chunk_pass(case):
     require_gpu()
     seed, nq, nA, nB, last, merge = case
     say(f"attn chunk pass seed={seed} nq={nq} last={last} merge={merge}")
-    rng = np.random.default_rng(seed)
     # odd seeds take a head range that starts past head 0 (q holds 4 heads)
     H, h0, h1 = (3, 0, 3) if seed % 2 == 0 else (4, 1, 4)
+    check_chunk_pass(seed, nq, nA, nB, last, merge, H, h0, h1)
+
+
+def check_chunk_pass(seed, nq, nA, nB, last, merge, H, h0, h1):
+    """mla_prefill_attn_chunk on seeded inputs against the oracle, and the
+    rows each route must leave alone unchanged (see test_attention_chunk_pass)."""
+    rng = np.random.default_rng(seed)
     Hs = h1 - h0
     nC = [int(x) for x in rng.integers(1, 200, len(nq))] if merge else [0] * len(nq)
     B = len(nq)

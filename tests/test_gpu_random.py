@@ -2,8 +2,9 @@
 oracle: the chunked prefill (head counts, batch sizes, context and new-token
 lengths around the 64-token block and the 128-row tile, chunk sizes, bf16
 and fp8 caches, the launch arrangements), head-partitioned reuse (documents,
-offsets, protected rows, key splits, both Local paths, both merges) and the
-offline artifact build. Tolerances as in the other parity tests: rows over
+offsets, protected rows, key splits, both Local paths, both merges), one
+chunk pass with per-request last-chunk flags, and the offline artifact
+build. Tolerances as in the other parity tests: rows over
 fewer than 256 keys use a selection kv_b_proj (exact keys) or, with random
 weights, the bound derived from their own data; reuse rows over few keys the
 bound from the relocated query's rounding."""
@@ -17,6 +18,7 @@ from oracle import mla_oracle as orc
 
 from gpu_util import FP8_REL_L2, LSE_ABS, check_lse, check_out, f64, relocation_lse_bound, require_gpu, say
 from test_gpu_artifact import _doc_latent, _lse_tol
+from test_gpu_kernels import check_chunk_pass
 from test_gpu_prefill import _compare_chunked, _run
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +51,27 @@ def test_random_chunked_prefill(seed):
     _compare_chunked(prob, pre, exact=exact)
     if dtype == "fp8":
         _compare_chunked(prob, pre, rl2=FP8_REL_L2, exact=exact)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_chunk_pass(seed):
+    """One chunk pass (mla_prefill_attn_chunk) with random requests: lengths
+    around the 64-key tile and the 32/128-row tiles, empty segments, random
+    last-chunk flags, a first or a merging pass, a head range."""
+    require_gpu()
+    rng = np.random.default_rng(9000 + seed)
+    B = int(rng.integers(1, 7))
+    nq = [int(rng.choice([0, 1, 31, 32, 33, 64, 65, 127, 128, 129, int(rng.integers(1, 400))])) for _ in range(B)]
+    nA = [int(rng.choice([0, 1, 63, 64, 65, int(rng.integers(0, 700))])) for _ in range(B)]
+    # the new tokens' keys are the rows' own, or a different count
+    nB = [n if rng.integers(0, 4) else int(rng.integers(0, 300)) for n in nq]
+    last = [int(rng.integers(0, 2)) for _ in range(B)]
+    merge = bool(rng.integers(0, 2))
+    H = int(rng.choice([1, 2, 4]))
+    h0 = int(rng.integers(0, H))
+    h1 = int(rng.integers(h0 + 1, H + 1))
+    say(f"random chunk pass seed={seed}: nq={nq} nA={nA} nB={nB} last={last} merge={merge} heads {h0}..{h1} of {H}")
+    check_chunk_pass(9100 + seed, nq, nA, nB, last, merge, H, h0, h1)
 
 
 @pytest.mark.parametrize("seed", range(30))
